@@ -1,0 +1,217 @@
+/*
+ * lcd_oracle.c -- plain CPU oracle for context-lookup drafting.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, literal statement of what
+ * the drafting hot path computes.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark load it; the product path never does, and it
+ * shares no source, header, table or helper with the HIP library.
+ *
+ * Source of the method: the HyperQwen lookup-drafting article (page titled
+ * "HyperQwen 上下文复述加速：lookup 草稿如何把 25k 文档复读推到 381 tok/s"),
+ * sections "第 1 步" (search the request's own history), "第 2 步" (fuse with the
+ * draft model's proposal), "第 3 步" (schedule the long block only while a copy
+ * is in progress) and the closing paragraph on losslessness (greedy verification
+ * never reads the draft distribution).  Where the article leaves a step open the
+ * reading taken is stated at the function.
+ *
+ * Conventions: token ids are int32; PAD = -1 marks an empty draft or block slot.
+ * Every array is host memory owned by the caller.  Nothing here allocates.
+ * Each function handles B requests with a plain loop; no blocking, no early
+ * termination beyond what the definition itself implies.
+ */
+#include <stdint.h>
+#include <stddef.h>
+
+#define ORACLE_PAD (-1)
+#define ORACLE_DRAFT_STRIDE 15   /* draft and block rows */
+#define ORACLE_Q_STRIDE 7        /* draft-model proposal rows */
+#define ORACLE_TARGET_STRIDE 16  /* target argmax rows */
+
+/* Method parameters; the defaults are the article's numbers (4..12-token
+ * suffixes, up to 15 drafted tokens, 7-slot draft-model head, head thresholds
+ * 8 and 6-with-2-agreeing, tail threshold 4, two-step entry, sticky exit 3). */
+typedef struct oracle_params {
+    int32_t l_min, l_max, k_max;
+    int32_t n_head, n_block;
+    int32_t head_full, head_agree, agree_n, tail_min;
+    int32_t entry_steps, sticky, near_full_slack;
+} oracle_params;
+
+/*
+ * Lookup for one request (article, "第 1 步").
+ *
+ * The longest current suffix of l_max..l_min tokens is searched for, longest
+ * length first; for a given length the most recent earlier occurrence wins
+ * (positions scanned from latest to earliest).  "Earlier occurrence" is read as
+ * an occurrence that ends at most at index n-2, so that at least one following
+ * token exists; it may overlap the suffix itself (the article allows a match to
+ * overlap the suffix so periodic text matches at its own period).
+ *
+ * Draft: the tokens that follow the occurrence, read LZ77-style from the history
+ * extended by the draft itself, so when the occurrence overlaps the suffix the
+ * copy runs past the end of the history and repeats with period n-1-e.  Up to
+ * k_max tokens; the remaining slots of the 15-slot row are PAD.  No match:
+ * m = 0, e = -1, all PAD.
+ */
+static void lookup_one(const int32_t *h, int64_t n, const oracle_params *p,
+                       int32_t *m_out, int32_t *e_out, int32_t *draft)
+{
+    int32_t m = 0;
+    int64_t e = -1;
+    for (int32_t L = p->l_max; L >= p->l_min && m == 0; --L) {
+        /* the occurrence h[q..q+L-1] must end at q+L-1 <= n-2 */
+        for (int64_t q = n - L - 1; q >= 0; --q) {
+            int same = 1;
+            for (int32_t j = 0; j < L; ++j) {
+                if (h[q + j] != h[n - L + j]) { same = 0; break; }
+            }
+            if (same) { m = L; e = q + L - 1; break; }
+        }
+    }
+    for (int k = 0; k < ORACLE_DRAFT_STRIDE; ++k) draft[k] = ORACLE_PAD;
+    if (m > 0) {
+        /* append one token at a time: source index e+1+k in (history ++ draft) */
+        for (int32_t k = 0; k < p->k_max; ++k) {
+            int64_t src = e + 1 + k;
+            draft[k] = (src < n) ? h[src] : draft[src - n];
+        }
+    }
+    *m_out = m;
+    *e_out = (int32_t)e;
+}
+
+int oracle_lookup_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                          int32_t B, const oracle_params *p,
+                          int32_t *match_len, int32_t *match_end, int32_t *draft)
+{
+    for (int32_t r = 0; r < B; ++r) {
+        int64_t n = len[r] > 0 ? len[r] : 0;
+        lookup_one(hist + row_off[r], n, p, &match_len[r], &match_end[r],
+                   draft + (int64_t)r * ORACLE_DRAFT_STRIDE);
+    }
+    return 0;
+}
+
+/*
+ * Fusion into the verify block (article, "第 2 步").
+ *
+ * The verify block is the input token plus n_block draft slots when long and
+ * n_head slots when short.  Head slots 0..n_head-1 already hold the draft
+ * model's proposal; they are all replaced by the lookup draft when the match is
+ * at least head_full tokens, or at least head_agree tokens and the draft model
+ * independently proposed the same first agree_n tokens.  Tail slots
+ * n_head..blk-1 were proposed by nobody; in a long block they take the lookup
+ * draft whenever the match is at least tail_min tokens, independently of the
+ * head decision, and PAD otherwise.  Slots beyond the verified length, and
+ * draft slots at or past k_max, are never taken from the lookup.
+ */
+int oracle_fuse_verify_block(const int32_t *draft, const int32_t *match_len,
+                             const int32_t *q, const int32_t *long_mode, int32_t B,
+                             const oracle_params *p, int32_t *block, int32_t *block_len)
+{
+    for (int32_t r = 0; r < B; ++r) {
+        const int32_t *d = draft + (int64_t)r * ORACLE_DRAFT_STRIDE;
+        const int32_t *qr = q + (int64_t)r * ORACLE_Q_STRIDE;
+        int32_t *out = block + (int64_t)r * ORACLE_DRAFT_STRIDE;
+        int32_t m = match_len[r];
+        int is_long = long_mode[r] != 0;
+
+        int agree = 1;
+        for (int32_t i = 0; i < p->agree_n; ++i)
+            if (qr[i] != d[i]) agree = 0;
+        int head = (m >= p->head_full) || (m >= p->head_agree && agree);
+        int tail = is_long && (m >= p->tail_min);
+        int32_t blk = is_long ? p->n_block : p->n_head;
+
+        for (int32_t i = 0; i < ORACLE_DRAFT_STRIDE; ++i) {
+            int32_t v;
+            if (i >= blk)
+                v = ORACLE_PAD;
+            else if (i < p->n_head)
+                v = (head && i < p->k_max) ? d[i] : qr[i];
+            else
+                v = (tail && i < p->k_max) ? d[i] : ORACLE_PAD;
+            out[i] = v;
+        }
+        block_len[r] = blk;
+    }
+    return 0;
+}
+
+/*
+ * Greedy acceptance (article, closing paragraph on losslessness; the Polish
+ * speculative-decoding post, section on why token-by-token generation is
+ * expensive: the first rejected proposal ends the run).
+ *
+ * a = length of the longest prefix of the block equal to the target's argmax
+ * tokens, at most blk.  The step emits target[0..a] (a+1 tokens: the accepted
+ * drafts plus the target's own token at the first mismatch, or its bonus token).
+ * Optional append: when hist is non-NULL, target[0..a] is written at
+ * row_off[r]+len[r] and len[r] grows by a+1; if that would exceed cap[r] the
+ * request is flagged with accept = -1 and nothing is written.
+ */
+int oracle_greedy_accept(const int32_t *block, const int32_t *block_len,
+                         const int32_t *target, int32_t B, int32_t *accept,
+                         int32_t *hist, const int64_t *row_off, int32_t *len,
+                         const int32_t *cap)
+{
+    for (int32_t r = 0; r < B; ++r) {
+        const int32_t *blkr = block + (int64_t)r * ORACLE_DRAFT_STRIDE;
+        const int32_t *t = target + (int64_t)r * ORACLE_TARGET_STRIDE;
+        int32_t blk = block_len[r];
+        int32_t a = 0;
+        while (a < blk && blkr[a] == t[a]) a++;
+        if (hist != NULL) {
+            int64_t have = len[r];
+            if (have + a + 1 > (int64_t)cap[r]) {
+                accept[r] = -1;
+                continue;
+            }
+            for (int32_t i = 0; i <= a; ++i)
+                hist[row_off[r] + have + i] = t[i];
+            len[r] = (int32_t)(have + a + 1);
+        }
+        accept[r] = a;
+    }
+    return 0;
+}
+
+/*
+ * Long-block scheduler (article, "第 3 步").
+ *
+ * Per request the state is {long_mode, streak, down}.  This step's flag is
+ * "the lookup match could fill the tail" (m >= tail_min) and "the step came out
+ * nearly full" (a >= blk - near_full_slack, reading "nearly full" as at most
+ * near_full_slack short of the verified length; a failed append, a = -1, never
+ * counts).  In short mode the flag must hold on entry_steps consecutive steps to
+ * switch to the long block; in long mode the block is kept while the flag has
+ * been down for at most `sticky` consecutive steps and dropped on the next one,
+ * after which entry has to be earned again from zero.  The returned mode is the
+ * one the next step uses.
+ */
+int oracle_lookup_schedule_step(int32_t *state /* B x 3 */, const int32_t *match_len,
+                                const int32_t *accept, const int32_t *block_len, int32_t B,
+                                const oracle_params *p, int32_t *long_next)
+{
+    for (int32_t r = 0; r < B; ++r) {
+        int32_t *st = state + (int64_t)r * 3;
+        int32_t is_long = st[0], streak = st[1], down = st[2];
+        int32_t a = accept[r];
+        int flag = (match_len[r] >= p->tail_min) && (a >= 0) &&
+                   (a >= block_len[r] - p->near_full_slack);
+        if (!is_long) {
+            streak = flag ? streak + 1 : 0;
+            if (streak >= p->entry_steps) { is_long = 1; streak = 0; down = 0; }
+        } else {
+            if (flag) {
+                down = 0;
+            } else {
+                down = down + 1;
+                if (down > p->sticky) { is_long = 0; down = 0; streak = 0; }
+            }
+        }
+        st[0] = is_long; st[1] = streak; st[2] = down;
+        long_next[r] = is_long;
+    }
+    return 0;
+}
