@@ -1,0 +1,213 @@
+"""Context-lookup drafting for speculative decoding on AMD Instinct MI355X.
+
+A thin ctypes binding over ``liblcd.so`` (HIP kernels for gfx950, C ABI in
+``include/lcd.h``).  The functions below only check and marshal arguments: every
+step of the hot path runs in the library's kernels, asynchronously on the
+current torch stream.  There is no CPU fallback; a missing or unloadable
+library raises.
+
+Entry points (same names as the C ABI):
+  lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end, draft, params)
+  fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len, params)
+  greedy_accept(block, block_len, target, accept, hist=None, row_off=None, lens=None, cap=None)
+  lookup_schedule_step(state, match_len, accept, block_len, long_next, params)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PAD = -1
+DRAFT_STRIDE = 15
+Q_STRIDE = 7
+TARGET_STRIDE = 16
+MAX_SUFFIX = 16
+
+LCD_OK = 0
+LCD_EINVAL = -1
+LCD_EHIP = -2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblcd.so")
+
+
+class LCDError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        what = {LCD_EINVAL: "invalid argument", LCD_EHIP: "HIP launch error"}.get(code, "error")
+        super().__init__(f"{fn} returned {code} ({what})")
+        self.code = code
+
+
+class Params(ctypes.Structure):
+    """Mirror of ``lcd_params`` (include/lcd.h)."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "l_min", "l_max", "k_max", "n_head", "n_block", "head_full", "head_agree",
+        "agree_n", "tail_min", "entry_steps", "sticky", "near_full_slack", "scan_wgs")]
+
+    def __repr__(self):
+        return "Params(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def load():
+    """Load liblcd.so once; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} "
+                               "(run python -m context_lookup_drafting_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        pp = ctypes.POINTER(Params)
+        L.lcd_default_params.argtypes = [pp]
+        L.lcd_default_params.restype = None
+        L.lcd_check_params.argtypes = [pp]
+        L.lcd_check_params.restype = ctypes.c_int
+        L.lcd_workspace_bytes.argtypes = [i32]
+        L.lcd_workspace_bytes.restype = ctypes.c_size_t
+        L.lookup_propose.argtypes = [P, P, P, i32, i32, pp, P, P, P, P, P]
+        L.fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P]
+        L.greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P, P]
+        L.lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P, P]
+        for f in (L.lookup_propose, L.fuse_verify_block, L.greedy_accept, L.lookup_schedule_step):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def default_params(**overrides) -> Params:
+    p = Params()
+    load().lcd_default_params(ctypes.byref(p))
+    for k, v in overrides.items():
+        if not hasattr(p, k):
+            raise KeyError(k)
+        setattr(p, k, int(v))
+    return p
+
+
+def check_params(p: Params) -> bool:
+    return load().lcd_check_params(ctypes.byref(p)) == LCD_OK
+
+
+def workspace_bytes(B: int) -> int:
+    return int(load().lcd_workspace_bytes(int(B)))
+
+
+def alloc_workspace(B: int, device):
+    """Zero-filled lookup workspace for B requests (kept zero by every call)."""
+    import torch
+    n = max(workspace_bytes(B), 16)
+    return torch.zeros(n // 8, dtype=torch.int64, device=device)
+
+
+# ---------------------------------------------------------------------------
+# argument marshalling
+# ---------------------------------------------------------------------------
+
+def _dev(t, name, dtype, numel=None, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != LCD_OK:
+        raise LCDError(fn, rc)
+
+
+def lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end, draft,
+                   params: Params | None = None):
+    """Longest-suffix / latest-occurrence lookup and 15-token draft for every
+    request (include/lcd.h, lookup_propose)."""
+    import torch
+    p = params or default_params()
+    B = lens.numel()
+    dev = lens.device
+    args = (
+        _dev(hist, "hist", torch.int32, device=dev),
+        _dev(row_off, "row_off", torch.int64, B, dev),
+        _dev(lens, "lens", torch.int32, B, dev),
+        ctypes.c_int32(B), ctypes.c_int32(int(max_len)), ctypes.byref(p),
+        _dev(workspace, "workspace", workspace.dtype, device=dev),
+        _dev(match_len, "match_len", torch.int32, B, dev),
+        _dev(match_end, "match_end", torch.int32, B, dev),
+        _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev),
+        _stream(dev),
+    )
+    if workspace.numel() * workspace.element_size() < workspace_bytes(B):
+        raise ValueError("workspace too small")
+    _check("lookup_propose", load().lookup_propose(*args))
+
+
+def fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len,
+                      params: Params | None = None):
+    import torch
+    p = params or default_params()
+    B = match_len.numel()
+    dev = match_len.device
+    _check("fuse_verify_block", load().fuse_verify_block(
+        _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev),
+        _dev(match_len, "match_len", torch.int32, B, dev),
+        _dev(model_draft, "model_draft", torch.int32, B * Q_STRIDE, dev),
+        _dev(long_mode, "long_mode", torch.int32, B, dev),
+        ctypes.c_int32(B), ctypes.byref(p),
+        _dev(block, "block", torch.int32, B * DRAFT_STRIDE, dev),
+        _dev(block_len, "block_len", torch.int32, B, dev),
+        _stream(dev)))
+
+
+def greedy_accept(block, block_len, target, accept, hist=None, row_off=None, lens=None, cap=None):
+    import torch
+    B = block_len.numel()
+    dev = block_len.device
+    if hist is None:
+        h = ro = ln = cp = ctypes.c_void_p(None)
+    else:
+        h = _dev(hist, "hist", torch.int32, device=dev)
+        ro = _dev(row_off, "row_off", torch.int64, B, dev)
+        ln = _dev(lens, "lens", torch.int32, B, dev)
+        cp = _dev(cap, "cap", torch.int32, B, dev)
+    _check("greedy_accept", load().greedy_accept(
+        _dev(block, "block", torch.int32, B * DRAFT_STRIDE, dev),
+        _dev(block_len, "block_len", torch.int32, B, dev),
+        _dev(target, "target", torch.int32, B * TARGET_STRIDE, dev),
+        ctypes.c_int32(B),
+        _dev(accept, "accept", torch.int32, B, dev),
+        h, ro, ln, cp, _stream(dev)))
+
+
+def lookup_schedule_step(state, match_len, accept, block_len, long_next,
+                         params: Params | None = None):
+    """``state`` is an int32 [B,3] device tensor {long_mode, streak, down}."""
+    import torch
+    p = params or default_params()
+    B = match_len.numel()
+    dev = match_len.device
+    _check("lookup_schedule_step", load().lookup_schedule_step(
+        _dev(state, "state", torch.int32, 3 * B, dev),
+        _dev(match_len, "match_len", torch.int32, B, dev),
+        _dev(accept, "accept", torch.int32, B, dev),
+        _dev(block_len, "block_len", torch.int32, B, dev),
+        ctypes.c_int32(B), ctypes.byref(p),
+        _dev(long_next, "long_next", torch.int32, B, dev),
+        _stream(dev)))

@@ -1,0 +1,219 @@
+// lcd_step.hip -- fusion, greedy acceptance and long-block scheduling for
+// MI355X / gfx950.  One lane per request: each of these moves about 200 bytes
+// per request, so they are bound by launch latency, not by the memory system.
+//
+// Method: HyperQwen lookup-drafting article, sections "第 2 步" (fuse the
+// lookup draft with the draft model's proposal: head slots need a long match,
+// or a shorter one confirmed by the draft model's first two tokens; tail slots
+// take any match of the tail threshold), "第 3 步" (long block entered after
+// two consecutive nearly-full steps with a tail-filling match, kept for a few
+// steps after the flag drops) and the closing paragraph (greedy verification
+// keeps the output identical: accept the longest draft prefix equal to the
+// target's argmax tokens).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lcd.h"
+
+namespace lcd {
+namespace {
+
+constexpr int kStepThreads = 256;
+
+struct FuseArgs {
+    int32_t k_max, n_head, n_block, head_full, head_agree, agree_n, tail_min;
+};
+
+struct SchedArgs {
+    int32_t tail_min, entry_steps, sticky, near_full_slack;
+};
+
+__global__ void __launch_bounds__(kStepThreads)
+fuse_kernel(const int32_t *__restrict__ draft, const int32_t *__restrict__ match_len,
+            const int32_t *__restrict__ q, const int32_t *__restrict__ long_mode, int32_t B,
+            FuseArgs a, int32_t *__restrict__ block, int32_t *__restrict__ block_len) {
+    const int r = blockIdx.x * kStepThreads + threadIdx.x;
+    if (r >= B) return;
+    const int32_t *d = draft + (int64_t)r * LCD_DRAFT_STRIDE;
+    const int32_t *qr = q + (int64_t)r * LCD_Q_STRIDE;
+    int32_t *out = block + (int64_t)r * LCD_DRAFT_STRIDE;
+    const int32_t m = match_len[r];
+    const bool is_long = long_mode[r] != 0;
+
+    int dv[LCD_DRAFT_STRIDE];
+    int qv[LCD_Q_STRIDE];
+#pragma unroll
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) dv[i] = d[i];
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = qr[i];
+
+    bool agree = true;
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i)
+        if (i < a.agree_n && qv[i] != dv[i]) agree = false;
+    const bool head = (m >= a.head_full) || (m >= a.head_agree && agree);
+    const bool tail = is_long && (m >= a.tail_min);
+    const int32_t blk = is_long ? a.n_block : a.n_head;
+
+    // head slots (the draft model's proposal) -- n_head <= 7 = LCD_Q_STRIDE
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i) {
+        int v = LCD_PAD;
+        if (i < a.n_head) v = (head && i < a.k_max) ? dv[i] : qv[i];
+        else if (i < blk) v = (tail && i < a.k_max) ? dv[i] : LCD_PAD;
+        out[i] = v;
+    }
+    // tail slots of a long block
+#pragma unroll
+    for (int i = LCD_Q_STRIDE; i < LCD_DRAFT_STRIDE; ++i)
+        out[i] = (i < blk && tail && i < a.k_max) ? dv[i] : LCD_PAD;
+    block_len[r] = blk;
+}
+
+__global__ void __launch_bounds__(kStepThreads)
+accept_kernel(const int32_t *__restrict__ block, const int32_t *__restrict__ block_len,
+              const int32_t *__restrict__ target, int32_t B, int32_t *__restrict__ accept,
+              int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
+              int32_t *__restrict__ len, const int32_t *__restrict__ cap) {
+    const int r = blockIdx.x * kStepThreads + threadIdx.x;
+    if (r >= B) return;
+    const int32_t *b = block + (int64_t)r * LCD_DRAFT_STRIDE;
+    const int32_t *t = target + (int64_t)r * LCD_TARGET_STRIDE;
+    int tv[LCD_TARGET_STRIDE];
+#pragma unroll
+    for (int i = 0; i < LCD_TARGET_STRIDE; ++i) tv[i] = t[i];
+    const int32_t blk = block_len[r];
+    int32_t acc = 0;
+    bool run = true;
+#pragma unroll
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) {
+        run = run && (i < blk) && (b[i] == tv[i]);
+        acc += run ? 1 : 0;
+    }
+    if (hist != nullptr) {
+        const int64_t have = len[r];
+        if (have + acc + 1 > (int64_t)cap[r]) {
+            accept[r] = -1;
+            return;
+        }
+        int32_t *dst = hist + row_off[r] + have;
+#pragma unroll
+        for (int i = 0; i < LCD_TARGET_STRIDE; ++i)
+            if (i <= acc) dst[i] = tv[i];
+        len[r] = (int32_t)(have + acc + 1);
+    }
+    accept[r] = acc;
+}
+
+__global__ void __launch_bounds__(kStepThreads)
+schedule_kernel(lcd_sched_state *__restrict__ state, const int32_t *__restrict__ match_len,
+                const int32_t *__restrict__ accept, const int32_t *__restrict__ block_len,
+                int32_t B, SchedArgs a, int32_t *__restrict__ long_next) {
+    const int r = blockIdx.x * kStepThreads + threadIdx.x;
+    if (r >= B) return;
+    lcd_sched_state st = state[r];
+    const int32_t acc = accept[r];
+    const bool flag = (match_len[r] >= a.tail_min) && (acc >= 0) &&
+                      (acc >= block_len[r] - a.near_full_slack);
+    if (!st.long_mode) {
+        st.streak = flag ? st.streak + 1 : 0;
+        if (st.streak >= a.entry_steps) {
+            st.long_mode = 1;
+            st.streak = 0;
+            st.down = 0;
+        }
+    } else if (flag) {
+        st.down = 0;
+    } else {
+        st.down += 1;
+        if (st.down > a.sticky) {
+            st.long_mode = 0;
+            st.down = 0;
+            st.streak = 0;
+        }
+    }
+    state[r] = st;
+    long_next[r] = st.long_mode;
+}
+
+inline int blocks_for(int32_t B) { return (B + kStepThreads - 1) / kStepThreads; }
+
+}  // namespace
+}  // namespace lcd
+
+extern "C" void lcd_default_params(lcd_params *p) {
+    if (!p) return;
+    p->l_min = 4;
+    p->l_max = 12;
+    p->k_max = 15;
+    p->n_head = 7;
+    p->n_block = 15;
+    p->head_full = 8;
+    p->head_agree = 6;
+    p->agree_n = 2;
+    p->tail_min = 4;
+    p->entry_steps = 2;
+    p->sticky = 3;
+    p->near_full_slack = 1;
+    p->scan_wgs = 0;
+}
+
+extern "C" int lcd_check_params(const lcd_params *p) {
+    if (!p) return LCD_EINVAL;
+    const bool ok = p->l_min >= 1 && p->l_min <= p->l_max && p->l_max <= LCD_MAX_SUFFIX &&
+                    p->k_max >= 0 && p->k_max <= LCD_DRAFT_STRIDE &&
+                    p->n_head >= 1 && p->n_head <= LCD_Q_STRIDE &&
+                    p->n_block >= p->n_head && p->n_block <= LCD_DRAFT_STRIDE &&
+                    p->head_full >= 1 && p->head_agree >= 1 &&
+                    p->agree_n >= 0 && p->agree_n <= p->n_head && p->tail_min >= 1 &&
+                    p->entry_steps >= 1 && p->sticky >= 0 && p->near_full_slack >= 0 &&
+                    p->scan_wgs >= 0 && p->scan_wgs <= (1 << 20);
+    return ok ? LCD_OK : LCD_EINVAL;
+}
+
+extern "C" int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
+                                 const int32_t *model_draft, const int32_t *long_mode, int32_t B,
+                                 const lcd_params *p, int32_t *block, int32_t *block_len,
+                                 void *stream) {
+    using namespace lcd;
+    if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!draft || !match_len || !model_draft || !long_mode || !block || !block_len)
+        return LCD_EINVAL;
+    FuseArgs a{p->k_max, p->n_head, p->n_block, p->head_full, p->head_agree, p->agree_n,
+               p->tail_min};
+    hipLaunchKernelGGL(fuse_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), draft, match_len, model_draft,
+                       long_mode, B, a, block, block_len);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+
+extern "C" int greedy_accept(const int32_t *block, const int32_t *block_len,
+                             const int32_t *target, int32_t B, int32_t *accept, int32_t *hist,
+                             const int64_t *row_off, int32_t *len, const int32_t *cap,
+                             void *stream) {
+    using namespace lcd;
+    if (B < 0) return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!block || !block_len || !target || !accept) return LCD_EINVAL;
+    if (hist && (!row_off || !len || !cap)) return LCD_EINVAL;
+    hipLaunchKernelGGL(accept_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), block, block_len, target, B, accept,
+                       hist, row_off, len, cap);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+
+extern "C" int lookup_schedule_step(lcd_sched_state *state, const int32_t *match_len,
+                                    const int32_t *accept, const int32_t *block_len, int32_t B,
+                                    const lcd_params *p, int32_t *long_next, void *stream) {
+    using namespace lcd;
+    if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!state || !match_len || !accept || !block_len || !long_next) return LCD_EINVAL;
+    SchedArgs a{p->tail_min, p->entry_steps, p->sticky, p->near_full_slack};
+    hipLaunchKernelGGL(schedule_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), state, match_len, accept, block_len,
+                       B, a, long_next);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}

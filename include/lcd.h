@@ -1,0 +1,176 @@
+/*
+ * lcd.h -- C ABI of the context-lookup drafting hot path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Method source: the HyperQwen lookup-drafting article (page titled
+ * "HyperQwen 上下文复述加速：lookup 草稿如何把 25k 文档复读推到 381 tok/s"),
+ * sections "第 1 步" (lookup), "第 2 步" (fusion), "第 3 步" (long-block
+ * scheduling) and its closing paragraph on losslessness (greedy verification).
+ *
+ * Every entry point handles a batch of B independent requests, runs
+ * asynchronously on the caller's HIP stream and allocates nothing: all arrays
+ * are DEVICE memory allocated and owned by the caller, only `p` is read on the
+ * host at call time.  `stream` is a hipStream_t (NULL = the null stream).
+ *
+ * Token ids are opaque int32 values; LCD_PAD (-1) marks an empty draft or block
+ * slot and is never produced by the lookup from a history of non-negative ids.
+ *
+ * Return values: LCD_OK on success; LCD_EINVAL for host-checkable misuse
+ * (B < 0, a NULL array with B > 0, a misaligned pointer where alignment is
+ * required, parameters out of range) -- nothing is launched; LCD_EHIP when the
+ * HIP runtime reports a launch error.  B == 0 is a no-op returning LCD_OK.
+ * Errors in device data cannot be seen by the host: lengths are clamped at 0,
+ * and an append that would overflow a row's capacity is reported per request
+ * (accept = -1) without writing.
+ */
+#ifndef LCD_H
+#define LCD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCD_PAD (-1)
+#define LCD_DRAFT_STRIDE 15   /* int32 per row of draft[] and block[] */
+#define LCD_Q_STRIDE 7        /* int32 per row of the draft-model proposal */
+#define LCD_TARGET_STRIDE 16  /* int32 per row of the target argmax tokens */
+#define LCD_MAX_SUFFIX 16     /* largest supported l_max */
+
+#define LCD_OK 0
+#define LCD_EINVAL (-1)
+#define LCD_EHIP (-2)
+
+/*
+ * Method parameters (defaults from lcd_default_params = the article's values).
+ *   l_min, l_max  suffix lengths searched, 1 <= l_min <= l_max <= 16 (4, 12)
+ *   k_max         drafted tokens per lookup, 0..15 (15)
+ *   n_head        draft-model proposal length = short block, 1..7 (7)
+ *   n_block       draft slots of a long block, n_head..15 (15; 7 disables it)
+ *   head_full     match length replacing the head outright, >= 1 (8)
+ *   head_agree    shorter match length replacing the head when the draft model
+ *                 agrees on its first agree_n slots, >= 1 (6)
+ *   agree_n       0..n_head (2)
+ *   tail_min      match length filling the tail of a long block, >= 1 (4)
+ *   entry_steps   consecutive flagged steps needed to enter long mode, >= 1 (2)
+ *   sticky        flag-down steps tolerated in long mode, >= 0 (3)
+ *   near_full_slack  a step is "nearly full" when accept >= blk - slack, >= 0 (1)
+ *   scan_wgs      launch tuning of lookup_propose only: workgroups per launch,
+ *                 0 = automatic.  Results never depend on it.
+ */
+typedef struct lcd_params {
+    int32_t l_min, l_max, k_max;
+    int32_t n_head, n_block;
+    int32_t head_full, head_agree, agree_n, tail_min;
+    int32_t entry_steps, sticky, near_full_slack;
+    int32_t scan_wgs;
+} lcd_params;
+
+/* Per-request scheduler state, caller-owned (device), start at {0,0,0}. */
+typedef struct lcd_sched_state {
+    int32_t long_mode, streak, down;
+} lcd_sched_state;
+
+/* Fills *p with the defaults above. */
+void lcd_default_params(lcd_params *p);
+
+/* Returns LCD_OK when *p is in range, LCD_EINVAL otherwise (host only). */
+int lcd_check_params(const lcd_params *p);
+
+/* Bytes of device workspace lookup_propose needs for B requests (16 per
+ * request).  The workspace must be zero-filled once before its first use;
+ * every completed call leaves it zero-filled again.  Concurrent calls must
+ * not share a workspace. */
+size_t lcd_workspace_bytes(int32_t B);
+
+/*
+ * lookup_propose -- article, section "第 1 步".
+ *
+ * For each request r, with h = hist + row_off[r] and n = max(len[r], 0):
+ * among candidate ends e in [0, n-2], let ell(e) be the number of tokens,
+ * capped at l_max, for which h[e-j] == h[n-1-j] for j = 0, 1, ... while
+ * e-j >= 0.  The result is the candidate with the largest ell(e) >= l_min,
+ * the latest such e on ties (the longest current suffix of l_min..l_max
+ * tokens and its most recent earlier occurrence; the occurrence may overlap
+ * the suffix).  Outputs:
+ *   match_len[r] = that length m, or 0 when there is none;
+ *   match_end[r] = e (an index into the row), or -1;
+ *   draft[r*15 + k] = h[n - D + (k mod D)] for k < k_max with D = n-1-e
+ *     (the tokens following the occurrence, copied LZ77-style, so an
+ *     overlapping match repeats with period D past the end of the history),
+ *     LCD_PAD for k >= k_max or when m == 0.
+ *
+ * hist      int32 token buffer, 16-byte aligned.  Row r occupies
+ *           [row_off[r], row_off[r] + len[r]); rows may be packed (CSR) or
+ *           padded.  Reads touch only the 16-byte granules that intersect a row.
+ * row_off   int64[B], len int32[B] (read on the device).
+ * max_len   an upper bound of len[] used only to size the launch; results are
+ *           correct for any value >= 0.
+ * workspace lcd_workspace_bytes(B) bytes, 16-byte aligned, see above.
+ * match_len, match_end int32[B]; draft int32[B*15].
+ */
+int lookup_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                   int32_t B, int32_t max_len, const lcd_params *p, void *workspace,
+                   int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream);
+
+/*
+ * fuse_verify_block -- article, section "第 2 步" (fusion, not overwrite).
+ *
+ * blk = long_mode[r] ? n_block : n_head draft slots are verified.
+ * head = (m >= head_full) || (m >= head_agree && q[i] == draft[i] for all
+ * i < agree_n).  Slots i < n_head: draft[i] if head and i < k_max, else q[i].
+ * Slots n_head <= i < blk (tail, long blocks only): draft[i] if m >= tail_min
+ * and i < k_max, else LCD_PAD.  Slots i >= blk: LCD_PAD.
+ *
+ * draft int32[B*15], match_len int32[B], model_draft (q) int32[B*7],
+ * long_mode int32[B] (non-zero = long block) -> block int32[B*15],
+ * block_len int32[B].
+ */
+int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
+                      const int32_t *model_draft, const int32_t *long_mode, int32_t B,
+                      const lcd_params *p, int32_t *block, int32_t *block_len, void *stream);
+
+/*
+ * greedy_accept -- article, closing paragraph (greedy verification never reads
+ * the draft distribution); the first rejected slot ends the run.
+ *
+ * accept[r] = the largest a <= block_len[r] with block[r*15+i] ==
+ * target[r*16+i] for every i < a.  The step emits target[r*16 + 0..a]
+ * (a+1 tokens).  When hist is non-NULL those a+1 tokens are appended at
+ * hist[row_off[r] + len[r]] and len[r] grows by a+1; if len[r]+a+1 > cap[r]
+ * nothing is written for that request and accept[r] = -1.  row_off, len and
+ * cap are only read when hist is non-NULL.
+ *
+ * block int32[B*15], block_len int32[B], target int32[B*16],
+ * accept int32[B]; hist int32 buffer (nullable), row_off int64[B],
+ * len int32[B] (in/out), cap int32[B].
+ */
+int greedy_accept(const int32_t *block, const int32_t *block_len, const int32_t *target,
+                  int32_t B, int32_t *accept, int32_t *hist, const int64_t *row_off,
+                  int32_t *len, const int32_t *cap, void *stream);
+
+/*
+ * lookup_schedule_step -- article, section "第 3 步" (long block only while a
+ * copy is in progress; sticky exit).
+ *
+ * flag = match_len[r] >= tail_min && accept[r] >= 0 &&
+ *        accept[r] >= block_len[r] - near_full_slack.
+ * Short mode: streak = flag ? streak+1 : 0; at streak >= entry_steps switch to
+ * long mode with streak = down = 0.  Long mode: down = flag ? 0 : down+1; at
+ * down > sticky switch to short mode with streak = down = 0.  long_next[r] is
+ * the mode of the next step (also written to state[r].long_mode).
+ *
+ * state lcd_sched_state[B] (in/out), match_len, accept, block_len int32[B],
+ * long_next int32[B].
+ */
+int lookup_schedule_step(lcd_sched_state *state, const int32_t *match_len,
+                         const int32_t *accept, const int32_t *block_len, int32_t B,
+                         const lcd_params *p, int32_t *long_next, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCD_H */

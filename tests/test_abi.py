@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/lcd.h declares, and rejects misuse before launching."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import context_lookup_drafting_amd as lcd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lcd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|void|size_t)\s+\**\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"lookup_propose", "fuse_verify_block", "greedy_accept",
+            "lookup_schedule_step"} <= set(names)
+    L = lcd.load()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_default_params_are_the_articles_values():
+    p = lcd.default_params()
+    assert (p.l_min, p.l_max, p.k_max) == (4, 12, 15)
+    assert (p.n_head, p.n_block) == (7, 15)
+    assert (p.head_full, p.head_agree, p.agree_n, p.tail_min) == (8, 6, 2, 4)
+    assert (p.entry_steps, p.sticky, p.near_full_slack, p.scan_wgs) == (2, 3, 1, 0)
+    assert lcd.check_params(p)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(l_min=0), dict(l_min=5, l_max=4), dict(l_max=17), dict(k_max=-1), dict(k_max=16),
+    dict(n_head=0), dict(n_head=8, n_block=15), dict(n_block=6), dict(n_block=16),
+    dict(head_full=0), dict(head_agree=0), dict(agree_n=-1), dict(agree_n=8),
+    dict(tail_min=0), dict(entry_steps=0), dict(sticky=-1), dict(near_full_slack=-1),
+    dict(scan_wgs=-1),
+])
+def test_param_ranges_rejected(bad):
+    assert not lcd.check_params(lcd.default_params(**bad))
+
+
+def test_workspace_bytes():
+    assert lcd.workspace_bytes(0) == 0
+    assert lcd.workspace_bytes(64) == 64 * 16
+
+
+def _P(v):
+    return ctypes.c_void_p(v)
+
+
+def test_entry_points_reject_misuse_without_launching():
+    L = lcd.load()
+    p = lcd.default_params()
+    pp = ctypes.byref(p)
+    s = _P(None)
+    fake = 0x10000          # never dereferenced: validation fails first
+    # B < 0
+    assert L.lookup_propose(_P(fake), _P(fake), _P(fake), -1, 10, pp, _P(fake),
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    # NULL arrays with B > 0
+    assert L.lookup_propose(None, _P(fake), _P(fake), 4, 10, pp, _P(fake),
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    assert L.lookup_propose(_P(fake), _P(fake), _P(fake), 4, 10, pp, None,
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    # misaligned history / workspace
+    assert L.lookup_propose(_P(fake + 4), _P(fake), _P(fake), 4, 10, pp, _P(fake),
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    assert L.lookup_propose(_P(fake), _P(fake), _P(fake), 4, 10, pp, _P(fake + 8),
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    # negative max_len, bad params
+    assert L.lookup_propose(_P(fake), _P(fake), _P(fake), 4, -1, pp, _P(fake),
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    bad = lcd.default_params(l_max=20)
+    assert L.lookup_propose(_P(fake), _P(fake), _P(fake), 4, 10, ctypes.byref(bad), _P(fake),
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    assert L.lookup_propose(_P(fake), _P(fake), _P(fake), 4, 10, None, _P(fake),
+                            _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
+    assert L.fuse_verify_block(None, _P(fake), _P(fake), _P(fake), 3, pp, _P(fake), _P(fake),
+                               s) == lcd.LCD_EINVAL
+    assert L.greedy_accept(_P(fake), _P(fake), _P(fake), 3, None, None, None, None, None,
+                           s) == lcd.LCD_EINVAL
+    # appending needs row offsets, lengths and capacities
+    assert L.greedy_accept(_P(fake), _P(fake), _P(fake), 3, _P(fake), _P(fake), None, _P(fake),
+                           _P(fake), s) == lcd.LCD_EINVAL
+    assert L.lookup_schedule_step(_P(fake), _P(fake), _P(fake), None, 3, pp, _P(fake),
+                                  s) == lcd.LCD_EINVAL
+
+
+def test_empty_batch_is_a_noop():
+    L = lcd.load()
+    p = lcd.default_params()
+    pp = ctypes.byref(p)
+    assert L.lookup_propose(None, None, None, 0, 0, pp, None, None, None, None, None) == lcd.LCD_OK
+    assert L.fuse_verify_block(None, None, None, None, 0, pp, None, None, None) == lcd.LCD_OK
+    assert L.greedy_accept(None, None, None, 0, None, None, None, None, None, None) == lcd.LCD_OK
+    assert L.lookup_schedule_step(None, None, None, None, 0, pp, None, None) == lcd.LCD_OK
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(lcd, "LIB_PATH", "/nonexistent/liblcd.so")
+    monkeypatch.setattr(lcd, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        lcd.load()
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        lcd.lookup_propose(x, torch.zeros(4, dtype=torch.int64), x, 4, torch.zeros(8, dtype=torch.int64),
+                           x, x, torch.zeros(60, dtype=torch.int32))
