@@ -70,10 +70,12 @@ def load():
         L.lcd_workspace_bytes.argtypes = [i32]
         L.lcd_workspace_bytes.restype = ctypes.c_size_t
         L.lookup_propose.argtypes = [P, P, P, i32, i32, pp, P, P, P, P, P]
+        L.lookup_propose_timed.argtypes = [P, P, P, i32, i32, pp, P, P, P, P, P, P, P]
         L.fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P]
         L.greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P, P]
         L.lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P, P]
-        for f in (L.lookup_propose, L.fuse_verify_block, L.greedy_accept, L.lookup_schedule_step):
+        for f in (L.lookup_propose, L.lookup_propose_timed, L.fuse_verify_block,
+                  L.greedy_accept, L.lookup_schedule_step):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -135,15 +137,13 @@ def _check(fn, rc):
         raise LCDError(fn, rc)
 
 
-def lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end, draft,
-                   params: Params | None = None):
-    """Longest-suffix / latest-occurrence lookup and 15-token draft for every
-    request (include/lcd.h, lookup_propose)."""
+def _propose_args(hist, row_off, lens, max_len, workspace, match_len, match_end, draft, p):
     import torch
-    p = params or default_params()
     B = lens.numel()
     dev = lens.device
-    args = (
+    if workspace.numel() * workspace.element_size() < workspace_bytes(B):
+        raise ValueError("workspace too small")
+    return (
         _dev(hist, "hist", torch.int32, device=dev),
         _dev(row_off, "row_off", torch.int64, B, dev),
         _dev(lens, "lens", torch.int32, B, dev),
@@ -154,9 +154,25 @@ def lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end
         _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev),
         _stream(dev),
     )
-    if workspace.numel() * workspace.element_size() < workspace_bytes(B):
-        raise ValueError("workspace too small")
+
+
+def lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end, draft,
+                   params: Params | None = None):
+    """Longest-suffix / latest-occurrence lookup and 15-token draft for every
+    request (include/lcd.h, lookup_propose)."""
+    p = params or default_params()
+    args = _propose_args(hist, row_off, lens, max_len, workspace, match_len, match_end, draft, p)
     _check("lookup_propose", load().lookup_propose(*args))
+
+
+def lookup_propose_timed(hist, row_off, lens, max_len, workspace, match_len, match_end, draft,
+                         ev_start, ev_stop, params: Params | None = None):
+    """lookup_propose with GPU-stamped start/stop events (raw hipEvent_t handles
+    as ints, either may be 0) around its scan kernel, for profiling."""
+    p = params or default_params()
+    args = _propose_args(hist, row_off, lens, max_len, workspace, match_len, match_end, draft, p)
+    _check("lookup_propose_timed", load().lookup_propose_timed(
+        *args, ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
 
 
 def fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len,

@@ -116,6 +116,19 @@ int lookup_propose(const int32_t *hist, const int64_t *row_off, const int32_t *l
                    int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream);
 
 /*
+ * lookup_propose_timed -- for profiling only: the same work and launch
+ * configuration as lookup_propose, launched so that the GPU itself stamps the
+ * start of the first scan kernel of the call into ev_start and the end of the
+ * last one into ev_stop (both hipEvent_t created by the caller, either may be
+ * NULL).  The interval excludes host submission time, so it matches a kernel
+ * trace of the same launch.
+ */
+int lookup_propose_timed(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                         int32_t B, int32_t max_len, const lcd_params *p, void *workspace,
+                         int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream,
+                         void *ev_start, void *ev_stop);
+
+/*
  * fuse_verify_block -- article, section "第 2 步" (fusion, not overwrite).
  *
  * blk = long_mode[r] ? n_block : n_head draft slots are verified.
