@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the context-lookup drafting hot path on one MI355X.
 
-One step = lookup_propose + fuse_verify_block + greedy_accept +
-lookup_schedule_step over a whole batch (default: 64 requests of 25,000
-tokens, 32 verbatim-restatement and 32 ordinary Zipf texts, vocabulary 40,960).
+One step = lookup + fusion + greedy acceptance + scheduler update over a whole
+batch (default: 64 requests of 25,000 tokens, 32 verbatim-restatement and 32
+ordinary Zipf texts, vocabulary 40,960), through the fused lookup_decode_step
+entry point (two kernels), or with --separate through the four entry points
+lookup_propose, fuse_verify_block, greedy_accept, lookup_schedule_step.
 Inputs are resident in HBM before timing.  The batch is copied into enough
 distinct buffers (>= 320 MB) that consecutive steps never hit the 256 MB
 Infinity Cache, and the steps are replayed from a HIP graph so the host does
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-work-seconds", type=float, default=20.0,
                     help="CPU work (seconds summed over threads) for the oracle baseline; 0 = skip")
     ap.add_argument("--scan-wgs", type=int, default=0, help="lookup launch tuning (0 = auto)")
+    ap.add_argument("--separate", action="store_true",
+                    help="time the four separate entry points instead of the fused step")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="profiling aid: only N eager lookup launches over the rotating sets")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -205,29 +209,39 @@ def main():
     q, tgt = w.step_inputs(np.zeros(B, np.int64), 0)
     q_d, tgt_d = t(q), t(tgt)
     ws = lcd.alloc_workspace(B, dev)
+    dws = lcd.alloc_decode_workspace(B, max_len, dev, p)
     m = torch.empty(B, dtype=torch.int32, device=dev)
     e = torch.empty_like(m)
     d = torch.empty((B, 15), dtype=torch.int32, device=dev)
     blk = torch.empty((B, 15), dtype=torch.int32, device=dev)
     bl = torch.empty(B, dtype=torch.int32, device=dev)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
+    ln_next = torch.empty(B, dtype=torch.int32, device=dev)
     state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
     longs = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
 
     if args.kernel_only:
         for i in range(args.kernel_only):
-            lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
+            if args.separate:
+                lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
+            else:
+                lcd.lookup_decode_step(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d,
+                                       state, dws, m, e, d, blk, bl, acc, ln_next, False, p)
         torch.cuda.synchronize()
         print(json.dumps({"kernel_only_launches": args.kernel_only, "workload": w.name,
                           "tokens_per_launch": tokens, "alg_bytes_per_launch": 4 * tokens + 80 * B,
-                          "rotating_sets": R}), flush=True)
+                          "rotating_sets": R, "separate": args.separate}), flush=True)
         return
 
     def step(i):
-        lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
-        lcd.fuse_verify_block(d, m, q_d, longs[i % 2], blk, bl, p)
-        lcd.greedy_accept(blk, bl, tgt_d, acc)
-        lcd.lookup_schedule_step(state, m, acc, bl, longs[(i + 1) % 2], p)
+        if args.separate:
+            lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
+            lcd.fuse_verify_block(d, m, q_d, longs[i % 2], blk, bl, p)
+            lcd.greedy_accept(blk, bl, tgt_d, acc)
+            lcd.lookup_schedule_step(state, m, acc, bl, longs[(i + 1) % 2], p)
+        else:
+            lcd.lookup_decode_step(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d, state,
+                                   dws, m, e, d, blk, bl, acc, ln_next, False, p)
 
     # eager reference of one step, then the graphs
     for i in range(2):
@@ -277,8 +291,13 @@ def main():
     n_k = min(K, 400)
     evs = [(hev.create(), hev.create()) for _ in range(n_k)]
     for i in range(n_k):
-        lcd.lookup_propose_timed(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d,
-                                 evs[i][0], evs[i][1], p)
+        if args.separate:
+            lcd.lookup_propose_timed(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d,
+                                     evs[i][0], evs[i][1], p)
+        else:
+            lcd.lookup_decode_step_timed(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d,
+                                         state, dws, m, e, d, blk, bl, acc, evs[i][0], evs[i][1],
+                                         ln_next, False, p)
     torch.cuda.synchronize()
     durs = np.array([hev.elapsed_ms(a, b) for a, b in evs]) * 1e-3
     for a, b in evs:
@@ -288,7 +307,7 @@ def main():
 
     alg_bytes = 4 * tokens + 80 * B          # history once + row_off/len/outputs
     achieved = alg_bytes / k_avg / 1e9
-    traffic = load_traffic(w.name)
+    traffic = None if args.separate else load_traffic(w.name)
     value = K * tokens / elapsed
     out = {
         "metric": METRIC,
@@ -311,7 +330,9 @@ def main():
             "vocab": w.vocab,
             "rotating_sets": R,
             "rotating_bytes": R * set_bytes,
-            "launch": f"HIP graph of {R} steps (4 kernels each)",
+            "launch": (f"HIP graph of {R} steps, "
+                       + ("4 entry points (4 kernels) per step" if args.separate
+                          else "lookup_decode_step (2 kernels) per step")),
         },
         "lookups_per_s": round(K * B / elapsed, 1),
         "step_hbm_gbps": round(value * 4 / 1e9, 2),
@@ -323,7 +344,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "lookup_scan_kernel<4>",
+            "kernel": ("lookup_scan_kernel<4,false>" if args.separate
+                       else "lookup_scan_kernel<4,true>"),
             "kernel_us_mean": round(k_avg * 1e6, 3),
             "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, x)) * 1e6, 3)
                                       for x in (10, 50, 90)],

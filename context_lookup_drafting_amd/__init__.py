@@ -8,6 +8,8 @@ library raises.
 
 Entry points (same names as the C ABI):
   lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end, draft, params)
+  lookup_decode_step(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
+                     match_len, match_end, draft, block, block_len, accept, long_next, append, params)
   fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len, params)
   greedy_accept(block, block_len, target, accept, hist=None, row_off=None, lens=None, cap=None)
   lookup_schedule_step(state, match_len, accept, block_len, long_next, params)
@@ -72,10 +74,16 @@ def load():
         L.lookup_propose.argtypes = [P, P, P, i32, i32, pp, P, P, P, P, P]
         L.lookup_propose_timed.argtypes = [P, P, P, i32, i32, pp, P, P, P, P, P, P, P]
         L.fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P]
+        L.lcd_decode_step_workspace_bytes.argtypes = [i32, i32, pp]
+        L.lcd_decode_step_workspace_bytes.restype = ctypes.c_size_t
+        dec = [P, P, P, P, i32, i32, P, P, P, pp, P, ctypes.c_size_t, P, P, P, P, P, P, P, i32, P]
+        L.lookup_decode_step.argtypes = dec
+        L.lookup_decode_step_timed.argtypes = dec + [P, P]
         L.greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P, P]
         L.lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P, P]
         for f in (L.lookup_propose, L.lookup_propose_timed, L.fuse_verify_block,
-                  L.greedy_accept, L.lookup_schedule_step):
+                  L.greedy_accept, L.lookup_schedule_step, L.lookup_decode_step,
+                  L.lookup_decode_step_timed):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,3 +235,68 @@ def lookup_schedule_step(state, match_len, accept, block_len, long_next,
         ctypes.c_int32(B), ctypes.byref(p),
         _dev(long_next, "long_next", torch.int32, B, dev),
         _stream(dev)))
+
+
+def decode_step_workspace_bytes(B: int, max_len: int, params: Params | None = None) -> int:
+    p = params or default_params()
+    return int(load().lcd_decode_step_workspace_bytes(int(B), int(max_len), ctypes.byref(p)))
+
+
+def alloc_decode_workspace(B: int, max_len: int, device, params: Params | None = None):
+    """Workspace for lookup_decode_step (no initial contents required)."""
+    import torch
+    n = max(decode_step_workspace_bytes(B, max_len, params), 16)
+    return torch.empty((n + 7) // 8, dtype=torch.int64, device=device)
+
+
+def _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
+                 match_len, match_end, draft, block, block_len, accept, long_next, append, p):
+    import torch
+    B = lens.numel()
+    dev = lens.device
+    nul = ctypes.c_void_p(None)
+    return (
+        _dev(hist, "hist", torch.int32, device=dev),
+        _dev(row_off, "row_off", torch.int64, B, dev),
+        _dev(lens, "lens", torch.int32, B, dev),
+        _dev(cap, "cap", torch.int32, B, dev) if cap is not None else nul,
+        ctypes.c_int32(B), ctypes.c_int32(int(max_len)),
+        _dev(model_draft, "model_draft", torch.int32, B * Q_STRIDE, dev),
+        _dev(target, "target", torch.int32, B * TARGET_STRIDE, dev),
+        _dev(state, "state", torch.int32, 3 * B, dev),
+        ctypes.byref(p),
+        _dev(workspace, "workspace", workspace.dtype, device=dev),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _dev(match_len, "match_len", torch.int32, B, dev),
+        _dev(match_end, "match_end", torch.int32, B, dev),
+        _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev),
+        _dev(block, "block", torch.int32, B * DRAFT_STRIDE, dev),
+        _dev(block_len, "block_len", torch.int32, B, dev),
+        _dev(accept, "accept", torch.int32, B, dev),
+        _dev(long_next, "long_next", torch.int32, B, dev) if long_next is not None else nul,
+        ctypes.c_int32(1 if append else 0),
+        _stream(dev),
+    )
+
+
+def lookup_decode_step(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
+                       match_len, match_end, draft, block, block_len, accept, long_next=None,
+                       append=True, params: Params | None = None):
+    """One whole decode step (lookup, fusion under state's current mode, greedy
+    accept with optional append, scheduler update) in two kernels."""
+    p = params or default_params()
+    _check("lookup_decode_step", load().lookup_decode_step(*_decode_args(
+        hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,
+        match_end, draft, block, block_len, accept, long_next, append, p)))
+
+
+def lookup_decode_step_timed(hist, row_off, lens, cap, max_len, model_draft, target, state,
+                             workspace, match_len, match_end, draft, block, block_len, accept,
+                             ev_start, ev_stop, long_next=None, append=True,
+                             params: Params | None = None):
+    """lookup_decode_step with GPU-stamped events around its scan kernel."""
+    p = params or default_params()
+    _check("lookup_decode_step_timed", load().lookup_decode_step_timed(*_decode_args(
+        hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,
+        match_end, draft, block, block_len, accept, long_next, append, p),
+        ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))

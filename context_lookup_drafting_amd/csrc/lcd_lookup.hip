@@ -37,11 +37,15 @@
 #include <stdint.h>
 
 #include "lcd.h"
+#include "lcd_rules.h"
 
 namespace lcd {
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef LCD_WAVES
+#define LCD_WAVES 4
+#endif
+constexpr int kWaves = LCD_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileTok = 256;   // 64 lanes x 4 tokens
 #ifndef LCD_UNROLL
@@ -62,12 +66,6 @@ struct WsSlot {   // one per request, 16 bytes, zero between calls
 };
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-__device__ __forceinline__ int64_t uni64(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 __device__ __forceinline__ u64 ballot(bool p) { return __ballot(p); }
 
@@ -154,11 +152,23 @@ __device__ __forceinline__ int4 load_granule(const int32_t *__restrict__ hist, i
     return *reinterpret_cast<const int4 *>(hist + pos);
 }
 
-template <int PF>
+// Chunk length of a row of n > 0 tokens cut into cpr chunks: whole tiles, at
+// most 2^30 tokens (positions inside a chunk then fit in 32 bits).
+__device__ __forceinline__ int64_t chunk_tokens(int64_t n, int cpr) {
+    int64_t T = (n + cpr - 1) / cpr;
+    T = ((T + kTileTok - 1) / kTileTok) * kTileTok;
+    return T > (int64_t(1) << 30) ? (int64_t(1) << 30) : T;
+}
+
+// kPartials = false: workgroups of a request merge their keys through the
+// workspace (atomic max + arrival count) and the last one writes the result.
+// kPartials = true: each workgroup stores its key in part[r*cpr + c] and a
+// following kernel finishes the step.
+template <int PF, bool kPartials>
 __global__ void __launch_bounds__(kThreads)
 lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
                    const int32_t *__restrict__ len, int32_t cpr, ScanArgs a,
-                   WsSlot *__restrict__ ws, int32_t *__restrict__ match_len,
+                   WsSlot *__restrict__ ws, u64 *__restrict__ part, int32_t *__restrict__ match_len,
                    int32_t *__restrict__ match_end, int32_t *__restrict__ draft)
 {
     __shared__ u64 s_wkey[kWaves];
@@ -173,7 +183,7 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     const int64_t n = len[r] > 0 ? len[r] : 0;
 
     if (n == 0) {                       // empty row: no match, chunk 0 writes it
-        if (c0 == 0 && tid < LCD_DRAFT_STRIDE) {
+        if (!kPartials && c0 == 0 && tid < LCD_DRAFT_STRIDE) {
             draft[(int64_t)r * LCD_DRAFT_STRIDE + tid] = LCD_PAD;
             if (tid == 0) {
                 match_len[r] = 0;
@@ -182,14 +192,13 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
         }
         return;
     }
-    // Equal chunks of whole tiles (at most 2^30 tokens, so positions inside a
-    // chunk fit in 32 bits); a row with more chunks than the grid provides is
-    // covered by letting each workgroup take every cpr-th chunk.
-    int64_t T = (n + cpr - 1) / cpr;
-    T = ((T + kTileTok - 1) / kTileTok) * kTileTok;
-    if (T > (int64_t(1) << 30)) T = int64_t(1) << 30;
+    // Equal chunks of whole tiles; a row with more chunks than the grid
+    // provides is covered by letting each workgroup take every cpr-th chunk.
+    const int64_t T = chunk_tokens(n, cpr);
     const int contrib = (int)((n + T - 1) / T);
+    if (c0 >= contrib) return;
     const int J = a.l_max;
+    u64 wg_key = 0;                     // kPartials: best key over this workgroup's chunks
 
     for (int ch = c0; ch < contrib; ch += cpr) {
         const int64_t seg_a = (int64_t)ch * T;
@@ -286,26 +295,50 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
 
         u64 best = 0;
         if (k0 < k1) {
-            u64 psh[4];
+            // Quick test: a candidate end e needs h[e-jq] == s_jq for every
+            // jq < PF, so a tile can hold one only if some position in it, or
+            // in the previous tile's last lane, holds s_jq.  Each wave uses the
+            // suffix token that is rarest in its first tile; the choice only
+            // changes how many tiles get the full test, never the result.
+            int jq = 0;
             {
-                u64 pin[4];
-                prefilter_masks<PF>(fix_halo(halo, k0), s4, pin, psh);
+                const int4 t = fix_tile(buf[0], k0);
+                int fewest = 1 << 30;
+#pragma unroll
+                for (int j = 0; j < PF; ++j) {
+                    const int cnt = __popcll(ballot(t.x == s4[j])) + __popcll(ballot(t.y == s4[j])) +
+                                    __popcll(ballot(t.z == s4[j])) + __popcll(ballot(t.w == s4[j]));
+                    if (cnt < fewest) { fewest = cnt; jq = j; }
+                }
             }
+            const int sq = uni(jq == 0 ? s4[0] : jq == 1 ? s4[1] : jq == 2 ? s4[2] : s4[3]);
+            auto quick = [&](const int4 &t) -> u64 {
+                return ballot(t.x == sq) | ballot(t.y == sq) | ballot(t.z == sq) | ballot(t.w == sq);
+            };
+            int4 prev = fix_halo(halo, k0);          // tile before the next one processed
+            u64 carry = quick(prev) >> 63;           // a hit in its last lane
             for (int kb = k0; kb < k1; kb += kUnroll) {
                 if (kb != k0) load_batch(kb);
-                // hot loop: the 4-token test only; tiles with a survivor are
-                // marked and revisited below
+                // hot loop: quick test on every tile; flagged tiles get the
+                // full 4-token test from registers; tiles with a survivor of
+                // that are marked and extended below
                 unsigned surv = 0;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     if (kb + u < k1) {
-                        u64 P[4], sh[4];
-                        survivors(fix_tile(buf[u], kb + u), kb + u, psh, P, sh);
-                        if ((P[0] | P[1] | P[2] | P[3]) != 0) surv |= 1u << u;
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) psh[c] = sh[c];
+                        const int4 t = fix_tile(buf[u], kb + u);
+                        const u64 q = quick(t);
+                        if ((q | carry) != 0) {
+                            const int4 pt = (u == 0) ? prev : fix_tile(buf[u > 0 ? u - 1 : 0], kb + u - 1);
+                            u64 pin[4], psh[4], P[4], sh[4];
+                            prefilter_masks<PF>(pt, s4, pin, psh);
+                            survivors(t, kb + u, psh, P, sh);
+                            if ((P[0] | P[1] | P[2] | P[3]) != 0) surv |= 1u << u;
+                        }
+                        carry = q >> 63;
                     }
                 }
+                prev = fix_tile(buf[kUnroll - 1], kb + kUnroll - 1);
                 // rare path: reload a marked tile and the 16 tokens before it
                 // (both still in cache), redo its test and extend survivors
                 while (surv != 0) {
@@ -339,47 +372,103 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
         if (tid == 0) {
             u64 key = s_wkey[0];
             for (int w = 1; w < kWaves; ++w) key = s_wkey[w] > key ? s_wkey[w] : key;
-            bool last = true;
-            if (contrib > 1) {
-                // Merge across the workgroups covering this request.  Both words
-                // are only touched by device-scope atomic read-modify-writes,
-                // which the memory system performs at one coherence point per
-                // address.  Waiting for this workgroup's max to return before
-                // counting it means every max is performed before the final
-                // count is, and the last arriver reads the key only after that.
-                WsSlot *slot = ws + r;
-                if (key) __hip_atomic_fetch_max(&slot->key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __builtin_amdgcn_s_waitcnt(0);
-                const unsigned old = __hip_atomic_fetch_add(&slot->count, 1u, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
-                last = (old == (unsigned)(contrib - 1));
-                if (last) {
-                    key = __hip_atomic_exchange(&slot->key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&slot->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (kPartials) {
+                wg_key = key > wg_key ? key : wg_key;
+            } else {
+                bool last = true;
+                if (contrib > 1) {
+                    // Merge across the workgroups covering this request.  Both
+                    // words are only touched by device-scope atomic
+                    // read-modify-writes, which the memory system performs at
+                    // one coherence point per address.  Waiting for this
+                    // workgroup's max to return before counting it means every
+                    // max is performed before the final count is, and the last
+                    // arriver reads the key only after that.
+                    WsSlot *slot = ws + r;
+                    if (key) __hip_atomic_fetch_max(&slot->key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    const unsigned old = __hip_atomic_fetch_add(&slot->count, 1u, __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_AGENT);
+                    last = (old == (unsigned)(contrib - 1));
+                    if (last) {
+                        key = __hip_atomic_exchange(&slot->key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&slot->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
-            }
-            if (last) {
-                int32_t *d = draft + (int64_t)r * LCD_DRAFT_STRIDE;
-                if (key == 0) {
-                    match_len[r] = 0;
-                    match_end[r] = -1;
-                    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) d[k] = LCD_PAD;
-                } else {
+                if (last) {
                     const int m = (int)(key >> 32);
-                    const int64_t e = (int64_t)(uint32_t)key;
-                    const int64_t D = n - 1 - e;
+                    const int64_t e = key ? (int64_t)(uint32_t)key : -1;
+                    int d[LCD_DRAFT_STRIDE];
+                    lz_draft(hist + ro, n, m, e, a.k_max, d);
                     match_len[r] = m;
                     match_end[r] = (int32_t)e;
-                    int64_t idx = 0;   // k mod D
-                    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) {
-                        d[k] = (k < a.k_max) ? hist[ro + n - D + idx] : LCD_PAD;
-                        if (++idx == D) idx = 0;
-                    }
+#pragma unroll
+                    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) draft[(int64_t)r * LCD_DRAFT_STRIDE + k] = d[k];
                 }
             }
         }
         __syncthreads();
     }
+    if (kPartials && tid == 0) part[(int64_t)r * cpr + c0] = wg_key;
+}
+
+// Second kernel of the fused decode step: one lane per request reduces the
+// chunk keys, copies the draft, fuses the verify block, accepts greedily
+// (optionally appending the emitted tokens) and advances the scheduler.
+struct PostArgs {
+    int32_t k_max, append;
+    FuseArgs f;
+    SchedArgs s;
+};
+
+__global__ void __launch_bounds__(256)
+decode_post_kernel(int32_t *hist, const int64_t *__restrict__ row_off, int32_t *__restrict__ len,
+                   const int32_t *__restrict__ cap, int32_t B, int32_t cpr,
+                   const u64 *__restrict__ part, const int32_t *__restrict__ q,
+                   const int32_t *__restrict__ target, lcd_sched_state *__restrict__ state,
+                   PostArgs pa, int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
+                   int32_t *__restrict__ draft, int32_t *__restrict__ block,
+                   int32_t *__restrict__ block_len, int32_t *__restrict__ accept,
+                   int32_t *__restrict__ long_next) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= B) return;
+    const int64_t ro = row_off[r];
+    const int64_t n = len[r] > 0 ? len[r] : 0;
+    u64 key = 0;
+    if (n > 0) {
+        const int64_t T = chunk_tokens(n, cpr);
+        const int64_t contrib = (n + T - 1) / T;
+        const int cw = (int)(contrib < cpr ? contrib : cpr);
+        for (int c = 0; c < cw; ++c) {
+            const u64 k = part[(int64_t)r * cpr + c];
+            key = k > key ? k : key;
+        }
+    }
+    const int m = (int)(key >> 32);
+    const int64_t e = key ? (int64_t)(uint32_t)key : -1;
+    int d[LCD_DRAFT_STRIDE];
+    lz_draft(hist + ro, n, m, e, pa.k_max, d);
+    match_len[r] = m;
+    match_end[r] = (int32_t)e;
+#pragma unroll
+    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) draft[(int64_t)r * LCD_DRAFT_STRIDE + k] = d[k];
+
+    int qv[LCD_Q_STRIDE], tv[LCD_TARGET_STRIDE], bv[LCD_DRAFT_STRIDE];
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = q[(int64_t)r * LCD_Q_STRIDE + i];
+#pragma unroll
+    for (int i = 0; i < LCD_TARGET_STRIDE; ++i) tv[i] = target[(int64_t)r * LCD_TARGET_STRIDE + i];
+    lcd_sched_state st = state[r];
+    const int blk = fuse_row(d, m, qv, st.long_mode != 0, pa.f, bv);
+#pragma unroll
+    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) block[(int64_t)r * LCD_DRAFT_STRIDE + k] = bv[k];
+    block_len[r] = blk;
+    int acc = accept_row(bv, blk, tv);
+    if (pa.append) acc = append_row(acc, tv, hist, ro, len + r, cap[r]);
+    accept[r] = acc;
+    const int ln = schedule_row(st, m, acc, blk, pa.s);
+    state[r] = st;
+    if (long_next) long_next[r] = ln;
 }
 
 // Chunks per request.  The launch has B*cpr workgroups; by default about
@@ -399,18 +488,30 @@ int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
     return (int)cpr;
 }
 
-template <int PF>
+template <int PF, bool kPartials>
 hipError_t launch(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
-                  int cpr, ScanArgs sa, WsSlot *ws, int32_t *ml, int32_t *me, int32_t *dr,
+                  int cpr, ScanArgs sa, WsSlot *ws, u64 *part, int32_t *ml, int32_t *me, int32_t *dr,
                   hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const dim3 grid((unsigned)((int64_t)B * cpr));
     if (ev0 != nullptr || ev1 != nullptr)
-        hipExtLaunchKernelGGL(lookup_scan_kernel<PF>, grid, dim3(kThreads), 0u, st, ev0, ev1, 0u,
-                              hist, row_off, len, cpr, sa, ws, ml, me, dr);
+        hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kPartials>, grid, dim3(kThreads), 0u, st, ev0, ev1,
+                              0u, hist, row_off, len, cpr, sa, ws, part, ml, me, dr);
     else
-        hipLaunchKernelGGL(lookup_scan_kernel<PF>, grid, dim3(kThreads), 0, st,
-                           hist, row_off, len, cpr, sa, ws, ml, me, dr);
+        hipLaunchKernelGGL((lookup_scan_kernel<PF, kPartials>), grid, dim3(kThreads), 0, st,
+                           hist, row_off, len, cpr, sa, ws, part, ml, me, dr);
     return hipGetLastError();
+}
+
+template <bool kPartials>
+hipError_t launch_scan(int pf, const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                       int32_t B, int cpr, ScanArgs sa, WsSlot *ws, u64 *part, int32_t *ml,
+                       int32_t *me, int32_t *dr, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    switch (pf) {
+    case 1: return launch<1, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
+    case 2: return launch<2, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
+    case 3: return launch<3, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
+    default: return launch<4, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
+    }
 }
 
 int propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
@@ -428,14 +529,45 @@ int propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int
     const int cpr = pick_cpr(B, max_len, p->scan_wgs);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     WsSlot *ws = reinterpret_cast<WsSlot *>(workspace);
-    hipError_t err;
-    switch (pf) {
-    case 1: err = launch<1>(hist, row_off, len, B, cpr, sa, ws, match_len, match_end, draft, st, ev0, ev1); break;
-    case 2: err = launch<2>(hist, row_off, len, B, cpr, sa, ws, match_len, match_end, draft, st, ev0, ev1); break;
-    case 3: err = launch<3>(hist, row_off, len, B, cpr, sa, ws, match_len, match_end, draft, st, ev0, ev1); break;
-    default: err = launch<4>(hist, row_off, len, B, cpr, sa, ws, match_len, match_end, draft, st, ev0, ev1); break;
-    }
+    const hipError_t err = launch_scan<false>(pf, hist, row_off, len, B, cpr, sa, ws, nullptr,
+                                              match_len, match_end, draft, st, ev0, ev1);
     return err == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+
+size_t decode_workspace_bytes(int32_t B, int32_t max_len, const lcd_params *p) {
+    if (B <= 0 || p == nullptr) return 0;
+    return (size_t)B * (size_t)pick_cpr(B, max_len, p->scan_wgs) * sizeof(u64);
+}
+
+int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap, int32_t B,
+                int32_t max_len, const int32_t *model_draft, const int32_t *target,
+                lcd_sched_state *state, const lcd_params *p, void *workspace, size_t ws_bytes,
+                int32_t *match_len, int32_t *match_end, int32_t *draft, int32_t *block,
+                int32_t *block_len, int32_t *accept, int32_t *long_next, int32_t append,
+                void *stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (B < 0 || p == nullptr || max_len < 0) return LCD_EINVAL;
+    if (lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!hist || !row_off || !len || !model_draft || !target || !state || !workspace ||
+        !match_len || !match_end || !draft || !block || !block_len || !accept)
+        return LCD_EINVAL;
+    if (append && !cap) return LCD_EINVAL;
+    if (((uintptr_t)hist & 15u) != 0 || ((uintptr_t)workspace & 15u) != 0) return LCD_EINVAL;
+    if (ws_bytes < decode_workspace_bytes(B, max_len, p)) return LCD_EINVAL;
+
+    ScanArgs sa{p->l_min, p->l_max, p->k_max};
+    const int pf = p->l_min < 4 ? p->l_min : 4;
+    const int cpr = pick_cpr(B, max_len, p->scan_wgs);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    u64 *part = reinterpret_cast<u64 *>(workspace);
+    hipError_t err = launch_scan<true>(pf, hist, row_off, len, B, cpr, sa, nullptr, part, nullptr,
+                                       nullptr, nullptr, st, ev0, ev1);
+    if (err != hipSuccess) return LCD_EHIP;
+    PostArgs pa{p->k_max, append ? 1 : 0, fuse_args(p), sched_args(p)};
+    hipLaunchKernelGGL(decode_post_kernel, dim3((B + 255) / 256), dim3(256), 0, st, hist, row_off,
+                       len, cap, B, cpr, part, model_draft, target, state, pa, match_len, match_end,
+                       draft, block, block_len, accept, long_next);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
 }
 
 }  // namespace
@@ -460,4 +592,37 @@ extern "C" int lookup_propose_timed(const int32_t *hist, const int64_t *row_off,
     return lcd::propose(hist, row_off, len, B, max_len, p, workspace, match_len, match_end, draft,
                         stream, reinterpret_cast<hipEvent_t>(ev_start),
                         reinterpret_cast<hipEvent_t>(ev_stop));
+}
+
+extern "C" size_t lcd_decode_step_workspace_bytes(int32_t B, int32_t max_len, const lcd_params *p) {
+    return lcd::decode_workspace_bytes(B, max_len, p);
+}
+
+extern "C" int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len,
+                                  const int32_t *cap, int32_t B, int32_t max_len,
+                                  const int32_t *model_draft, const int32_t *target,
+                                  lcd_sched_state *state, const lcd_params *p, void *workspace,
+                                  size_t workspace_bytes, int32_t *match_len, int32_t *match_end,
+                                  int32_t *draft, int32_t *block, int32_t *block_len,
+                                  int32_t *accept, int32_t *long_next, int32_t append,
+                                  void *stream) {
+    return lcd::decode_step(hist, row_off, len, cap, B, max_len, model_draft, target, state, p,
+                            workspace, workspace_bytes, match_len, match_end, draft, block,
+                            block_len, accept, long_next, append, stream, nullptr, nullptr);
+}
+
+extern "C" int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len,
+                                        const int32_t *cap, int32_t B, int32_t max_len,
+                                        const int32_t *model_draft, const int32_t *target,
+                                        lcd_sched_state *state, const lcd_params *p,
+                                        void *workspace, size_t workspace_bytes,
+                                        int32_t *match_len, int32_t *match_end, int32_t *draft,
+                                        int32_t *block, int32_t *block_len, int32_t *accept,
+                                        int32_t *long_next, int32_t append, void *stream,
+                                        void *ev_start, void *ev_stop) {
+    return lcd::decode_step(hist, row_off, len, cap, B, max_len, model_draft, target, state, p,
+                            workspace, workspace_bytes, match_len, match_end, draft, block,
+                            block_len, accept, long_next, append, stream,
+                            reinterpret_cast<hipEvent_t>(ev_start),
+                            reinterpret_cast<hipEvent_t>(ev_stop));
 }

@@ -1,0 +1,131 @@
+// lcd_rules.h -- per-request rules of a lookup-drafting step, as device
+// functions shared by the separate step kernels and the fused decode step.
+//
+// Method: HyperQwen lookup-drafting article, sections "第 1 步" (the draft is
+// the tokens following the matched occurrence), "第 2 步" (fuse the lookup
+// draft with the draft model's proposal: head slots need a long match, or a
+// shorter one confirmed by the draft model's first tokens; tail slots take any
+// match of the tail threshold), "第 3 步" (long block entered after consecutive
+// nearly-full steps with a tail-filling match, kept for a few steps after the
+// flag drops) and the closing paragraph (greedy verification: the longest
+// block prefix equal to the target's argmax tokens is accepted).
+#ifndef LCD_RULES_H
+#define LCD_RULES_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lcd.h"
+
+namespace lcd {
+
+struct FuseArgs {
+    int32_t k_max, n_head, n_block, head_full, head_agree, agree_n, tail_min;
+};
+
+struct SchedArgs {
+    int32_t tail_min, entry_steps, sticky, near_full_slack;
+};
+
+// Draft of a match ending at e in a row h of n tokens (m > 0): the tokens after
+// the occurrence, continued LZ77-style, d[k] = h[n - D + (k mod D)], D = n-1-e,
+// for k < k_max; PAD elsewhere and for m == 0.
+__device__ inline void lz_draft(const int32_t *__restrict__ h, int64_t n, int m, int64_t e,
+                                int k_max, int (&d)[LCD_DRAFT_STRIDE]) {
+    const int64_t D = n - 1 - e;
+    int64_t idx = 0;
+#pragma unroll
+    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) {
+        d[k] = (m > 0 && k < k_max) ? h[n - D + idx] : LCD_PAD;
+        if (++idx == D) idx = 0;
+    }
+}
+
+// Verify block of one request.  Returns the number of draft slots verified.
+__device__ inline int fuse_row(const int (&d)[LCD_DRAFT_STRIDE], int m, const int (&q)[LCD_Q_STRIDE],
+                               bool is_long, const FuseArgs &a, int (&out)[LCD_DRAFT_STRIDE]) {
+    bool agree = true;
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i)
+        if (i < a.agree_n && q[i] != d[i]) agree = false;
+    const bool head = (m >= a.head_full) || (m >= a.head_agree && agree);
+    const bool tail = is_long && (m >= a.tail_min);
+    const int blk = is_long ? a.n_block : a.n_head;
+    // slots below n_head (<= 7) carry the draft model's proposal
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i) {
+        int v = LCD_PAD;
+        if (i < a.n_head) v = (head && i < a.k_max) ? d[i] : q[i];
+        else if (i < blk) v = (tail && i < a.k_max) ? d[i] : LCD_PAD;
+        out[i] = v;
+    }
+#pragma unroll
+    for (int i = LCD_Q_STRIDE; i < LCD_DRAFT_STRIDE; ++i)
+        out[i] = (i < blk && tail && i < a.k_max) ? d[i] : LCD_PAD;
+    return blk;
+}
+
+// Greedy acceptance: the longest prefix of the block (at most blk slots)
+// equal to the target's argmax tokens.
+__device__ inline int accept_row(const int (&b)[LCD_DRAFT_STRIDE], int blk,
+                                 const int (&t)[LCD_TARGET_STRIDE]) {
+    int acc = 0;
+    bool run = true;
+#pragma unroll
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) {
+        run = run && (i < blk) && (b[i] == t[i]);
+        acc += run ? 1 : 0;
+    }
+    return acc;
+}
+
+// Append the a+1 emitted tokens t[0..a] to row r when they fit in its
+// capacity; returns a, or -1 (nothing written) when they do not.
+__device__ inline int append_row(int a, const int (&t)[LCD_TARGET_STRIDE], int32_t *__restrict__ hist,
+                                 int64_t ro, int32_t *__restrict__ len_r, int32_t cap_r) {
+    const int64_t have = *len_r;
+    if (have + a + 1 > (int64_t)cap_r) return -1;
+    int32_t *dst = hist + ro + have;
+#pragma unroll
+    for (int i = 0; i < LCD_TARGET_STRIDE; ++i)
+        if (i <= a) dst[i] = t[i];
+    *len_r = (int32_t)(have + a + 1);
+    return a;
+}
+
+// Scheduler update after a step with match length m, accept a (-1 = failed
+// append) and blk verified slots; returns the next step's mode.
+__device__ inline int schedule_row(lcd_sched_state &st, int m, int a, int blk, const SchedArgs &s) {
+    const bool flag = (m >= s.tail_min) && (a >= 0) && (a >= blk - s.near_full_slack);
+    if (!st.long_mode) {
+        st.streak = flag ? st.streak + 1 : 0;
+        if (st.streak >= s.entry_steps) {
+            st.long_mode = 1;
+            st.streak = 0;
+            st.down = 0;
+        }
+    } else if (flag) {
+        st.down = 0;
+    } else {
+        st.down += 1;
+        if (st.down > s.sticky) {
+            st.long_mode = 0;
+            st.down = 0;
+            st.streak = 0;
+        }
+    }
+    return st.long_mode;
+}
+
+inline FuseArgs fuse_args(const lcd_params *p) {
+    return FuseArgs{p->k_max, p->n_head, p->n_block, p->head_full, p->head_agree, p->agree_n,
+                    p->tail_min};
+}
+
+inline SchedArgs sched_args(const lcd_params *p) {
+    return SchedArgs{p->tail_min, p->entry_steps, p->sticky, p->near_full_slack};
+}
+
+}  // namespace lcd
+
+#endif  // LCD_RULES_H

@@ -15,19 +15,12 @@
 #include <stdint.h>
 
 #include "lcd.h"
+#include "lcd_rules.h"
 
 namespace lcd {
 namespace {
 
 constexpr int kStepThreads = 256;
-
-struct FuseArgs {
-    int32_t k_max, n_head, n_block, head_full, head_agree, agree_n, tail_min;
-};
-
-struct SchedArgs {
-    int32_t tail_min, entry_steps, sticky, near_full_slack;
-};
 
 __global__ void __launch_bounds__(kStepThreads)
 fuse_kernel(const int32_t *__restrict__ draft, const int32_t *__restrict__ match_len,
@@ -35,39 +28,14 @@ fuse_kernel(const int32_t *__restrict__ draft, const int32_t *__restrict__ match
             FuseArgs a, int32_t *__restrict__ block, int32_t *__restrict__ block_len) {
     const int r = blockIdx.x * kStepThreads + threadIdx.x;
     if (r >= B) return;
-    const int32_t *d = draft + (int64_t)r * LCD_DRAFT_STRIDE;
-    const int32_t *qr = q + (int64_t)r * LCD_Q_STRIDE;
-    int32_t *out = block + (int64_t)r * LCD_DRAFT_STRIDE;
-    const int32_t m = match_len[r];
-    const bool is_long = long_mode[r] != 0;
-
-    int dv[LCD_DRAFT_STRIDE];
-    int qv[LCD_Q_STRIDE];
+    int dv[LCD_DRAFT_STRIDE], qv[LCD_Q_STRIDE], out[LCD_DRAFT_STRIDE];
 #pragma unroll
-    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) dv[i] = d[i];
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) dv[i] = draft[(int64_t)r * LCD_DRAFT_STRIDE + i];
 #pragma unroll
-    for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = qr[i];
-
-    bool agree = true;
+    for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = q[(int64_t)r * LCD_Q_STRIDE + i];
+    const int blk = fuse_row(dv, match_len[r], qv, long_mode[r] != 0, a, out);
 #pragma unroll
-    for (int i = 0; i < LCD_Q_STRIDE; ++i)
-        if (i < a.agree_n && qv[i] != dv[i]) agree = false;
-    const bool head = (m >= a.head_full) || (m >= a.head_agree && agree);
-    const bool tail = is_long && (m >= a.tail_min);
-    const int32_t blk = is_long ? a.n_block : a.n_head;
-
-    // head slots (the draft model's proposal) -- n_head <= 7 = LCD_Q_STRIDE
-#pragma unroll
-    for (int i = 0; i < LCD_Q_STRIDE; ++i) {
-        int v = LCD_PAD;
-        if (i < a.n_head) v = (head && i < a.k_max) ? dv[i] : qv[i];
-        else if (i < blk) v = (tail && i < a.k_max) ? dv[i] : LCD_PAD;
-        out[i] = v;
-    }
-    // tail slots of a long block
-#pragma unroll
-    for (int i = LCD_Q_STRIDE; i < LCD_DRAFT_STRIDE; ++i)
-        out[i] = (i < blk && tail && i < a.k_max) ? dv[i] : LCD_PAD;
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) block[(int64_t)r * LCD_DRAFT_STRIDE + i] = out[i];
     block_len[r] = blk;
 }
 
@@ -78,31 +46,13 @@ accept_kernel(const int32_t *__restrict__ block, const int32_t *__restrict__ blo
               int32_t *__restrict__ len, const int32_t *__restrict__ cap) {
     const int r = blockIdx.x * kStepThreads + threadIdx.x;
     if (r >= B) return;
-    const int32_t *b = block + (int64_t)r * LCD_DRAFT_STRIDE;
-    const int32_t *t = target + (int64_t)r * LCD_TARGET_STRIDE;
-    int tv[LCD_TARGET_STRIDE];
+    int bv[LCD_DRAFT_STRIDE], tv[LCD_TARGET_STRIDE];
 #pragma unroll
-    for (int i = 0; i < LCD_TARGET_STRIDE; ++i) tv[i] = t[i];
-    const int32_t blk = block_len[r];
-    int32_t acc = 0;
-    bool run = true;
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) bv[i] = block[(int64_t)r * LCD_DRAFT_STRIDE + i];
 #pragma unroll
-    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) {
-        run = run && (i < blk) && (b[i] == tv[i]);
-        acc += run ? 1 : 0;
-    }
-    if (hist != nullptr) {
-        const int64_t have = len[r];
-        if (have + acc + 1 > (int64_t)cap[r]) {
-            accept[r] = -1;
-            return;
-        }
-        int32_t *dst = hist + row_off[r] + have;
-#pragma unroll
-        for (int i = 0; i < LCD_TARGET_STRIDE; ++i)
-            if (i <= acc) dst[i] = tv[i];
-        len[r] = (int32_t)(have + acc + 1);
-    }
+    for (int i = 0; i < LCD_TARGET_STRIDE; ++i) tv[i] = target[(int64_t)r * LCD_TARGET_STRIDE + i];
+    int acc = accept_row(bv, block_len[r], tv);
+    if (hist != nullptr) acc = append_row(acc, tv, hist, row_off[r], len + r, cap[r]);
     accept[r] = acc;
 }
 
@@ -113,28 +63,9 @@ schedule_kernel(lcd_sched_state *__restrict__ state, const int32_t *__restrict__
     const int r = blockIdx.x * kStepThreads + threadIdx.x;
     if (r >= B) return;
     lcd_sched_state st = state[r];
-    const int32_t acc = accept[r];
-    const bool flag = (match_len[r] >= a.tail_min) && (acc >= 0) &&
-                      (acc >= block_len[r] - a.near_full_slack);
-    if (!st.long_mode) {
-        st.streak = flag ? st.streak + 1 : 0;
-        if (st.streak >= a.entry_steps) {
-            st.long_mode = 1;
-            st.streak = 0;
-            st.down = 0;
-        }
-    } else if (flag) {
-        st.down = 0;
-    } else {
-        st.down += 1;
-        if (st.down > a.sticky) {
-            st.long_mode = 0;
-            st.down = 0;
-            st.streak = 0;
-        }
-    }
+    const int ln = schedule_row(st, match_len[r], accept[r], block_len[r], a);
     state[r] = st;
-    long_next[r] = st.long_mode;
+    long_next[r] = ln;
 }
 
 inline int blocks_for(int32_t B) { return (B + kStepThreads - 1) / kStepThreads; }
@@ -181,8 +112,7 @@ extern "C" int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
     if (B == 0) return LCD_OK;
     if (!draft || !match_len || !model_draft || !long_mode || !block || !block_len)
         return LCD_EINVAL;
-    FuseArgs a{p->k_max, p->n_head, p->n_block, p->head_full, p->head_agree, p->agree_n,
-               p->tail_min};
+    const FuseArgs a = fuse_args(p);
     hipLaunchKernelGGL(fuse_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), draft, match_len, model_draft,
                        long_mode, B, a, block, block_len);
@@ -211,7 +141,7 @@ extern "C" int lookup_schedule_step(lcd_sched_state *state, const int32_t *match
     if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
     if (!state || !match_len || !accept || !block_len || !long_next) return LCD_EINVAL;
-    SchedArgs a{p->tail_min, p->entry_steps, p->sticky, p->near_full_slack};
+    const SchedArgs a = sched_args(p);
     hipLaunchKernelGGL(schedule_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), state, match_len, accept, block_len,
                        B, a, long_next);

@@ -182,6 +182,45 @@ int lookup_schedule_step(lcd_sched_state *state, const int32_t *match_len,
                          const int32_t *accept, const int32_t *block_len, int32_t B,
                          const lcd_params *p, int32_t *long_next, void *stream);
 
+/*
+ * lookup_decode_step -- one whole decode step: lookup_propose, then
+ * fuse_verify_block under each request's current mode state[r].long_mode, then
+ * greedy_accept (appending the emitted tokens when `append` is non-zero), then
+ * lookup_schedule_step; every output equals what those four calls produce in
+ * that order.  (Article sections "第 1 步" to "第 3 步" and the paragraph on
+ * losslessness, as for the four calls.)  Two kernels: the scan stores one key
+ * per (request, chunk) in `workspace`; a per-request kernel reduces the keys,
+ * copies the draft, fuses, accepts, appends and schedules.
+ *
+ * hist, row_off, len, cap   as for lookup_propose / greedy_accept; cap may be
+ *                           NULL when append == 0 (then hist and len are only read)
+ * model_draft int32[B*7], target int32[B*16]
+ * state       lcd_sched_state[B], in/out; its long_mode selects this step's block
+ * workspace   lcd_decode_step_workspace_bytes(B, max_len, p) bytes (any contents,
+ *             16-byte aligned); workspace_bytes is its size, checked
+ * outputs     match_len, match_end int32[B]; draft, block int32[B*15];
+ *             block_len, accept int32[B]; long_next int32[B] (nullable)
+ */
+size_t lcd_decode_step_workspace_bytes(int32_t B, int32_t max_len, const lcd_params *p);
+
+int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap,
+                       int32_t B, int32_t max_len, const int32_t *model_draft,
+                       const int32_t *target, lcd_sched_state *state, const lcd_params *p,
+                       void *workspace, size_t workspace_bytes, int32_t *match_len,
+                       int32_t *match_end, int32_t *draft, int32_t *block, int32_t *block_len,
+                       int32_t *accept, int32_t *long_next, int32_t append, void *stream);
+
+/* lookup_decode_step with GPU-stamped events around its scan kernel (see
+ * lookup_propose_timed); for profiling only. */
+int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len,
+                             const int32_t *cap, int32_t B, int32_t max_len,
+                             const int32_t *model_draft, const int32_t *target,
+                             lcd_sched_state *state, const lcd_params *p, void *workspace,
+                             size_t workspace_bytes, int32_t *match_len, int32_t *match_end,
+                             int32_t *draft, int32_t *block, int32_t *block_len,
+                             int32_t *accept, int32_t *long_next, int32_t append, void *stream,
+                             void *ev_start, void *ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

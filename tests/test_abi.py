@@ -117,3 +117,27 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="device tensor"):
         lcd.lookup_propose(x, torch.zeros(4, dtype=torch.int64), x, 4, torch.zeros(8, dtype=torch.int64),
                            x, x, torch.zeros(60, dtype=torch.int32))
+
+
+def test_decode_step_rejects_misuse_without_launching():
+    L = lcd.load()
+    p = lcd.default_params()
+    pp = ctypes.byref(p)
+    f = 0x10000
+    need = lcd.decode_step_workspace_bytes(8, 1000)
+    assert need == 8 * min(1024 // 8, -(-1000 // 2048)) * 8
+
+    def call(B=8, max_len=1000, cap=f, ws=f, ws_bytes=need, append=1, hist=f, prm=pp, ln=f):
+        P = _P
+        return L.lookup_decode_step(P(hist), P(f), P(ln), P(cap), B, max_len, P(f), P(f), P(f), prm,
+                                    P(ws), ws_bytes, P(f), P(f), P(f), P(f), P(f), P(f), None,
+                                    append, None)
+    assert call(B=0, hist=None, ln=None, cap=None, ws=None, ws_bytes=0) == lcd.LCD_OK
+    assert call(B=-1) == lcd.LCD_EINVAL
+    assert call(ws_bytes=need - 8) == lcd.LCD_EINVAL          # workspace too small
+    assert call(cap=None) == lcd.LCD_EINVAL                   # append needs capacities
+    assert call(hist=f + 4) == lcd.LCD_EINVAL                 # misaligned history
+    assert call(ws=None) == lcd.LCD_EINVAL
+    assert call(max_len=-5) == lcd.LCD_EINVAL
+    bad = lcd.default_params(k_max=16)
+    assert call(prm=ctypes.byref(bad)) == lcd.LCD_EINVAL
