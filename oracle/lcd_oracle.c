@@ -147,8 +147,8 @@ int oracle_fuse_verify_block(const int32_t *draft, const int32_t *match_len,
  * tokens, at most blk.  The step emits target[0..a] (a+1 tokens: the accepted
  * drafts plus the target's own token at the first mismatch, or its bonus token).
  * Optional append: when hist is non-NULL, target[0..a] is written at
- * row_off[r]+len[r] and len[r] grows by a+1; if that would exceed cap[r] the
- * request is flagged with accept = -1 and nothing is written.
+ * row_off[r]+n with n = max(len[r], 0) and len[r] becomes n+a+1; if that would
+ * exceed cap[r] the request is flagged with accept = -1 and nothing is written.
  */
 int oracle_greedy_accept(const int32_t *block, const int32_t *block_len,
                          const int32_t *target, int32_t B, int32_t *accept,
@@ -162,7 +162,7 @@ int oracle_greedy_accept(const int32_t *block, const int32_t *block_len,
         int32_t a = 0;
         while (a < blk && blkr[a] == t[a]) a++;
         if (hist != NULL) {
-            int64_t have = len[r];
+            int64_t have = len[r] > 0 ? len[r] : 0;   /* a negative length reads as an empty row */
             if (have + a + 1 > (int64_t)cap[r]) {
                 accept[r] = -1;
                 continue;
