@@ -4,7 +4,7 @@
 One step = lookup + fusion + greedy acceptance + scheduler update over a whole
 batch (default: 64 requests of 25,000 tokens, 32 verbatim-restatement and 32
 ordinary Zipf texts, vocabulary 40,960), through the fused lookup_decode_step
-entry point (two kernels), or with --separate through the four entry points
+entry point (one kernel), or with --separate through the four entry points
 lookup_propose, fuse_verify_block, greedy_accept, lookup_schedule_step.
 Inputs are resident in HBM before timing.  The batch is copied into enough
 distinct buffers (>= 320 MB) that consecutive steps never hit the 256 MB
@@ -12,9 +12,9 @@ Infinity Cache, and the steps are replayed from a HIP graph so the host does
 not throttle the launches.
 
 Printed: one JSON line with the throughput (history tokens scanned per second),
-the roofline of the dominant kernel (the lookup scan; its duration is stamped
-by the GPU on each dispatch via lookup_propose_timed) and the CPU oracle timed
-on the host's cores as a baseline.
+the roofline of the dominant kernel (the scan kernel that runs the whole step;
+its duration is stamped by the GPU on each dispatch through the *_timed entry
+point) and the CPU oracle timed on the host's cores as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c4|c5]
 """
@@ -67,6 +67,15 @@ def calibrate_copy(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}), flush=True)
+
+
+def per_request_bytes(separate):
+    """Algorithmic bytes per request besides the history, for the timed kernel:
+    the lookup alone reads row_off and len (12) and writes match_len, match_end
+    and the draft (68); the whole step also reads the proposal, target tokens
+    and scheduler state (104) and writes the block, block_len, accept, state
+    and long_next (84)."""
+    return 80 if separate else 80 + 104 + 84
 
 
 def kernel_source_hash():
@@ -229,7 +238,8 @@ def main():
                                        state, dws, m, e, d, blk, bl, acc, ln_next, False, p)
         torch.cuda.synchronize()
         print(json.dumps({"kernel_only_launches": args.kernel_only, "workload": w.name,
-                          "tokens_per_launch": tokens, "alg_bytes_per_launch": 4 * tokens + 80 * B,
+                          "tokens_per_launch": tokens,
+                          "alg_bytes_per_launch": 4 * tokens + per_request_bytes(args.separate) * B,
                           "rotating_sets": R, "separate": args.separate}), flush=True)
         return
 
@@ -305,7 +315,7 @@ def main():
         hev.destroy(b)
     k_avg = float(durs.mean())
 
-    alg_bytes = 4 * tokens + 80 * B          # history once + row_off/len/outputs
+    alg_bytes = 4 * tokens + per_request_bytes(args.separate) * B
     achieved = alg_bytes / k_avg / 1e9
     traffic = None if args.separate else load_traffic(w.name)
     value = K * tokens / elapsed
@@ -332,7 +342,7 @@ def main():
             "rotating_bytes": R * set_bytes,
             "launch": (f"HIP graph of {R} steps, "
                        + ("4 entry points (4 kernels) per step" if args.separate
-                          else "lookup_decode_step (2 kernels) per step")),
+                          else "lookup_decode_step (1 kernel) per step")),
         },
         "lookups_per_s": round(K * B / elapsed, 1),
         "step_hbm_gbps": round(value * 4 / 1e9, 2),
@@ -344,8 +354,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": ("lookup_scan_kernel<4,false>" if args.separate
-                       else "lookup_scan_kernel<4,true>"),
+            "kernel": ("lookup_scan_kernel<4,kPropose>" if args.separate
+                       else "lookup_scan_kernel<4,kStep>"),
             "kernel_us_mean": round(k_avg * 1e6, 3),
             "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, x)) * 1e6, 3)
                                       for x in (10, 50, 90)],

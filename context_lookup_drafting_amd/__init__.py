@@ -243,10 +243,10 @@ def decode_step_workspace_bytes(B: int, max_len: int, params: Params | None = No
 
 
 def alloc_decode_workspace(B: int, max_len: int, device, params: Params | None = None):
-    """Workspace for lookup_decode_step (no initial contents required)."""
+    """Zero-filled workspace for lookup_decode_step (kept zero by every call)."""
     import torch
     n = max(decode_step_workspace_bytes(B, max_len, params), 16)
-    return torch.empty((n + 7) // 8, dtype=torch.int64, device=device)
+    return torch.zeros((n + 7) // 8, dtype=torch.int64, device=device)
 
 
 def _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
@@ -283,7 +283,7 @@ def lookup_decode_step(hist, row_off, lens, cap, max_len, model_draft, target, s
                        match_len, match_end, draft, block, block_len, accept, long_next=None,
                        append=True, params: Params | None = None):
     """One whole decode step (lookup, fusion under state's current mode, greedy
-    accept with optional append, scheduler update) in two kernels."""
+    accept with optional append, scheduler update) in one kernel."""
     p = params or default_params()
     _check("lookup_decode_step", load().lookup_decode_step(*_decode_args(
         hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,

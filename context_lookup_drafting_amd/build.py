@@ -17,10 +17,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblcd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed-FP32 instructions are disabled for every HIP translation unit.
+# Packed-FP32 instructions are disabled for every HIP translation unit.  The
+# atomic optimizer is off: it turns a single lane's fetch-and-add into a wave
+# reduction that waits for the returned value immediately, which would put a
+# full memory round trip in front of the scan's first loads.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", INCLUDE,
 ]

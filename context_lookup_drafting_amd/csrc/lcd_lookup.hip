@@ -1,36 +1,46 @@
 // lcd_lookup.hip -- batched context lookup (longest suffix, latest earlier
-// occurrence, LZ-style draft copy) for MI355X / gfx950.
+// occurrence, LZ-style draft copy) and the one-kernel decode step, for MI355X /
+// gfx950.
 //
 // Method: HyperQwen lookup-drafting article, section "第 1 步": each decode
 // step, for every request, scan that request's own token history for the most
 // recent earlier occurrence of its longest current suffix of 4..12 tokens
 // (overlap with the suffix allowed) and draft the tokens that follow it; most
-// candidates are rejected by a 4-token test, so extending the survivors costs
-// almost nothing.  The article runs one Triton program per request on a
-// consumer GPU; here the design is built around gfx950 instead:
+// candidates fail a 4-token test, so extending the survivors costs almost
+// nothing.  The article runs one Triton program per request on a consumer GPU;
+// the design here is built around gfx950 instead:
 //
-//  * The whole batch is one flat token space (prefix sums of the lengths).  It
-//    is cut into gridDim.x equal ranges, one per workgroup, so a ragged batch
-//    is as balanced as a uniform one and a launch always fills all 256 CUs.
-//    Each workgroup computes the prefix sums itself in LDS from len[] (no
-//    extra launch, no host knowledge of the lengths).
-//  * Within a range each wave streams contiguous 256-token tiles: lane i holds
-//    tokens 4i..4i+3 of the tile from one 16-byte load, so one wave-wide load
-//    moves 1 KiB, fully coalesced, 16-byte aligned.
-//  * The 4-token rejection test runs on wave-wide bit masks: one v_cmp per
-//    (component, suffix token) gives a 64-bit ballot, and the masks are
-//    shifted by whole lanes to line up positions e, e-1, e-2, e-3.  The test
-//    costs 4 compares per token and no divergence; tiles with no survivor
-//    (nearly all of them) go straight to the next tile on a scalar branch.
-//  * Survivor tiles extend all candidates at once with the same mask algebra
-//    up to l_max tokens (lane shifts of up to 4, carried from the previous
-//    tile), and pick the longest, then latest, candidate with scalar bit scans.
-//  * A packed key (length << 32 | end) orders candidates; workgroups covering
-//    one request merge keys with a 64-bit atomic max, and the last one to
-//    arrive (counted with an acquire-release atomic) writes the result and the
-//    15-token draft and re-zeroes the two workspace words it used.
+//  * The candidate ends of every request are cut into chunks of T tokens
+//    (whole 256-token tiles; the host derives T from the longest row), one
+//    workgroup of four waves per chunk, B x cpr workgroups per launch.
+//  * A decode-step scan is short, so dependent memory round trips cost as much
+//    as the bytes: the row offset and length are loaded together, then the 16
+//    suffix tokens (one per lane) and the wave's first batch of tiles go into
+//    the vector memory queue back to back, so the suffix is waited for alone
+//    and each tile as it lands.
+//  * Lane i of a wave holds tokens 4i..4i+3 of a tile from one 16-byte load:
+//    one wave-wide load moves 1 KiB, fully coalesced.
+//  * Quick test: a tile can hold a candidate only if it, or the last lane of
+//    the tile before it, holds the suffix token that is rarest in the wave's
+//    first tile -- four compares per lane and one scalar branch per tile.
+//  * Flagged tiles get the full 4-token test on wave-wide bit masks (one v_cmp
+//    per component and suffix token; masks shifted by whole lanes line up the
+//    positions e, e-1, e-2, e-3), and survivors are extended up to l_max
+//    tokens with the same mask algebra, from the registers holding the tile
+//    and the one before it.
+//  * A packed key (length, end) orders candidates.  Every workgroup of a
+//    request takes an arrival ticket when it starts (one atomic add, in flight
+//    during its scan), and at the end publishes its best key together with the
+//    15 tokens that follow that match (read back while they are still in its
+//    cache) as tagged 8-byte words in its own workspace slot.  The workgroup
+//    holding the last ticket gathers the slots -- it only waits for
+//    workgroups that started before it, so the wait always ends -- and thus
+//    has the winning draft without another dependent load.  It finishes the
+//    request with one wave (draft copy and, in the decode step, fusion,
+//    acceptance, append and scheduler update) and re-zeroes the workspace.
 //
-// No MFMA: the work is integer compares on a stream; HBM bandwidth bounds it.
+// No MFMA: the work is integer compares on a stream; HBM bandwidth and memory
+// latency bound it.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -55,15 +65,29 @@ constexpr int kUnroll = LCD_UNROLL;   // tiles loaded ahead by each wave
 
 typedef unsigned long long u64;
 
+// Match key: end (relative to the row) in bits 0..30, length in bits 31..35;
+// larger keys are longer, then later, matches.
+constexpr int kLenShift = 31;
+constexpr u64 kEndMask = (1ull << kLenShift) - 1;
+
+// Workspace of one request: the arrival-ticket counter, a pad word, then one
+// slot per workgroup of 16 words: units 0..14 hold the staged draft tokens as
+// kTokValid | token, unit 15 holds kKeyValid | key.  Zero means "not written".
+constexpr int kMaxCpr = 64;                               // workgroups per request, at most
+constexpr int kSlotWords = 16;
+constexpr int kReqWords = 2 + kMaxCpr * kSlotWords;
+constexpr u64 kKeyValid = 1ull << 63;
+constexpr u64 kTokValid = 1ull << 32;
+constexpr int kPollMax = 1 << 20;                         // gathering polls, at most
+constexpr int kBufferWord3 = 0x00020000;                  // gfx9 buffer descriptor, dword 3
+constexpr int kNoTile = 1 << 19;                          // a tile index past every descriptor
+
 struct ScanArgs {
+    int32_t cpr;               // workgroups per request
+    int32_t T;                 // chunk length in candidate ends, a multiple of kTileTok
     int32_t l_min, l_max, k_max;
 };
-
-struct WsSlot {   // one per request, 16 bytes, zero between calls
-    u64 key;
-    unsigned int count;
-    unsigned int pad;
-};
+// (The kernel takes cpr and T as separate leading arguments.)
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -110,28 +134,59 @@ __device__ __forceinline__ void prefilter_masks(const int4 &t, const int (&s)[4]
     }
 }
 
-// Extend the prefilter survivors M[c] of tile t (previous tile pt) one suffix
-// token at a time, up to J tokens, while some candidate still matches.  Returns
-// the largest length reached and leaves in M the candidates matching it.
+// Prefilter survivors of tile t (previous tile pt) whose tile index is kt,
+// restricted to candidate ends in [c_lo, c_hi).  The shifted masks line up
+// position e-j with e one lane up; their lane 0 needs the last lane of the
+// previous tile, so only that lane of pt is read.
 template <int PF>
-__device__ __forceinline__ int extend(const int4 &t, const int4 &pt, const int (&sj16)[LCD_MAX_SUFFIX], int J, u64 M[4]) {
+__device__ __forceinline__ void survivors(const int4 &t, const int4 &pt, const int (&s)[4], int kt,
+                                          int c_lo, int c_hi, int lane, u64 (&P)[4]) {
+    u64 in[4], sh[4];
+    prefilter_masks<PF>(t, s, in, sh);
+    const int p63[4] = {0, __builtin_amdgcn_readlane(pt.y, 63), __builtin_amdgcn_readlane(pt.z, 63),
+                        __builtin_amdgcn_readlane(pt.w, 63)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        bool top = true;                     // lane 63 of pt passes the shifted part for c
+#pragma unroll
+        for (int j = c + 1; j < PF; ++j) top = top && (p63[c - j + 4] == s[j]);
+        P[c] = in[c] & ((sh[c] << 1) | (top ? 1ull : 0ull));
+    }
+    const int A = kTileTok * kt;
+    if (A < c_lo || A + kTileTok > c_hi) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int x = A + 4 * lane + c;
+            P[c] &= ballot(x >= c_lo && x < c_hi);
+        }
+    }
+}
+
+// Extend the survivors M[c] of tile t (previous tile pt), which match PF
+// suffix tokens, one token at a time while some candidate still matches, up
+// to J tokens; sv holds suffix token s_j in lane j.  Returns the length
+// reached and leaves in M the candidates reaching it.  Fully unrolled: a loop
+// here, inside the unrolled tile loop, would make the compiler wait for every
+// load in flight at its header.
+template <int PF>
+__device__ __forceinline__ int extend(const int4 &t, const int4 &pt, int sv, int J, u64 (&M)[4]) {
     int L = PF;
     bool alive = true;
 #pragma unroll
     for (int j = PF; j < LCD_MAX_SUFFIX; ++j) {
         if (alive && j < J) {
-            const int sj = sj16[j];
+            const int sj = __builtin_amdgcn_readlane(sv, j);
             u64 N[4];
             u64 any = 0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int k = (j - c + 3) >> 2;      // lanes back: ceil((j-c)/4)
+                const int k = (j - c + 3) >> 2;      // lanes back: ceil((j-c)/4), 0..4
                 const int cc = (c - j) & 3;          // component of position e-j
                 const u64 cur = ballot(tok(t, cc) == sj);
                 u64 term = cur;
                 if (k > 0) {
-                    const u64 prev = ballot(tok(pt, cc) == sj);
-                    term = (cur << k) | (prev >> (64 - k));
+                    const u64 prv = ballot(tok(pt, cc) == sj);
+                    term = (cur << k) | (prv >> (64 - k));
                 }
                 N[c] = M[c] & term;
                 any |= N[c];
@@ -148,153 +203,254 @@ __device__ __forceinline__ int extend(const int4 &t, const int4 &pt, const int (
     return L;
 }
 
+// A register copy the compiler cannot fold away: the copy, not the source,
+// lives on, so a load can reuse the source's registers (a folded copy would
+// make the compiler load elsewhere and wait for the data to move it back).
+__device__ __forceinline__ int4 copy_tile(const int4 &t) {
+    int4 c;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c.x) : "v"(t.x));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c.y) : "v"(t.y));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c.z) : "v"(t.z));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c.w) : "v"(t.w));
+    return c;
+}
+
 __device__ __forceinline__ int4 load_granule(const int32_t *__restrict__ hist, int64_t pos) {
     return *reinterpret_cast<const int4 *>(hist + pos);
 }
 
-// Chunk length of a row of n > 0 tokens cut into cpr chunks: whole tiles, at
-// most 2^30 tokens (positions inside a chunk then fit in 32 bits).
-__device__ __forceinline__ int64_t chunk_tokens(int64_t n, int cpr) {
-    int64_t T = (n + cpr - 1) / cpr;
-    T = ((T + kTileTok - 1) / kTileTok) * kTileTok;
-    return T > (int64_t(1) << 30) ? (int64_t(1) << 30) : T;
+// Kernel modes.  kPropose: the lookup only.  kStep: the whole decode step; the
+// workgroup that finishes a request also fuses the verify block, accepts
+// greedily (optionally appending) and advances the scheduler.
+enum { kPropose = 0, kStep = 1 };
+
+// Inputs and outputs of the rest of the decode step (kStep only).  hist_w and
+// len_w alias hist and len: a request's row is appended to only after every
+// workgroup of that request has merged, i.e. finished reading it, and the
+// append lies past every position any scan of the row reads.
+struct StepIO {
+    int32_t *hist_w;
+    int32_t *len_w;
+    const int32_t *cap;
+    const int32_t *q;
+    const int32_t *target;
+    lcd_sched_state *state;
+    int32_t *block, *block_len, *accept, *long_next;
+    FuseArgs f;
+    SchedArgs s;
+    int32_t append;
+};
+
+// Per-request inputs of the rest of the step, one value per lane of the
+// finishing wave: lanes 0..6 the draft model's proposal, 7..22 the target
+// tokens, 23..25 the scheduler state, 26 the row capacity.  Loaded when the
+// workgroup starts, so they are in flight during the scan.
+__device__ __forceinline__ int load_step_input(int r, int lane, const StepIO &io) {
+    const int32_t *src = io.q + (int64_t)r * LCD_Q_STRIDE;     // lanes past 26 re-read q[0]
+    if (lane < LCD_Q_STRIDE)
+        src = io.q + (int64_t)r * LCD_Q_STRIDE + lane;
+    else if (lane < LCD_Q_STRIDE + LCD_TARGET_STRIDE)
+        src = io.target + (int64_t)r * LCD_TARGET_STRIDE + (lane - LCD_Q_STRIDE);
+    else if (lane < LCD_Q_STRIDE + LCD_TARGET_STRIDE + 3)
+        src = reinterpret_cast<const int32_t *>(io.state) + (int64_t)r * 3 +
+              (lane - LCD_Q_STRIDE - LCD_TARGET_STRIDE);
+    else if (lane == LCD_Q_STRIDE + LCD_TARGET_STRIDE + 3 && io.append)
+        src = io.cap + r;
+    return *src;
 }
 
-// kPartials = false: workgroups of a request merge their keys through the
-// workspace (atomic max + arrival count) and the last one writes the result.
-// kPartials = true: each workgroup stores its key in part[r*cpr + c] and a
-// following kernel finishes the step.
-template <int PF, bool kPartials>
+__device__ __forceinline__ u64 wave_max(u64 v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const u64 o = __shfl_xor(v, off);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Result of request r (row of n >= 0 tokens at ro) given its best key, run by
+// one whole wave: lane k < 15 holds tok = h[e+1+min(k, D-1)], D = n-1-e, the
+// tokens following the match.  Writes the match and draft and, in kStep mode,
+// the rest of the step (sin: the per-lane step inputs).
+template <int kMode>
+__device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin, int lane,
+                                               int64_t ro, int n, int k_max,
+                                               int32_t *__restrict__ match_len,
+                                               int32_t *__restrict__ match_end,
+                                               int32_t *__restrict__ draft, const StepIO &io) {
+    const int m = key ? (int)(key >> kLenShift) : 0;
+    const int e = key ? (int)(key & kEndMask) : -1;
+    const int D = key ? n - 1 - e : 1;
+    // LZ-style copy: d[k] = h[n - D + (k mod D)], the tok of lane (k mod D)
+    const int kk = lane < LCD_DRAFT_STRIDE ? lane : 0;
+    int dk = __shfl(tok, kk % D);
+    dk = (m > 0 && lane < k_max) ? dk : LCD_PAD;
+    if (lane < LCD_DRAFT_STRIDE) draft[(int64_t)r * LCD_DRAFT_STRIDE + lane] = dk;
+    if (lane == 0) {
+        match_len[r] = m;
+        match_end[r] = e;
+    }
+    if (kMode == kStep) {
+        int d[LCD_DRAFT_STRIDE], qv[LCD_Q_STRIDE], tv[LCD_TARGET_STRIDE];
+#pragma unroll
+        for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) d[k] = __builtin_amdgcn_readlane(dk, k);
+#pragma unroll
+        for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = __builtin_amdgcn_readlane(sin, i);
+#pragma unroll
+        for (int i = 0; i < LCD_TARGET_STRIDE; ++i)
+            tv[i] = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + i);
+        lcd_sched_state st;
+        st.long_mode = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE);
+        st.streak = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE + 1);
+        st.down = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE + 2);
+        const int32_t capr = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE + 3);
+        if (lane == 0) {
+            int bv[LCD_DRAFT_STRIDE];
+            const int blk = fuse_row(d, m, qv, st.long_mode != 0, io.f, bv);
+#pragma unroll
+            for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) io.block[(int64_t)r * LCD_DRAFT_STRIDE + k] = bv[k];
+            io.block_len[r] = blk;
+            int acc = accept_row(bv, blk, tv);
+            if (io.append) acc = append_row(acc, tv, io.hist_w, ro, n, io.len_w + r, capr);
+            io.accept[r] = acc;
+            const int ln = schedule_row(st, m, acc, blk, io.s);
+            io.state[r] = st;
+            if (io.long_next) io.long_next[r] = ln;
+        }
+    }
+}
+
+template <int PF, int kMode>
 __global__ void __launch_bounds__(kThreads)
 lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
-                   const int32_t *__restrict__ len, int32_t cpr, ScanArgs a,
-                   WsSlot *__restrict__ ws, u64 *__restrict__ part, int32_t *__restrict__ match_len,
-                   int32_t *__restrict__ match_end, int32_t *__restrict__ draft)
+                   const int32_t *__restrict__ len, int32_t cpr, int32_t T, ScanArgs a,
+                   u64 *__restrict__ ws,
+                   int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
+                   int32_t *__restrict__ draft, StepIO io)
 {
     __shared__ u64 s_wkey[kWaves];
+    __shared__ u64 s_units[kMaxCpr * kSlotWords];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    // workgroup = (request r, chunk c); cpr chunks per request
-    const int r = blockIdx.x / cpr;
-    const int c0 = blockIdx.x - r * cpr;
+    const int wave = uni(tid >> 6);   // wave-uniform
+    // workgroup = (request r, chunk c0)
+    const int r = (int)(blockIdx.x / (unsigned)cpr);
+    const int c0 = (int)blockIdx.x - r * cpr;
+    const int sin = (kMode == kStep && wave == 0) ? load_step_input(r, lane, io) : 0;
     const int64_t ro = row_off[r];
-    const int64_t n = len[r] > 0 ? len[r] : 0;
-
-    if (n == 0) {                       // empty row: no match, chunk 0 writes it
-        if (!kPartials && c0 == 0 && tid < LCD_DRAFT_STRIDE) {
-            draft[(int64_t)r * LCD_DRAFT_STRIDE + tid] = LCD_PAD;
-            if (tid == 0) {
-                match_len[r] = 0;
-                match_end[r] = -1;
-            }
-        }
+    const int32_t lr = len[r];
+    const int n = lr > 0 ? lr : 0;
+    const int nc = n - 1;             // candidate ends 0..n-2
+    if (nc <= 0) {                    // no earlier position: chunk 0 finishes the request
+        if (c0 == 0 && wave == 0)
+            finish_request<kMode>(r, 0, 0, sin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
         return;
     }
-    // Equal chunks of whole tiles; a row with more chunks than the grid
-    // provides is covered by letting each workgroup take every cpr-th chunk.
-    const int64_t T = chunk_tokens(n, cpr);
-    const int contrib = (int)((n + T - 1) / T);
-    if (c0 >= contrib) return;
+    if ((int64_t)c0 * T >= nc) return;                  // past the row's last chunk
+    const int contrib = (int)(((unsigned)nc + (unsigned)T - 1u) / (unsigned)T);
+    const int P = contrib < cpr ? contrib : cpr;      // workgroups taking part
     const int J = a.l_max;
-    u64 wg_key = 0;                     // kPartials: best key over this workgroup's chunks
+    u64 *__restrict__ req = ws + (int64_t)r * kReqWords;
+    // Arrival ticket of this workgroup, taken by lane 0 and read back only at
+    // the end (from lane 0): the other lanes' value is left unspecified so
+    // that no register copy of the result -- which would wait for it -- is
+    // needed here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wsometimes-uninitialized"
+#pragma clang diagnostic ignored "-Wuninitialized"
+    unsigned long long ticket;
+    if (P > 1 && tid == 0)
+        ticket = __hip_atomic_fetch_add(req, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+    // suffix token s_j = h[n-1-j] in lane j (lanes >= 16 repeat s_15, filler 0
+    // past the row start); the load is the first in the vector memory queue
+    int sv;
+    {
+        const int js = lane < LCD_MAX_SUFFIX ? lane : LCD_MAX_SUFFIX - 1;
+        const int sp = n - 1 - js;
+        sv = hist[ro + (sp > 0 ? sp : 0)];
+    }
+
+    u64 best = 0;                     // this wave's best key over its chunks
+    // One chunk per workgroup when every row fits in cpr chunks of T; a longer
+    // row is covered by letting each workgroup take every cpr-th chunk.
     for (int ch = c0; ch < contrib; ch += cpr) {
-        const int64_t seg_a = (int64_t)ch * T;
-        const int64_t seg_b = (seg_a + T < n) ? seg_a + T : n;
+        const unsigned seg_a = (unsigned)ch * (unsigned)T;               // < 2^31
+        const unsigned seg_b = min(seg_a + (unsigned)T, (unsigned)nc);
+        const bool head = (seg_a == 0);                                   // holds the row start
 
-        // Candidate ends of this segment, as positions relative to X0 (the
+        // Candidate ends of this chunk, as positions relative to X0 (the
         // 16-byte granule holding the first one); this wave's tiles.
         const int64_t cand_lo = ro + seg_a;
         const int64_t X0 = cand_lo & ~(int64_t)3;
         const int32_t *__restrict__ hb = hist + X0;                        // uniform base
-        const int c_lo = (int)(cand_lo - X0);                              // 0..3
-        const int c_hi = (int)(ro + (seg_b < n - 1 ? seg_b : n - 1) - X0); // exclusive
-        const int r_lo = (ro - X0 < -(1 << 30)) ? -(1 << 30) : (int)(ro - X0);   // row start
-        const int nt = c_hi > c_lo ? (c_hi + kTileTok - 1) / kTileTok : 0;
+        const int c_lo = (int)(cand_lo - X0);                              // 0..3 (the row start if head)
+        const int c_hi = c_lo + (int)(seg_b - seg_a);                      // exclusive
+        const int nt = (c_hi + kTileTok - 1) / kTileTok;                   // >= 1
         const int tpw = (nt + kWaves - 1) / kWaves;
         const int k0 = uni(tpw * wave);
         const int k1 = uni(min(k0 + tpw, nt));
         const int g_last = (c_hi - 1) & ~3;        // last granule with a candidate
-        const int g_first = r_lo & ~3;             // first granule of the row (if >= X0-16)
 
-        // suffix s_j = h[n-1-j] through the scalar cache (filler 0 past the row)
-        int s16[LCD_MAX_SUFFIX];
-        if (n >= LCD_MAX_SUFFIX) {
-            const int32_t *__restrict__ sp = hist + (ro + n - LCD_MAX_SUFFIX);
-#pragma unroll
-            for (int j = 0; j < LCD_MAX_SUFFIX; ++j) s16[j] = sp[LCD_MAX_SUFFIX - 1 - j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < LCD_MAX_SUFFIX; ++j) s16[j] = (j < n) ? hist[ro + n - 1 - j] : 0;
-        }
-        // Loads never leave the row: lanes whose granule lies past the last
-        // candidate re-read the last candidate's granule, halo lanes whose
-        // granule lies before the row re-read the row's first granule.
+        // Tiles are read through a buffer descriptor covering exactly the
+        // chunk's granules: the hardware range check turns reads past the last
+        // candidate's granule into zeros (those positions are never
+        // candidates), so no load leaves the chunk.  In the head chunk the
+        // halo before the first tile re-reads granule 0 (and is masked).
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(hb), 0, (g_last + 4) * 4, kBufferWord3);
         auto load_tile = [&](int kt) -> int4 {
-            const int off = min(kTileTok * kt + 4 * lane, g_last);
-            return load_granule(hb, off);
+            return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rsrc, kTileTok * 4 * kt + 16 * lane, 0, 0));
         };
-        auto load_halo = [&](int kt) -> int4 {   // 16 tokens before tile kt, lanes 60..63
-            const int off = max(kTileTok * kt - kTileTok + 4 * max(lane, 60), g_first);
-            return load_granule(hb, off);
-        };
-        // every wave issues the halo and a full batch, even past its last tile
-        // (re-reading a tile it owns, or the segment's last one), so the loads
-        // are unconditional and can be waited for one at a time
         const int kl = (k1 > k0) ? k1 - 1 : nt - 1;
         int4 buf[kUnroll];
-        int4 halo = make_int4(0, 0, 0, 0);
-        auto load_batch = [&](int kb) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) buf[u] = load_tile(min(kb + u, kl));
-        };
-        if (nt > 0) {                      // uniform over the workgroup
-            halo = load_halo(min(k0, kl));
-            load_batch(min(k0, kl));
+        int4 halo;                                 // 16 tokens before tile k0 (lanes 60..63)
+        {
+            const int off = kTileTok * min(k0, kl) - kTileTok + 4 * max(lane, 60);
+            halo = load_granule(hb, head ? max(off, 0) : off);
         }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) buf[u] = load_tile(min(k0 + u, kl));
 
+        // The suffix is needed now; the empty asm keeps its lane reads here,
+        // behind the tile loads, instead of hoisted ahead of them.
+        asm volatile("" : "+v"(sv));
+        sv = lane < n ? sv : 0;
+        int s16[LCD_MAX_SUFFIX];
+#pragma unroll
+        for (int j = 0; j < LCD_MAX_SUFFIX; ++j) s16[j] = __builtin_amdgcn_readlane(sv, j);
         int s4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) s4[j] = s16[j];
-        // a value equal to no suffix token stands in for tokens before the row
-        int sent = s16[0] + 1;
-        for (int it = 0; it <= LCD_MAX_SUFFIX; ++it) {
-            bool hit = false;
+        // a value equal to no suffix token stands in for tokens before the row:
+        // one below the smallest, else one above the largest, else searched
+        int smin = s16[0], smax = s16[0];
 #pragma unroll
-            for (int j = 0; j < LCD_MAX_SUFFIX; ++j) hit |= (s16[j] == sent);
-            if (!hit) break;
-            ++sent;
+        for (int j = 1; j < LCD_MAX_SUFFIX; ++j) {
+            smin = s16[j] < smin ? s16[j] : smin;
+            smax = s16[j] > smax ? s16[j] : smax;
         }
-        // tokens at positions before the row start become `sent`
-        auto fix_tile = [&](int4 t, int kt) -> int4 {
-            const int A = kTileTok * kt;
-            return (A < r_lo) ? mask_before(t, r_lo - A - 4 * lane, sent) : t;
-        };
-        auto fix_halo = [&](int4 t, int kt) -> int4 {
-            const int A = kTileTok * kt - kTileTok;
-            return (A < r_lo) ? mask_before(t, r_lo - A - 4 * lane, sent) : t;
-        };
-        // prefilter survivors of tile kt (tokens t), given the shifted masks of
-        // the tile before it; also returns this tile's shifted masks
-        auto survivors = [&](const int4 &t, int kt, const u64 (&psh)[4], u64 (&P)[4], u64 (&sh)[4]) {
-            u64 in[4];
-            prefilter_masks<PF>(t, s4, in, sh);
+        int sent = smin != INT32_MIN ? smin - 1 : smax + 1;
+        if (smin == INT32_MIN && smax == INT32_MAX) {
+            sent = INT32_MIN + 1;
+            for (int it = 0; it <= LCD_MAX_SUFFIX; ++it) {
+                bool hit = false;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) P[c] = in[c] & ((sh[c] << 1) | (psh[c] >> 63));
-            const int A = kTileTok * kt;
-            if (A < c_lo || A + kTileTok > c_hi) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int x = A + 4 * lane + c;
-                    P[c] &= ballot(x >= c_lo && x < c_hi);
-                }
+                for (int j = 0; j < LCD_MAX_SUFFIX; ++j) hit |= (s16[j] == sent);
+                if (!hit) break;
+                ++sent;
             }
-        };
+        }
 
-        u64 best = 0;
         if (k0 < k1) {
+            // Only the head chunk's first tile and the halo before it can hold
+            // positions before the row start; they become `sent`.
+            if (head && k0 == 0) {
+                halo = make_int4(sent, sent, sent, sent);
+                if (c_lo > 0) buf[0] = mask_before(buf[0], c_lo - 4 * lane, sent);
+            }
             // Quick test: a candidate end e needs h[e-jq] == s_jq for every
             // jq < PF, so a tile can hold one only if some position in it, or
             // in the previous tile's last lane, holds s_jq.  Each wave uses the
@@ -302,7 +458,7 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
             // changes how many tiles get the full test, never the result.
             int jq = 0;
             {
-                const int4 t = fix_tile(buf[0], k0);
+                const int4 t = buf[0];
                 int fewest = 1 << 30;
 #pragma unroll
                 for (int j = 0; j < PF; ++j) {
@@ -315,203 +471,171 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
             auto quick = [&](const int4 &t) -> u64 {
                 return ballot(t.x == sq) | ballot(t.y == sq) | ballot(t.z == sq) | ballot(t.w == sq);
             };
-            int4 prev = fix_halo(halo, k0);          // tile before the next one processed
+            int4 prev = halo;                        // the tile before the next one processed
             u64 carry = quick(prev) >> 63;           // a hit in its last lane
-            for (int kb = k0; kb < k1; kb += kUnroll) {
-                if (kb != k0) load_batch(kb);
-                // hot loop: quick test on every tile; flagged tiles get the
-                // full 4-token test from registers; tiles with a survivor of
-                // that are marked and extended below
-                unsigned surv = 0;
+            // Test tile kt (tokens t) against its predecessor prev.
+            auto test_tile = [&](const int4 &t, int kt) {
+                const u64 q = quick(t);
+                if ((q | carry) != 0) {
+                    u64 P[4];
+                    survivors<PF>(t, prev, s4, kt, c_lo, c_hi, lane, P);
+                    if ((P[0] | P[1] | P[2] | P[3]) != 0) {
+                        const int L = extend<PF>(t, prev, sv, J, P);
+                        if (L >= a.l_min) {
+                            int ebest = -1;
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                if (P[c] != 0) {
+                                    const int e = 4 * (63 - __clzll(P[c])) + c;
+                                    ebest = e > ebest ? e : ebest;
+                                }
+                            }
+                            const int64_t e_abs = X0 + kTileTok * (int64_t)kt + ebest;
+                            const u64 key = ((u64)L << kLenShift) | (u64)(uint32_t)(e_abs - ro);
+                            best = key > best ? key : best;
+                        }
+                    }
+                }
+                carry = q >> 63;
+                prev = copy_tile(t);                 // frees the slot's registers for a refill
+            };
+            // Each wave keeps kUnroll tiles in flight.  While tiles remain
+            // beyond the current round, every slot is refilled with the tile
+            // kUnroll ahead as soon as its own tile has been tested (a refill
+            // past the wave's range points outside the descriptor: zeros, no
+            // memory access), so the loads form one regular sequence.
+            int kb = k0;
+            for (; kb + kUnroll < k1; kb += kUnroll) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    if (kb + u < k1) {
-                        const int4 t = fix_tile(buf[u], kb + u);
-                        const u64 q = quick(t);
-                        if ((q | carry) != 0) {
-                            const int4 pt = (u == 0) ? prev : fix_tile(buf[u > 0 ? u - 1 : 0], kb + u - 1);
-                            u64 pin[4], psh[4], P[4], sh[4];
-                            prefilter_masks<PF>(pt, s4, pin, psh);
-                            survivors(t, kb + u, psh, P, sh);
-                            if ((P[0] | P[1] | P[2] | P[3]) != 0) surv |= 1u << u;
-                        }
-                        carry = q >> 63;
-                    }
-                }
-                prev = fix_tile(buf[kUnroll - 1], kb + kUnroll - 1);
-                // rare path: reload a marked tile and the 16 tokens before it
-                // (both still in cache), redo its test and extend survivors
-                while (surv != 0) {
-                    const int kt = kb + __builtin_ctz(surv);
-                    surv &= surv - 1;
-                    const int4 t = fix_tile(load_tile(kt), kt);
-                    const int4 pt = fix_halo(load_halo(kt), kt);
-                    u64 pin[4], ppsh[4], P[4], sh[4];
-                    prefilter_masks<PF>(pt, s4, pin, ppsh);
-                    survivors(t, kt, ppsh, P, sh);
-                    const int L = extend<PF>(t, pt, s16, J, P);
-                    if (L >= a.l_min) {
-                        int ebest = -1;
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            if (P[c] != 0) {
-                                const int e = 4 * (63 - __clzll(P[c])) + c;
-                                ebest = e > ebest ? e : ebest;
-                            }
-                        }
-                        const int64_t e_abs = X0 + kTileTok * (int64_t)kt + ebest;
-                        const u64 key = ((u64)L << 32) | (u64)(uint32_t)(e_abs - ro);
-                        best = key > best ? key : best;
-                    }
+                    test_tile(buf[u], kb + u);
+                    const int nx = kb + u + kUnroll;
+                    buf[u] = load_tile(nx < k1 ? nx : kNoTile);
                 }
             }
-        }
-
-        if (lane == 0) s_wkey[wave] = best;
-        __syncthreads();
-        if (tid == 0) {
-            u64 key = s_wkey[0];
-            for (int w = 1; w < kWaves; ++w) key = s_wkey[w] > key ? s_wkey[w] : key;
-            if (kPartials) {
-                wg_key = key > wg_key ? key : wg_key;
-            } else {
-                bool last = true;
-                if (contrib > 1) {
-                    // Merge across the workgroups covering this request.  Both
-                    // words are only touched by device-scope atomic
-                    // read-modify-writes, which the memory system performs at
-                    // one coherence point per address.  Waiting for this
-                    // workgroup's max to return before counting it means every
-                    // max is performed before the final count is, and the last
-                    // arriver reads the key only after that.
-                    WsSlot *slot = ws + r;
-                    if (key) __hip_atomic_fetch_max(&slot->key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __builtin_amdgcn_s_waitcnt(0);
-                    const unsigned old = __hip_atomic_fetch_add(&slot->count, 1u, __ATOMIC_RELAXED,
-                                                                __HIP_MEMORY_SCOPE_AGENT);
-                    last = (old == (unsigned)(contrib - 1));
-                    if (last) {
-                        key = __hip_atomic_exchange(&slot->key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(&slot->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-                if (last) {
-                    const int m = (int)(key >> 32);
-                    const int64_t e = key ? (int64_t)(uint32_t)key : -1;
-                    int d[LCD_DRAFT_STRIDE];
-                    lz_draft(hist + ro, n, m, e, a.k_max, d);
-                    match_len[r] = m;
-                    match_end[r] = (int32_t)e;
+            // the last round: the remaining tiles are in the slots already
 #pragma unroll
-                    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) draft[(int64_t)r * LCD_DRAFT_STRIDE + k] = d[k];
+            for (int u = 0; u < kUnroll; ++u)
+                if (kb + u < k1) test_tile(buf[u], kb + u);
+        }
+        // Nothing is in flight here; saying so keeps the compiler from waiting
+        // on the next chunk's loads for registers this chunk's loads used.
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+
+    if (lane == 0) s_wkey[wave] = best;
+    __syncthreads();
+    if (wave != 0) return;
+    u64 key = s_wkey[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) key = s_wkey[w] > key ? s_wkey[w] : key;
+    // the tokens following this workgroup's best match, lane k: h[e+1+min(k, D-1)]
+    int tok = 0;
+    if (key != 0) {
+        const int e = (int)(key & kEndMask);
+        const int D = nc - e;                                  // n-1-e >= 1
+        tok = hist[ro + e + 1 + (lane < D ? lane : D - 1)];
+    }
+    if (P > 1) {
+        u64 *__restrict__ slots = req + 2;
+        const u64 unit = lane < kSlotWords - 1 ? (kTokValid | (u64)(uint32_t)tok) : (kKeyValid | key);
+        const int my_ticket = uni((int)ticket);    // lane 0 took it (P > 1)
+#pragma clang diagnostic pop
+        if (my_ticket != P - 1) {                  // not the last to start: publish, leave
+            if (lane < kSlotWords)
+                __hip_atomic_store(slots + c0 * kSlotWords + lane, unit, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        // Last to start: every other workgroup taking part has started, and
+        // publishes without waiting for anything, so the gathering ends.
+        if (lane < kSlotWords) s_units[c0 * kSlotWords + lane] = unit;
+        const int nu = P * kSlotWords;
+        bool all = false;
+        for (int tries = 0; tries < kPollMax && !all; ++tries) {
+            bool ok = true;
+            for (int u = lane; u < nu; u += 64) {
+                if (u / kSlotWords != c0) {
+                    const u64 v = __hip_atomic_load(slots + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_units[u] = v;
+                    ok = ok && (v != 0);
                 }
             }
+            all = ballot(!ok) == 0;
         }
-        __syncthreads();
+        // re-zero the request's workspace for the next call
+        for (int u = lane; u < nu; u += 64)
+            __hip_atomic_store(slots + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // best key over the slots (keys of different slots differ unless zero)
+        const u64 ks = lane < P ? (s_units[lane * kSlotWords + kSlotWords - 1] & ~kKeyValid) : 0;
+        key = wave_max(ks);
+        const u64 at = ballot(lane < P && ks == key);
+        const int w = at ? (int)__builtin_ctzll(at) : 0;
+        tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
+        if (!all) key = 0;                          // gathering gave up: report no match
     }
-    if (kPartials && tid == 0) part[(int64_t)r * cpr + c0] = wg_key;
+    finish_request<kMode>(r, key, tok, sin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
 }
 
-// Second kernel of the fused decode step: one lane per request reduces the
-// chunk keys, copies the draft, fuses the verify block, accepts greedily
-// (optionally appending the emitted tokens) and advances the scheduler.
-struct PostArgs {
-    int32_t k_max, append;
-    FuseArgs f;
-    SchedArgs s;
-};
-
-__global__ void __launch_bounds__(256)
-decode_post_kernel(int32_t *hist, const int64_t *__restrict__ row_off, int32_t *__restrict__ len,
-                   const int32_t *__restrict__ cap, int32_t B, int32_t cpr,
-                   const u64 *__restrict__ part, const int32_t *__restrict__ q,
-                   const int32_t *__restrict__ target, lcd_sched_state *__restrict__ state,
-                   PostArgs pa, int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
-                   int32_t *__restrict__ draft, int32_t *__restrict__ block,
-                   int32_t *__restrict__ block_len, int32_t *__restrict__ accept,
-                   int32_t *__restrict__ long_next) {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= B) return;
-    const int64_t ro = row_off[r];
-    const int64_t n = len[r] > 0 ? len[r] : 0;
-    u64 key = 0;
-    if (n > 0) {
-        const int64_t T = chunk_tokens(n, cpr);
-        const int64_t contrib = (n + T - 1) / T;
-        const int cw = (int)(contrib < cpr ? contrib : cpr);
-        for (int c = 0; c < cw; ++c) {
-            const u64 k = part[(int64_t)r * cpr + c];
-            key = k > key ? k : key;
-        }
-    }
-    const int m = (int)(key >> 32);
-    const int64_t e = key ? (int64_t)(uint32_t)key : -1;
-    int d[LCD_DRAFT_STRIDE];
-    lz_draft(hist + ro, n, m, e, pa.k_max, d);
-    match_len[r] = m;
-    match_end[r] = (int32_t)e;
-#pragma unroll
-    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) draft[(int64_t)r * LCD_DRAFT_STRIDE + k] = d[k];
-
-    int qv[LCD_Q_STRIDE], tv[LCD_TARGET_STRIDE], bv[LCD_DRAFT_STRIDE];
-#pragma unroll
-    for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = q[(int64_t)r * LCD_Q_STRIDE + i];
-#pragma unroll
-    for (int i = 0; i < LCD_TARGET_STRIDE; ++i) tv[i] = target[(int64_t)r * LCD_TARGET_STRIDE + i];
-    lcd_sched_state st = state[r];
-    const int blk = fuse_row(d, m, qv, st.long_mode != 0, pa.f, bv);
-#pragma unroll
-    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) block[(int64_t)r * LCD_DRAFT_STRIDE + k] = bv[k];
-    block_len[r] = blk;
-    int acc = accept_row(bv, blk, tv);
-    if (pa.append) acc = append_row(acc, tv, hist, ro, len + r, cap[r]);
-    accept[r] = acc;
-    const int ln = schedule_row(st, m, acc, blk, pa.s);
-    state[r] = st;
-    if (long_next) long_next[r] = ln;
-}
-
-// Chunks per request.  The launch has B*cpr workgroups; by default about
-// 1024 of them (4 per CU) with at least 2048 tokens per chunk.
+// Workgroups per request.  By default about 512 per launch (two per CU), with
+// chunks of at least 2048 and at most 32768 tokens of the longest row.
 int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
     int64_t cpr;
     if (scan_wgs > 0) {
         cpr = scan_wgs / B;
     } else {
-        cpr = 1024 / B;
-        const int64_t by_len = ((int64_t)max_len + 2047) / 2048;
-        if (cpr > by_len) cpr = by_len;
+        cpr = (512 + B / 2) / B;
+        const int64_t most = ((int64_t)max_len + 2047) / 2048;
+        const int64_t least = ((int64_t)max_len + 32767) / 32768;
+        if (cpr > most) cpr = most;
+        if (cpr < least) cpr = least;
     }
     if (cpr < 1) cpr = 1;
+    if (cpr > kMaxCpr) cpr = kMaxCpr;
     const int64_t cap = (int64_t(1) << 31) / ((int64_t)B > 0 ? B : 1) - 1;
     if (cpr > cap) cpr = cap;
     return (int)cpr;
 }
 
-template <int PF, bool kPartials>
+// Chunk length: the longest row's candidate ends (max_len - 1) split over cpr
+// chunks, in whole tiles, at most 2^30 so chunk-relative positions fit in 32 bits.
+int32_t chunk_len(int32_t max_len, int cpr) {
+    const int64_t nc = max_len > 1 ? (int64_t)max_len - 1 : 1;
+    int64_t T = (nc + cpr - 1) / cpr;
+    T = (T + kTileTok - 1) / kTileTok * kTileTok;
+    return (int32_t)(T < (int64_t(1) << 30) ? T : (int64_t(1) << 30));
+}
+
+template <int PF, int kMode>
 hipError_t launch(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
-                  int cpr, ScanArgs sa, WsSlot *ws, u64 *part, int32_t *ml, int32_t *me, int32_t *dr,
+                  ScanArgs sa, u64 *ws, int32_t *ml, int32_t *me, int32_t *dr, const StepIO &io,
                   hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    const dim3 grid((unsigned)((int64_t)B * cpr));
+    const dim3 grid((unsigned)((int64_t)B * sa.cpr));
     if (ev0 != nullptr || ev1 != nullptr)
-        hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kPartials>, grid, dim3(kThreads), 0u, st, ev0, ev1,
-                              0u, hist, row_off, len, cpr, sa, ws, part, ml, me, dr);
+        hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kMode>, grid, dim3(kThreads), 0u, st, ev0, ev1,
+                              0u, hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
     else
-        hipLaunchKernelGGL((lookup_scan_kernel<PF, kPartials>), grid, dim3(kThreads), 0, st,
-                           hist, row_off, len, cpr, sa, ws, part, ml, me, dr);
+        hipLaunchKernelGGL((lookup_scan_kernel<PF, kMode>), grid, dim3(kThreads), 0, st,
+                           hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
     return hipGetLastError();
 }
 
-template <bool kPartials>
+template <int kMode>
 hipError_t launch_scan(int pf, const int32_t *hist, const int64_t *row_off, const int32_t *len,
-                       int32_t B, int cpr, ScanArgs sa, WsSlot *ws, u64 *part, int32_t *ml,
-                       int32_t *me, int32_t *dr, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                       int32_t B, ScanArgs sa, u64 *ws, int32_t *ml, int32_t *me, int32_t *dr,
+                       const StepIO &io, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     switch (pf) {
-    case 1: return launch<1, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
-    case 2: return launch<2, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
-    case 3: return launch<3, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
-    default: return launch<4, kPartials>(hist, row_off, len, B, cpr, sa, ws, part, ml, me, dr, st, ev0, ev1);
+    case 1: return launch<1, kMode>(hist, row_off, len, B, sa, ws, ml, me, dr, io, st, ev0, ev1);
+    case 2: return launch<2, kMode>(hist, row_off, len, B, sa, ws, ml, me, dr, io, st, ev0, ev1);
+    case 3: return launch<3, kMode>(hist, row_off, len, B, sa, ws, ml, me, dr, io, st, ev0, ev1);
+    default: return launch<4, kMode>(hist, row_off, len, B, sa, ws, ml, me, dr, io, st, ev0, ev1);
     }
+}
+
+ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
+    const int cpr = pick_cpr(B, max_len, p->scan_wgs);
+    return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max};
 }
 
 int propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
@@ -524,19 +648,17 @@ int propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int
         return LCD_EINVAL;
     if (((uintptr_t)hist & 15u) != 0 || ((uintptr_t)workspace & 15u) != 0) return LCD_EINVAL;
 
-    ScanArgs sa{p->l_min, p->l_max, p->k_max};
     const int pf = p->l_min < 4 ? p->l_min : 4;
-    const int cpr = pick_cpr(B, max_len, p->scan_wgs);
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    WsSlot *ws = reinterpret_cast<WsSlot *>(workspace);
-    const hipError_t err = launch_scan<false>(pf, hist, row_off, len, B, cpr, sa, ws, nullptr,
-                                              match_len, match_end, draft, st, ev0, ev1);
+    const StepIO io{};
+    const hipError_t err = launch_scan<kPropose>(pf, hist, row_off, len, B, scan_args(B, max_len, p),
+                                                 reinterpret_cast<u64 *>(workspace), match_len,
+                                                 match_end, draft, io,
+                                                 reinterpret_cast<hipStream_t>(stream), ev0, ev1);
     return err == hipSuccess ? LCD_OK : LCD_EHIP;
 }
 
-size_t decode_workspace_bytes(int32_t B, int32_t max_len, const lcd_params *p) {
-    if (B <= 0 || p == nullptr) return 0;
-    return (size_t)B * (size_t)pick_cpr(B, max_len, p->scan_wgs) * sizeof(u64);
+size_t workspace_bytes(int32_t B) {
+    return B > 0 ? (size_t)B * kReqWords * sizeof(u64) : 0;
 }
 
 int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap, int32_t B,
@@ -553,29 +675,22 @@ int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32
         return LCD_EINVAL;
     if (append && !cap) return LCD_EINVAL;
     if (((uintptr_t)hist & 15u) != 0 || ((uintptr_t)workspace & 15u) != 0) return LCD_EINVAL;
-    if (ws_bytes < decode_workspace_bytes(B, max_len, p)) return LCD_EINVAL;
+    if (ws_bytes < workspace_bytes(B)) return LCD_EINVAL;
 
-    ScanArgs sa{p->l_min, p->l_max, p->k_max};
     const int pf = p->l_min < 4 ? p->l_min : 4;
-    const int cpr = pick_cpr(B, max_len, p->scan_wgs);
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    u64 *part = reinterpret_cast<u64 *>(workspace);
-    hipError_t err = launch_scan<true>(pf, hist, row_off, len, B, cpr, sa, nullptr, part, nullptr,
-                                       nullptr, nullptr, st, ev0, ev1);
-    if (err != hipSuccess) return LCD_EHIP;
-    PostArgs pa{p->k_max, append ? 1 : 0, fuse_args(p), sched_args(p)};
-    hipLaunchKernelGGL(decode_post_kernel, dim3((B + 255) / 256), dim3(256), 0, st, hist, row_off,
-                       len, cap, B, cpr, part, model_draft, target, state, pa, match_len, match_end,
-                       draft, block, block_len, accept, long_next);
-    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+    StepIO io{hist, len, cap, model_draft, target, state, block, block_len, accept, long_next,
+              fuse_args(p), sched_args(p), append ? 1 : 0};
+    const hipError_t err = launch_scan<kStep>(pf, hist, row_off, len, B, scan_args(B, max_len, p),
+                                              reinterpret_cast<u64 *>(workspace), match_len,
+                                              match_end, draft, io,
+                                              reinterpret_cast<hipStream_t>(stream), ev0, ev1);
+    return err == hipSuccess ? LCD_OK : LCD_EHIP;
 }
 
 }  // namespace
 }  // namespace lcd
 
-extern "C" size_t lcd_workspace_bytes(int32_t B) {
-    return B > 0 ? (size_t)B * sizeof(lcd::WsSlot) : 0;
-}
+extern "C" size_t lcd_workspace_bytes(int32_t B) { return lcd::workspace_bytes(B); }
 
 extern "C" int lookup_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
                               int32_t B, int32_t max_len, const lcd_params *p, void *workspace,
@@ -595,7 +710,8 @@ extern "C" int lookup_propose_timed(const int32_t *hist, const int64_t *row_off,
 }
 
 extern "C" size_t lcd_decode_step_workspace_bytes(int32_t B, int32_t max_len, const lcd_params *p) {
-    return lcd::decode_workspace_bytes(B, max_len, p);
+    (void)max_len;
+    return p != nullptr ? lcd::workspace_bytes(B) : 0;
 }
 
 extern "C" int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len,

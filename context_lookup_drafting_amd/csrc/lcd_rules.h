@@ -1,8 +1,7 @@
 // lcd_rules.h -- per-request rules of a lookup-drafting step, as device
 // functions shared by the separate step kernels and the fused decode step.
 //
-// Method: HyperQwen lookup-drafting article, sections "第 1 步" (the draft is
-// the tokens following the matched occurrence), "第 2 步" (fuse the lookup
+// Method: HyperQwen lookup-drafting article, sections "第 2 步" (fuse the lookup
 // draft with the draft model's proposal: head slots need a long match, or a
 // shorter one confirmed by the draft model's first tokens; tail slots take any
 // match of the tail threshold), "第 3 步" (long block entered after consecutive
@@ -26,20 +25,6 @@ struct FuseArgs {
 struct SchedArgs {
     int32_t tail_min, entry_steps, sticky, near_full_slack;
 };
-
-// Draft of a match ending at e in a row h of n tokens (m > 0): the tokens after
-// the occurrence, continued LZ77-style, d[k] = h[n - D + (k mod D)], D = n-1-e,
-// for k < k_max; PAD elsewhere and for m == 0.
-__device__ inline void lz_draft(const int32_t *__restrict__ h, int64_t n, int m, int64_t e,
-                                int k_max, int (&d)[LCD_DRAFT_STRIDE]) {
-    const int64_t D = n - 1 - e;
-    int64_t idx = 0;
-#pragma unroll
-    for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) {
-        d[k] = (m > 0 && k < k_max) ? h[n - D + idx] : LCD_PAD;
-        if (++idx == D) idx = 0;
-    }
-}
 
 // Verify block of one request.  Returns the number of draft slots verified.
 __device__ inline int fuse_row(const int (&d)[LCD_DRAFT_STRIDE], int m, const int (&q)[LCD_Q_STRIDE],
@@ -79,11 +64,11 @@ __device__ inline int accept_row(const int (&b)[LCD_DRAFT_STRIDE], int blk,
     return acc;
 }
 
-// Append the a+1 emitted tokens t[0..a] to row r when they fit in its
-// capacity; returns a, or -1 (nothing written) when they do not.
+// Append the a+1 emitted tokens t[0..a] to row r, which holds have >= 0
+// tokens, when they fit in its capacity; returns a, or -1 (nothing written)
+// when they do not.
 __device__ inline int append_row(int a, const int (&t)[LCD_TARGET_STRIDE], int32_t *__restrict__ hist,
-                                 int64_t ro, int32_t *__restrict__ len_r, int32_t cap_r) {
-    const int64_t have = *len_r;
+                                 int64_t ro, int64_t have, int32_t *__restrict__ len_r, int32_t cap_r) {
     if (have + a + 1 > (int64_t)cap_r) return -1;
     int32_t *dst = hist + ro + have;
 #pragma unroll

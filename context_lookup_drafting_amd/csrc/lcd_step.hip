@@ -52,7 +52,10 @@ accept_kernel(const int32_t *__restrict__ block, const int32_t *__restrict__ blo
 #pragma unroll
     for (int i = 0; i < LCD_TARGET_STRIDE; ++i) tv[i] = target[(int64_t)r * LCD_TARGET_STRIDE + i];
     int acc = accept_row(bv, block_len[r], tv);
-    if (hist != nullptr) acc = append_row(acc, tv, hist, row_off[r], len + r, cap[r]);
+    if (hist != nullptr) {
+        const int32_t have = len[r];
+        acc = append_row(acc, tv, hist, row_off[r], have > 0 ? have : 0, len + r, cap[r]);
+    }
     accept[r] = acc;
 }
 

@@ -79,10 +79,14 @@ void lcd_default_params(lcd_params *p);
 /* Returns LCD_OK when *p is in range, LCD_EINVAL otherwise (host only). */
 int lcd_check_params(const lcd_params *p);
 
-/* Bytes of device workspace lookup_propose needs for B requests (16 per
- * request).  The workspace must be zero-filled once before its first use;
- * every completed call leaves it zero-filled again.  Concurrent calls must
- * not share a workspace. */
+/* Device workspace per request: an arrival counter and one 128-byte slot for
+ * each of up to 64 workgroups scanning the request. */
+#define LCD_WORKSPACE_PER_REQUEST 8208
+
+/* Bytes of device workspace lookup_propose needs for B requests
+ * (B * LCD_WORKSPACE_PER_REQUEST).  The workspace must be zero-filled once
+ * before its first use; every completed call leaves it zero-filled again.
+ * Concurrent calls must not share a workspace. */
 size_t lcd_workspace_bytes(int32_t B);
 
 /*
@@ -152,8 +156,9 @@ int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
  * accept[r] = the largest a <= block_len[r] with block[r*15+i] ==
  * target[r*16+i] for every i < a.  The step emits target[r*16 + 0..a]
  * (a+1 tokens).  When hist is non-NULL those a+1 tokens are appended at
- * hist[row_off[r] + len[r]] and len[r] grows by a+1; if len[r]+a+1 > cap[r]
- * nothing is written for that request and accept[r] = -1.  row_off, len and
+ * hist[row_off[r] + n], n = max(len[r], 0), and len[r] becomes n+a+1; if
+ * n+a+1 > cap[r] nothing is written for that request and accept[r] = -1.
+ * row_off, len and
  * cap are only read when hist is non-NULL.
  *
  * block int32[B*15], block_len int32[B], target int32[B*16],
@@ -188,16 +193,19 @@ int lookup_schedule_step(lcd_sched_state *state, const int32_t *match_len,
  * greedy_accept (appending the emitted tokens when `append` is non-zero), then
  * lookup_schedule_step; every output equals what those four calls produce in
  * that order.  (Article sections "第 1 步" to "第 3 步" and the paragraph on
- * losslessness, as for the four calls.)  Two kernels: the scan stores one key
- * per (request, chunk) in `workspace`; a per-request kernel reduces the keys,
- * copies the draft, fuses, accepts, appends and schedules.
+ * losslessness, as for the four calls.)  One kernel: the workgroups covering a
+ * request merge their match keys in `workspace`, and the one whose merge
+ * completes the request copies the draft, fuses, accepts, appends and
+ * schedules it.
  *
  * hist, row_off, len, cap   as for lookup_propose / greedy_accept; cap may be
  *                           NULL when append == 0 (then hist and len are only read)
  * model_draft int32[B*7], target int32[B*16]
  * state       lcd_sched_state[B], in/out; its long_mode selects this step's block
- * workspace   lcd_decode_step_workspace_bytes(B, max_len, p) bytes (any contents,
- *             16-byte aligned); workspace_bytes is its size, checked
+ * workspace   lcd_decode_step_workspace_bytes(B, max_len, p) bytes (as for
+ *             lookup_propose), 16-byte aligned, zero-filled before its first use and
+ *             left zero-filled by every completed call; workspace_bytes is its
+ *             size, checked.  Concurrent calls must not share it.
  * outputs     match_len, match_end int32[B]; draft, block int32[B*15];
  *             block_len, accept int32[B]; long_next int32[B] (nullable)
  */

@@ -49,7 +49,7 @@ def test_param_ranges_rejected(bad):
 
 def test_workspace_bytes():
     assert lcd.workspace_bytes(0) == 0
-    assert lcd.workspace_bytes(64) == 64 * 16
+    assert lcd.workspace_bytes(64) == 64 * 8208      # LCD_WORKSPACE_PER_REQUEST
 
 
 def _P(v):
@@ -115,7 +115,8 @@ def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(ValueError, match="device tensor"):
-        lcd.lookup_propose(x, torch.zeros(4, dtype=torch.int64), x, 4, torch.zeros(8, dtype=torch.int64),
+        lcd.lookup_propose(x, torch.zeros(4, dtype=torch.int64), x, 4,
+                           torch.zeros(4 * 8208 // 8, dtype=torch.int64),
                            x, x, torch.zeros(60, dtype=torch.int32))
 
 
@@ -125,7 +126,7 @@ def test_decode_step_rejects_misuse_without_launching():
     pp = ctypes.byref(p)
     f = 0x10000
     need = lcd.decode_step_workspace_bytes(8, 1000)
-    assert need == 8 * min(1024 // 8, -(-1000 // 2048)) * 8
+    assert need == 8 * 8208           # LCD_WORKSPACE_PER_REQUEST
 
     def call(B=8, max_len=1000, cap=f, ws=f, ws_bytes=need, append=1, hist=f, prm=pp, ln=f):
         P = _P
