@@ -20,14 +20,17 @@
 //    and each tile as it lands.
 //  * Lane i of a wave holds tokens 4i..4i+3 of a tile from one 16-byte load:
 //    one wave-wide load moves 1 KiB, fully coalesced.
-//  * Quick test: a tile can hold a candidate only if it, or the last lane of
-//    the tile before it, holds the suffix token that is rarest in the wave's
-//    first tile -- four compares per lane and one scalar branch per tile.
-//  * Flagged tiles get the full 4-token test on wave-wide bit masks (one v_cmp
-//    per component and suffix token; masks shifted by whole lanes line up the
-//    positions e, e-1, e-2, e-3), and survivors are extended up to l_max
-//    tokens with the same mask algebra, from the registers holding the tile
-//    and the one before it.
+//  * Quick test: a tile can hold a candidate only if it holds the rarest
+//    adjacent pair of suffix tokens (s_j, s_j+1), possibly straddling the tile
+//    before it, or the tile before it holds one in its last lane: eight
+//    compares per lane and one scalar branch per tile.  A wave whose pair
+//    turns out to be common drops the quick test and runs the full one.
+//  * Flagged tiles get the full 4-token test: each lane receives the previous
+//    lane's last three tokens by one wave-wide DPP lane shift, compares the
+//    four tokens ending at each of its positions, and one ballot per
+//    component gives the wave-uniform survivor masks.  Survivors are extended
+//    up to l_max tokens with ballot masks shifted by whole lanes, from the
+//    registers holding the tile and the one before it.
 //  * A packed key (length, end) orders candidates.  Every workgroup of a
 //    request takes an arrival ticket when it starts (one atomic add, in flight
 //    during its scan), and at the end publishes its best key together with the
@@ -81,6 +84,7 @@ constexpr u64 kTokValid = 1ull << 32;
 constexpr int kPollMax = 1 << 20;                         // gathering polls, at most
 constexpr int kBufferWord3 = 0x00020000;                  // gfx9 buffer descriptor, dword 3
 constexpr int kNoTile = 1 << 19;                          // a tile index past every descriptor
+constexpr int kFullAfter = 4;                             // flagged tiles before a wave drops the quick test
 
 struct ScanArgs {
     int32_t cpr;               // workgroups per request
@@ -107,50 +111,32 @@ __device__ __forceinline__ int4 mask_before(int4 t, int rel, int sent) {
     return t;
 }
 
-// Prefilter masks of one tile for a PF-token test (PF <= 4).  Bit i of the
-// masks for component c stands for the candidate end at tile position 4i+c.
-//   in[c] = [token(4i+c-j) == s_j for all j<PF, j<=c]     (same lane)
-//   sh[c] = [token(4i+c-j+4) == s_j for all j<PF, j>c]    (lane i-1's
-//           tokens, so this mask is shifted up one lane before use)
-// Equalities are combined per lane with xor/or, then one ballot per mask
-// gives a wave-uniform 64-bit mask.
-template <int PF>
-__device__ __forceinline__ void prefilter_masks(const int4 &t, const int (&s)[4], u64 in[4], u64 sh[4]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        unsigned x = 0, y = 0;
-        bool has_y = false;
-#pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            if (j <= c) {
-                x |= (unsigned)(tok(t, c - j) ^ s[j]);
-            } else {
-                y |= (unsigned)(tok(t, c - j + 4) ^ s[j]);
-                has_y = true;
-            }
-        }
-        in[c] = ballot(x == 0);
-        sh[c] = has_y ? ballot(y == 0) : ~0ull;
-    }
-}
-
 // Prefilter survivors of tile t (previous tile pt) whose tile index is kt,
-// restricted to candidate ends in [c_lo, c_hi).  The shifted masks line up
-// position e-j with e one lane up; their lane 0 needs the last lane of the
-// previous tile, so only that lane of pt is read.
+// restricted to candidate ends in [c_lo, c_hi): bit i of P[c] is set when the
+// PF tokens ending at position 4i+c equal s_0..s_PF-1.  Positions before the
+// lane's own granule are the previous lane's last three tokens, brought over
+// by one wave-wide lane shift (lane 0 takes the previous tile's lane 63), so
+// every test is a per-lane compare and one ballot per component.
+constexpr int kDppWaveShr1 = 0x138;          // DPP: lane i reads lane i-1
+
 template <int PF>
 __device__ __forceinline__ void survivors(const int4 &t, const int4 &pt, const int (&s)[4], int kt,
                                           int c_lo, int c_hi, int lane, u64 (&P)[4]) {
-    u64 in[4], sh[4];
-    prefilter_masks<PF>(t, s, in, sh);
-    const int p63[4] = {0, __builtin_amdgcn_readlane(pt.y, 63), __builtin_amdgcn_readlane(pt.z, 63),
-                        __builtin_amdgcn_readlane(pt.w, 63)};
+    const int q1 = __builtin_amdgcn_update_dpp(__builtin_amdgcn_readlane(pt.y, 63), t.y, kDppWaveShr1, 0xf, 0xf, false);
+    const int q2 = __builtin_amdgcn_update_dpp(__builtin_amdgcn_readlane(pt.z, 63), t.z, kDppWaveShr1, 0xf, 0xf, false);
+    const int q3 = __builtin_amdgcn_update_dpp(__builtin_amdgcn_readlane(pt.w, 63), t.w, kDppWaveShr1, 0xf, 0xf, false);
+    // token at position 4i+c-j: component c-j of this lane, or component
+    // c-j+4 (1..3) of the previous lane
+    auto at = [&](int c, int j) -> int {
+        const int k = c - j;
+        return k >= 0 ? tok(t, k) : (k == -3 ? q1 : (k == -2 ? q2 : q3));
+    };
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        bool top = true;                     // lane 63 of pt passes the shifted part for c
+        bool ok = true;
 #pragma unroll
-        for (int j = c + 1; j < PF; ++j) top = top && (p63[c - j + 4] == s[j]);
-        P[c] = in[c] & ((sh[c] << 1) | (top ? 1ull : 0ull));
+        for (int j = 0; j < PF; ++j) ok = ok && (at(c, j) == s[j]);
+        P[c] = ballot(ok);
     }
     const int A = kTileTok * kt;
     if (A < c_lo || A + kTileTok > c_hi) {
@@ -291,29 +277,35 @@ __device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin,
         match_end[r] = e;
     }
     if (kMode == kStep) {
-        int d[LCD_DRAFT_STRIDE], qv[LCD_Q_STRIDE], tv[LCD_TARGET_STRIDE];
-#pragma unroll
-        for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) d[k] = __builtin_amdgcn_readlane(dk, k);
-#pragma unroll
-        for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = __builtin_amdgcn_readlane(sin, i);
-#pragma unroll
-        for (int i = 0; i < LCD_TARGET_STRIDE; ++i)
-            tv[i] = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + i);
+        // The rest of the step across the wave: lane i < 15 owns verify slot i.
+        constexpr int kSt = LCD_Q_STRIDE + LCD_TARGET_STRIDE;      // sin lane of the state
+        const int qk = sin;                                       // lanes 0..6: proposal
+        const int tk = __shfl(sin, LCD_Q_STRIDE + (lane < LCD_TARGET_STRIDE ? lane : 0));
         lcd_sched_state st;
-        st.long_mode = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE);
-        st.streak = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE + 1);
-        st.down = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE + 2);
-        const int32_t capr = __builtin_amdgcn_readlane(sin, LCD_Q_STRIDE + LCD_TARGET_STRIDE + 3);
+        st.long_mode = __builtin_amdgcn_readlane(sin, kSt);
+        st.streak = __builtin_amdgcn_readlane(sin, kSt + 1);
+        st.down = __builtin_amdgcn_readlane(sin, kSt + 2);
+        const int32_t capr = __builtin_amdgcn_readlane(sin, kSt + 3);
+        const bool agree = ballot(lane < io.f.agree_n && qk != dk) == 0;
+        bool head, tail;
+        const int blk = fuse_mode(m, agree, st.long_mode != 0, io.f, head, tail);
+        const int bk = fuse_slot(lane, dk, lane < LCD_Q_STRIDE ? qk : LCD_PAD, head, tail, blk, io.f);
+        if (lane < LCD_DRAFT_STRIDE) io.block[(int64_t)r * LCD_DRAFT_STRIDE + lane] = bk;
+        // greedy accept: the slots before the first mismatch within blk
+        const u64 miss = ballot(lane < blk && bk != tk);
+        int acc = miss ? (int)__builtin_ctzll(miss) : blk;
+        if (io.append) {
+            if ((int64_t)n + acc + 1 > (int64_t)capr) {
+                acc = -1;
+            } else {
+                if (lane <= acc) io.hist_w[ro + n + lane] = tk;
+                if (lane == 0) io.len_w[r] = n + acc + 1;
+            }
+        }
+        const int ln = schedule_row(st, m, acc, blk, io.s);
         if (lane == 0) {
-            int bv[LCD_DRAFT_STRIDE];
-            const int blk = fuse_row(d, m, qv, st.long_mode != 0, io.f, bv);
-#pragma unroll
-            for (int k = 0; k < LCD_DRAFT_STRIDE; ++k) io.block[(int64_t)r * LCD_DRAFT_STRIDE + k] = bv[k];
             io.block_len[r] = blk;
-            int acc = accept_row(bv, blk, tv);
-            if (io.append) acc = append_row(acc, tv, io.hist_w, ro, n, io.len_w + r, capr);
             io.accept[r] = acc;
-            const int ln = schedule_row(st, m, acc, blk, io.s);
             io.state[r] = st;
             if (io.long_next) io.long_next[r] = ln;
         }
@@ -451,32 +443,63 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
                 halo = make_int4(sent, sent, sent, sent);
                 if (c_lo > 0) buf[0] = mask_before(buf[0], c_lo - 4 * lane, sent);
             }
-            // Quick test: a candidate end e needs h[e-jq] == s_jq for every
-            // jq < PF, so a tile can hold one only if some position in it, or
-            // in the previous tile's last lane, holds s_jq.  Each wave uses the
-            // suffix token that is rarest in its first tile; the choice only
-            // changes how many tiles get the full test, never the result.
-            int jq = 0;
+            // Quick test.  A candidate end e needs h[e-j] == s_j for every
+            // j < PF; with PF >= 2 it needs in particular the adjacent pair
+            // s_j at p = e-j and s_{j+1} at p-1.  So a tile can hold a
+            // candidate only if it holds such a pair (the pair's second token
+            // may be the previous tile's last position), or if the previous
+            // tile holds one in its last lane (then e may lie in this tile).
+            // Each wave picks the pair that is rarest in its first tile; the
+            // choice only changes how many tiles get the full test, never the
+            // result.  Pairs, unlike single tokens, stay rare when every
+            // suffix token is a common one.  (PF = 1: the single token s_0.)
+            int cnt[4] = {0, 0, 0, 0};
             {
                 const int4 t = buf[0];
+#pragma unroll
+                for (int j = 0; j < PF; ++j)
+                    cnt[j] = __popcll(ballot(t.x == s4[j])) + __popcll(ballot(t.y == s4[j])) +
+                             __popcll(ballot(t.z == s4[j])) + __popcll(ballot(t.w == s4[j]));
+            }
+            int jp = 0;
+            if (PF >= 2) {
                 int fewest = 1 << 30;
 #pragma unroll
-                for (int j = 0; j < PF; ++j) {
-                    const int cnt = __popcll(ballot(t.x == s4[j])) + __popcll(ballot(t.y == s4[j])) +
-                                    __popcll(ballot(t.z == s4[j])) + __popcll(ballot(t.w == s4[j]));
-                    if (cnt < fewest) { fewest = cnt; jq = j; }
+                for (int j = 0; j + 1 < PF; ++j) {
+                    const int score = cnt[j] * cnt[j + 1] + cnt[j] + cnt[j + 1];
+                    if (score < fewest) { fewest = score; jp = j; }
                 }
             }
-            const int sq = uni(jq == 0 ? s4[0] : jq == 1 ? s4[1] : jq == 2 ? s4[2] : s4[3]);
+            const int sa = uni(jp == 0 ? s4[0] : jp == 1 ? s4[1] : s4[2]);                   // s_jp
+            const int sb = uni(PF >= 2 ? (jp == 0 ? s4[1] : jp == 1 ? s4[2] : s4[3]) : s4[0]);  // s_jp+1
+            u64 cb = 0;          // the previous tile's last position holds s_jp+1
+            // pair hits of tile t (bit i of the result: a pair with p in lane i)
             auto quick = [&](const int4 &t) -> u64 {
-                return ballot(t.x == sq) | ballot(t.y == sq) | ballot(t.z == sq) | ballot(t.w == sq);
+                if (PF < 2) return ballot(t.x == sa) | ballot(t.y == sa) | ballot(t.z == sa) | ballot(t.w == sa);
+                const u64 a0 = ballot(t.x == sa), a1 = ballot(t.y == sa);
+                const u64 a2 = ballot(t.z == sa), a3 = ballot(t.w == sa);
+                const u64 b0 = ballot(t.x == sb), b1 = ballot(t.y == sb);
+                const u64 b2 = ballot(t.z == sb), b3 = ballot(t.w == sb);
+                const u64 q = (a1 & b0) | (a2 & b1) | (a3 & b2) | (a0 & ((b3 << 1) | cb));
+                cb = b3 >> 63;
+                return q;
             };
             int4 prev = halo;                        // the tile before the next one processed
             u64 carry = quick(prev) >> 63;           // a hit in its last lane
+            // A wave whose pair turns out to be common stops running the quick
+            // test after kFullAfter flagged tiles and gives every tile the
+            // full test (which the quick test would have passed anyway).
+            int nflag = 0;
             // Test tile kt (tokens t) against its predecessor prev.
             auto test_tile = [&](const int4 &t, int kt) {
-                const u64 q = quick(t);
-                if ((q | carry) != 0) {
+                bool flagged = true;
+                if (nflag < kFullAfter) {
+                    const u64 q = quick(t);
+                    flagged = (q | carry) != 0;
+                    carry = q >> 63;
+                }
+                if (flagged) {
+                    ++nflag;
                     u64 P[4];
                     survivors<PF>(t, prev, s4, kt, c_lo, c_hi, lane, P);
                     if ((P[0] | P[1] | P[2] | P[3]) != 0) {
@@ -496,7 +519,6 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
                         }
                     }
                 }
-                carry = q >> 63;
                 prev = copy_tile(t);                 // frees the slot's registers for a refill
             };
             // Each wave keeps kUnroll tiles in flight.  While tiles remain
@@ -538,18 +560,18 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     }
     if (P > 1) {
         u64 *__restrict__ slots = req + 2;
-        const u64 unit = lane < kSlotWords - 1 ? (kTokValid | (u64)(uint32_t)tok) : (kKeyValid | key);
         const int my_ticket = uni((int)ticket);    // lane 0 took it (P > 1)
 #pragma clang diagnostic pop
         if (my_ticket != P - 1) {                  // not the last to start: publish, leave
+            const u64 unit = lane < kSlotWords - 1 ? (kTokValid | (u64)(uint32_t)tok) : (kKeyValid | key);
             if (lane < kSlotWords)
                 __hip_atomic_store(slots + c0 * kSlotWords + lane, unit, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
         // Last to start: every other workgroup taking part has started, and
-        // publishes without waiting for anything, so the gathering ends.
-        if (lane < kSlotWords) s_units[c0 * kSlotWords + lane] = unit;
+        // publishes without waiting for anything, so the gathering ends.  Its
+        // own key and tokens stay in registers (their load overlaps the polls).
         const int nu = P * kSlotWords;
         bool all = false;
         for (int tries = 0; tries < kPollMax && !all; ++tries) {
@@ -568,12 +590,14 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
             __hip_atomic_store(slots + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // best key over the slots (keys of different slots differ unless zero)
-        const u64 ks = lane < P ? (s_units[lane * kSlotWords + kSlotWords - 1] & ~kKeyValid) : 0;
-        key = wave_max(ks);
-        const u64 at = ballot(lane < P && ks == key);
-        const int w = at ? (int)__builtin_ctzll(at) : 0;
-        tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
-        if (!all) key = 0;                          // gathering gave up: report no match
+        const u64 ks = lane >= P ? 0
+                       : lane == c0 ? key
+                                    : (s_units[lane * kSlotWords + kSlotWords - 1] & ~kKeyValid);
+        const u64 kbest = wave_max(ks);
+        const u64 at = ballot(lane < P && ks == kbest);
+        const int w = at ? (int)__builtin_ctzll(at) : c0;
+        if (w != c0) tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
+        key = all ? kbest : 0;                      // gathering gave up: report no match
     }
     finish_request<kMode>(r, key, tok, sin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
 }

@@ -26,6 +26,25 @@ struct SchedArgs {
     int32_t tail_min, entry_steps, sticky, near_full_slack;
 };
 
+// Fusion decisions of one request: head slots take the lookup draft when the
+// match is long enough, or shorter but confirmed by the draft model's first
+// agree_n tokens; tail slots take it in a long block with a tail-length match.
+// Returns the number of draft slots verified.
+__device__ inline int fuse_mode(int m, bool agree, bool is_long, const FuseArgs &a, bool &head,
+                                bool &tail) {
+    head = (m >= a.head_full) || (m >= a.head_agree && agree);
+    tail = is_long && (m >= a.tail_min);
+    return is_long ? a.n_block : a.n_head;
+}
+
+// Verify-block slot i given the draft token d and the draft model's token q
+// for that slot (slots below n_head <= 7 carry the draft model's proposal).
+__device__ inline int fuse_slot(int i, int d, int q, bool head, bool tail, int blk, const FuseArgs &a) {
+    if (i < a.n_head) return (head && i < a.k_max) ? d : q;
+    if (i < blk) return (tail && i < a.k_max) ? d : LCD_PAD;
+    return LCD_PAD;
+}
+
 // Verify block of one request.  Returns the number of draft slots verified.
 __device__ inline int fuse_row(const int (&d)[LCD_DRAFT_STRIDE], int m, const int (&q)[LCD_Q_STRIDE],
                                bool is_long, const FuseArgs &a, int (&out)[LCD_DRAFT_STRIDE]) {
@@ -33,20 +52,11 @@ __device__ inline int fuse_row(const int (&d)[LCD_DRAFT_STRIDE], int m, const in
 #pragma unroll
     for (int i = 0; i < LCD_Q_STRIDE; ++i)
         if (i < a.agree_n && q[i] != d[i]) agree = false;
-    const bool head = (m >= a.head_full) || (m >= a.head_agree && agree);
-    const bool tail = is_long && (m >= a.tail_min);
-    const int blk = is_long ? a.n_block : a.n_head;
-    // slots below n_head (<= 7) carry the draft model's proposal
+    bool head, tail;
+    const int blk = fuse_mode(m, agree, is_long, a, head, tail);
 #pragma unroll
-    for (int i = 0; i < LCD_Q_STRIDE; ++i) {
-        int v = LCD_PAD;
-        if (i < a.n_head) v = (head && i < a.k_max) ? d[i] : q[i];
-        else if (i < blk) v = (tail && i < a.k_max) ? d[i] : LCD_PAD;
-        out[i] = v;
-    }
-#pragma unroll
-    for (int i = LCD_Q_STRIDE; i < LCD_DRAFT_STRIDE; ++i)
-        out[i] = (i < blk && tail && i < a.k_max) ? d[i] : LCD_PAD;
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i)
+        out[i] = fuse_slot(i, d[i], i < LCD_Q_STRIDE ? q[i] : LCD_PAD, head, tail, blk, a);
     return blk;
 }
 
