@@ -62,7 +62,7 @@ constexpr int kWaves = LCD_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileTok = 256;   // 64 lanes x 4 tokens
 #ifndef LCD_UNROLL
-#define LCD_UNROLL 8
+#define LCD_UNROLL 4
 #endif
 constexpr int kUnroll = LCD_UNROLL;   // tiles loaded ahead by each wave
 
@@ -602,14 +602,17 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     finish_request<kMode>(r, key, tok, sin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
 }
 
-// Workgroups per request.  By default about 512 per launch (two per CU), with
-// chunks of at least 2048 and at most 32768 tokens of the longest row.
+// Workgroups per request.  By default one workgroup per ~12k tokens of the
+// batch's size bound B x max_len, between 256 and 2048 per launch (1 to 8 per
+// CU), with chunks of at least 2048 and at most 32768 tokens of the longest row.
 int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
     int64_t cpr;
     if (scan_wgs > 0) {
         cpr = scan_wgs / B;
     } else {
-        cpr = (512 + B / 2) / B;
+        int64_t wgs = (int64_t)B * max_len / 12000;
+        wgs = wgs < 256 ? 256 : (wgs > 2048 ? 2048 : wgs);
+        cpr = (wgs + B / 2) / B;
         const int64_t most = ((int64_t)max_len + 2047) / 2048;
         const int64_t least = ((int64_t)max_len + 32767) / 32768;
         if (cpr > most) cpr = most;
