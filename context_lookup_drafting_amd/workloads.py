@@ -110,6 +110,15 @@ class Workload:
     q0: Optional[np.ndarray] = None       # fixed [B,7] proposal (single-step configs)
     target0: Optional[np.ndarray] = None  # fixed [B,16] argmax vector (single-step configs)
     note: str = ""
+    classes: Optional[List[str]] = None   # per-request task class ("copy" / "ordinary")
+
+    CLASS_NAMES = ("copy", "ordinary")
+
+    @property
+    def class_ids(self) -> np.ndarray:
+        """int32 [B]: index of each request's class in CLASS_NAMES."""
+        names = self.classes or ["copy"] * self.B
+        return np.array([self.CLASS_NAMES.index(c) for c in names], dtype=np.int32)
 
     @property
     def B(self) -> int:
@@ -194,7 +203,7 @@ def config1(seed: int = 1001) -> Workload:
     tgt = truth[:N_TARGET].copy()
     tgt[j] = (tgt[j] + 1) % V
     return Workload("c1_single_2k", seed, V, [h], [truth], 1, q0, tgt[None, :],
-                    note=f"copy source {s}, mismatch slot {j}")
+                    note=f"copy source {s}, mismatch slot {j}", classes=["copy"])
 
 
 def _copy_request(rng, cdf, V, doc_len, tail_len, truth_len, edit_p=0.0):
@@ -217,7 +226,7 @@ def config2(seed: int = 1002) -> Workload:
     rng = np.random.Generator(np.random.PCG64(seed))
     cdf = zipf_cdf(V)
     h, truth = _copy_request(rng, cdf, V, 24_000, 1_000, 4_112)
-    return Workload("c2_b1_25k_copy", seed, V, [h], [truth], 200)
+    return Workload("c2_b1_25k_copy", seed, V, [h], [truth], 200, classes=["copy"])
 
 
 def config3(seed: int = 1003, steps: int = 256) -> Workload:
@@ -237,7 +246,8 @@ def config3(seed: int = 1003, steps: int = 256) -> Workload:
             tr = zipf_tokens(rng, tl, cdf)
         hists.append(h)
         truths.append(tr)
-    return Workload("c3_b64_25k_mixed", seed, V, hists, truths, steps)
+    return Workload("c3_b64_25k_mixed", seed, V, hists, truths, steps,
+                    classes=["copy"] * 32 + ["ordinary"] * 32)
 
 
 def _plant_periodic_runs(rng, doc, cdf, frac=0.10, p_lo=2, p_hi=8, l_lo=20, l_hi=200):
@@ -279,7 +289,7 @@ def config4(seed: int = 1004, B: int = 64, n: int = 150_000) -> Workload:
         h = np.concatenate([doc, doc[o:o + 1000]]).astype(np.int32)
         hists.append(h)
         truths.append(doc[o + 1000:o + 1000 + N_TARGET].copy())
-    w = Workload("c4_b64_150k_periodic", seed, V, hists, truths, 1)
+    w = Workload("c4_b64_150k_periodic", seed, V, hists, truths, 1, classes=["copy"] * B)
     w.target0 = np.stack(truths).astype(np.int32)
     w.q0 = draft_model_proposal(w.target0, seed, 0, V)
     return w
@@ -293,10 +303,12 @@ def config5(seed: int = 1005, B: int = 256) -> Workload:
     V = 248_320
     rng = np.random.Generator(np.random.PCG64(seed))
     cdf = zipf_cdf(V)
-    hists, truths = [], []
+    hists, truths, classes = [], [], []
     for r in range(B):
         n = int(math.floor(math.exp(rng.uniform(math.log(1024), math.log(262_144)))))
-        if rng.random() < 0.5:
+        copy = bool(rng.random() < 0.5)
+        classes.append("copy" if copy else "ordinary")
+        if copy:
             tl = int(rng.integers(2000, 20_001))
             tl = min(tl, (n - N_TARGET) // 2)
             npre = n - tl
@@ -309,7 +321,7 @@ def config5(seed: int = 1005, B: int = 256) -> Workload:
             tr = zipf_tokens(rng, N_TARGET, cdf)
         hists.append(h)
         truths.append(tr)
-    w = Workload("c5_b256_ragged", seed, V, hists, truths, 1)
+    w = Workload("c5_b256_ragged", seed, V, hists, truths, 1, classes=classes)
     w.target0 = np.stack(truths).astype(np.int32)
     w.q0 = draft_model_proposal(w.target0, seed, 0, V)
     return w

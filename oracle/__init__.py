@@ -65,8 +65,11 @@ def lib():
         L.oracle_fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P]
         L.oracle_greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P]
         L.oracle_lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P]
+        L.oracle_telemetry_update.argtypes = [P, P, P, P, P, P, P, P, i32, pp]
+        L.oracle_telemetry_reduce.argtypes = [P, P, i32, i32, P]
         for f in (L.oracle_lookup_propose, L.oracle_fuse_verify_block,
-                  L.oracle_greedy_accept, L.oracle_lookup_schedule_step):
+                  L.oracle_greedy_accept, L.oracle_lookup_schedule_step,
+                  L.oracle_telemetry_update, L.oracle_telemetry_reduce):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -153,3 +156,33 @@ def lookup_schedule_step(state, match_len, accept, block_len, params=None):
         lib().oracle_lookup_schedule_step(_ptr(state), _ptr(match_len), _ptr(accept),
                                           _ptr(block_len), B, ctypes.byref(params), _ptr(ln))
     return ln
+
+
+TELE_WORDS = 32
+TELE_FIELDS = ("steps", "hits", "head_lookup", "tail_lookup", "long_steps", "entries", "exits",
+               "emitted", "failed_append")
+
+
+def telemetry_update(tele, match_len, draft, q, long_mode, block_len, accept, long_next,
+                     params=None):
+    """Adds one step to the per-request counters ``tele`` (uint32 [B,32], in place)."""
+    params = params or default_params()
+    assert tele.dtype == np.uint32 and tele.flags.c_contiguous
+    match_len = _c(match_len, np.int32)
+    B = len(match_len)
+    if B:
+        lib().oracle_telemetry_update(
+            _ptr(tele), _ptr(match_len), _ptr(_c(draft, np.int32).reshape(-1, DRAFT_STRIDE)),
+            _ptr(_c(q, np.int32).reshape(-1, Q_STRIDE)), _ptr(_c(long_mode, np.int32)),
+            _ptr(_c(block_len, np.int32)), _ptr(_c(accept, np.int32)),
+            _ptr(_c(long_next, np.int32)), B, ctypes.byref(params))
+    return tele
+
+
+def telemetry_reduce(tele, class_id, K):
+    """Per-class totals: uint64 [K,32]."""
+    tele = _c(tele, np.uint32).reshape(-1, TELE_WORDS)
+    class_id = _c(class_id, np.int32)
+    out = np.zeros((K, TELE_WORDS), np.uint64)
+    lib().oracle_telemetry_reduce(_ptr(tele), _ptr(class_id), len(class_id), K, _ptr(out))
+    return out

@@ -215,3 +215,77 @@ int oracle_lookup_schedule_step(int32_t *state /* B x 3 */, const int32_t *match
     }
     return 0;
 }
+
+
+/*
+ * Acceptance telemetry (the forum thread on the article: wire up hit rate and
+ * mean accepted length before drawing conclusions, and print the accepted-
+ * length distribution; the Polish post, "Jak testować bez mylenia prędkości z
+ * jakością", item 5: measure acceptance per task class).
+ *
+ * Per request r, tele[r*32 + k] are unsigned 32-bit counters that one decode
+ * step updates once:
+ *   0 steps            1 hits (m > 0)
+ *   2 steps whose head slots took the lookup draft (the fusion head decision)
+ *   3 steps whose tail slots took the lookup draft (the fusion tail decision)
+ *   4 steps verified as a long block (the mode the step used)
+ *   5 entries into the long block (this step short, the next one long)
+ *   6 exits from it (this step long, the next one short)
+ *   7 tokens emitted (a+1 summed over steps with a >= 0)
+ *   8 failed appends (a = -1)
+ *   9 + i, i = 0..15: steps that accepted exactly i draft slots
+ *   25..31 unused (zero)
+ * The head and tail decisions are recomputed from the step's match length,
+ * draft, draft-model proposal and mode with the fusion rule above.
+ */
+int oracle_telemetry_update(uint32_t *tele, const int32_t *match_len, const int32_t *draft,
+                            const int32_t *q, const int32_t *long_mode,
+                            const int32_t *block_len, const int32_t *accept,
+                            const int32_t *long_next, int32_t B, const oracle_params *p)
+{
+    for (int32_t r = 0; r < B; ++r) {
+        uint32_t *t = tele + (int64_t)r * 32;
+        const int32_t *d = draft + (int64_t)r * ORACLE_DRAFT_STRIDE;
+        const int32_t *qr = q + (int64_t)r * ORACLE_Q_STRIDE;
+        int32_t m = match_len[r];
+        int is_long = long_mode[r] != 0;
+        int agree = 1;
+        for (int32_t i = 0; i < p->agree_n; ++i)
+            if (qr[i] != d[i]) agree = 0;
+        int head = (m >= p->head_full) || (m >= p->head_agree && agree);
+        int tail = is_long && (m >= p->tail_min);
+        int32_t a = accept[r];
+        (void)block_len;
+        t[0] += 1;
+        if (m > 0) t[1] += 1;
+        if (head) t[2] += 1;
+        if (tail) t[3] += 1;
+        if (is_long) t[4] += 1;
+        if (!is_long && long_next[r]) t[5] += 1;
+        if (is_long && !long_next[r]) t[6] += 1;
+        if (a >= 0) {
+            t[7] += (uint32_t)(a + 1);
+            if (a < 16) t[9 + a] += 1;
+        } else {
+            t[8] += 1;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Per-class totals of the telemetry counters: out[k*32 + c] = the sum over
+ * requests r with class_id[r] == k of tele[r*32 + c], for 0 <= k < K (64-bit
+ * sums; requests whose class is outside [0, K) are left out).
+ */
+int oracle_telemetry_reduce(const uint32_t *tele, const int32_t *class_id, int32_t B,
+                            int32_t K, uint64_t *out)
+{
+    for (int64_t i = 0; i < (int64_t)K * 32; ++i) out[i] = 0;
+    for (int32_t r = 0; r < B; ++r) {
+        int32_t k = class_id[r];
+        if (k < 0 || k >= K) continue;
+        for (int c = 0; c < 32; ++c) out[(int64_t)k * 32 + c] += tele[(int64_t)r * 32 + c];
+    }
+    return 0;
+}
