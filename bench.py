@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--scan-wgs", type=int, default=0, help="lookup launch tuning (0 = auto)")
     ap.add_argument("--separate", action="store_true",
                     help="time the four separate entry points instead of the fused step")
+    ap.add_argument("--telemetry", action="store_true",
+                    help="fused step with per-request acceptance telemetry on")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="profiling aid: only N eager lookup launches over the rotating sets")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -69,18 +71,28 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}), flush=True)
 
 
-def per_request_bytes(separate):
+def per_request_bytes(separate, telemetry=False):
     """Algorithmic bytes per request besides the history, for the timed kernel:
     the lookup alone reads row_off and len (12) and writes match_len, match_end
     and the draft (68); the whole step also reads the proposal, target tokens
     and scheduler state (104) and writes the block, block_len, accept, state
-    and long_next (84)."""
-    return 80 if separate else 80 + 104 + 84
+    and long_next (84); telemetry reads the request's 32-word row (128) and
+    writes its 25 counters back (100)."""
+    if separate:
+        return 80
+    return 80 + 104 + 84 + (228 if telemetry else 0)
+
+
+KERNEL_SOURCES = ("context_lookup_drafting_amd/csrc/lcd_lookup.hip",
+                  "context_lookup_drafting_amd/csrc/lcd_rules.h", "include/lcd.h")
 
 
 def kernel_source_hash():
-    src = os.path.join(ROOT, "context_lookup_drafting_amd", "csrc", "lcd_lookup.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """sha256[:16] over the sources the fused step kernel is compiled from."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload_name, launches_per_step=1):
@@ -228,6 +240,10 @@ def main():
     ln_next = torch.empty(B, dtype=torch.int32, device=dev)
     state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
     longs = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    tele = lcd.alloc_telemetry(B, dev) if args.telemetry else None
+    if args.telemetry and args.separate:
+        print("bench.py: --telemetry applies to the fused step only", file=sys.stderr)
+        sys.exit(2)
 
     if args.kernel_only:
         for i in range(args.kernel_only):
@@ -235,11 +251,13 @@ def main():
                 lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
             else:
                 lcd.lookup_decode_step(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d,
-                                       state, dws, m, e, d, blk, bl, acc, ln_next, False, p)
+                                       state, dws, m, e, d, blk, bl, acc, ln_next, False, p,
+                                       telemetry=tele)
         torch.cuda.synchronize()
         print(json.dumps({"kernel_only_launches": args.kernel_only, "workload": w.name,
                           "tokens_per_launch": tokens,
-                          "alg_bytes_per_launch": 4 * tokens + per_request_bytes(args.separate) * B,
+                          "alg_bytes_per_launch": (4 * tokens
+                                                   + per_request_bytes(args.separate, args.telemetry) * B),
                           "rotating_sets": R, "separate": args.separate}), flush=True)
         return
 
@@ -251,7 +269,7 @@ def main():
             lcd.lookup_schedule_step(state, m, acc, bl, longs[(i + 1) % 2], p)
         else:
             lcd.lookup_decode_step(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d, state,
-                                   dws, m, e, d, blk, bl, acc, ln_next, False, p)
+                                   dws, m, e, d, blk, bl, acc, ln_next, False, p, telemetry=tele)
 
     # eager reference of one step, then the graphs
     for i in range(2):
@@ -307,7 +325,7 @@ def main():
         else:
             lcd.lookup_decode_step_timed(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d,
                                          state, dws, m, e, d, blk, bl, acc, evs[i][0], evs[i][1],
-                                         ln_next, False, p)
+                                         ln_next, False, p, telemetry=tele)
     torch.cuda.synchronize()
     durs = np.array([hev.elapsed_ms(a, b) for a, b in evs]) * 1e-3
     for a, b in evs:
@@ -315,9 +333,9 @@ def main():
         hev.destroy(b)
     k_avg = float(durs.mean())
 
-    alg_bytes = 4 * tokens + per_request_bytes(args.separate) * B
+    alg_bytes = 4 * tokens + per_request_bytes(args.separate, args.telemetry) * B
     achieved = alg_bytes / k_avg / 1e9
-    traffic = None if args.separate else load_traffic(w.name)
+    traffic = None if (args.separate or args.telemetry) else load_traffic(w.name)
     value = K * tokens / elapsed
     out = {
         "metric": METRIC,
@@ -343,6 +361,7 @@ def main():
             "launch": (f"HIP graph of {R} steps, "
                        + ("4 entry points (4 kernels) per step" if args.separate
                           else "lookup_decode_step (1 kernel) per step")),
+            "telemetry": args.telemetry,
         },
         "lookups_per_s": round(K * B / elapsed, 1),
         "step_hbm_gbps": round(value * 4 / 1e9, 2),

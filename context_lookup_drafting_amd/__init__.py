@@ -76,14 +76,17 @@ def load():
         L.fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P]
         L.lcd_decode_step_workspace_bytes.argtypes = [i32, i32, pp]
         L.lcd_decode_step_workspace_bytes.restype = ctypes.c_size_t
-        dec = [P, P, P, P, i32, i32, P, P, P, pp, P, ctypes.c_size_t, P, P, P, P, P, P, P, i32, P]
+        dec = [P, P, P, P, i32, i32, P, P, P, pp, P, ctypes.c_size_t, P, P, P, P, P, P, P, P, i32, P]
         L.lookup_decode_step.argtypes = dec
         L.lookup_decode_step_timed.argtypes = dec + [P, P]
         L.greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P, P]
         L.lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P, P]
+        L.lookup_telemetry_update.argtypes = [P, P, P, P, P, P, P, P, i32, pp, P]
+        L.lookup_telemetry_reduce.argtypes = [P, P, i32, i32, P, P]
         for f in (L.lookup_propose, L.lookup_propose_timed, L.fuse_verify_block,
                   L.greedy_accept, L.lookup_schedule_step, L.lookup_decode_step,
-                  L.lookup_decode_step_timed):
+                  L.lookup_decode_step_timed, L.lookup_telemetry_update,
+                  L.lookup_telemetry_reduce):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -250,7 +253,8 @@ def alloc_decode_workspace(B: int, max_len: int, device, params: Params | None =
 
 
 def _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
-                 match_len, match_end, draft, block, block_len, accept, long_next, append, p):
+                 match_len, match_end, draft, block, block_len, accept, long_next, append, p,
+                 telemetry=None):
     import torch
     B = lens.numel()
     dev = lens.device
@@ -274,6 +278,8 @@ def _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, 
         _dev(block_len, "block_len", torch.int32, B, dev),
         _dev(accept, "accept", torch.int32, B, dev),
         _dev(long_next, "long_next", torch.int32, B, dev) if long_next is not None else nul,
+        (_dev(telemetry, "telemetry", torch.int32, B * TELE_WORDS, dev)
+         if telemetry is not None else nul),
         ctypes.c_int32(1 if append else 0),
         _stream(dev),
     )
@@ -281,22 +287,67 @@ def _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, 
 
 def lookup_decode_step(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
                        match_len, match_end, draft, block, block_len, accept, long_next=None,
-                       append=True, params: Params | None = None):
+                       append=True, params: Params | None = None, telemetry=None):
     """One whole decode step (lookup, fusion under state's current mode, greedy
-    accept with optional append, scheduler update) in one kernel."""
+    accept with optional append, scheduler update, optional telemetry) in one
+    kernel.  ``telemetry``: int32 [B,32] counter rows (from alloc_telemetry)."""
     p = params or default_params()
     _check("lookup_decode_step", load().lookup_decode_step(*_decode_args(
         hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,
-        match_end, draft, block, block_len, accept, long_next, append, p)))
+        match_end, draft, block, block_len, accept, long_next, append, p, telemetry)))
 
 
 def lookup_decode_step_timed(hist, row_off, lens, cap, max_len, model_draft, target, state,
                              workspace, match_len, match_end, draft, block, block_len, accept,
                              ev_start, ev_stop, long_next=None, append=True,
-                             params: Params | None = None):
+                             params: Params | None = None, telemetry=None):
     """lookup_decode_step with GPU-stamped events around its scan kernel."""
     p = params or default_params()
     _check("lookup_decode_step_timed", load().lookup_decode_step_timed(*_decode_args(
         hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,
-        match_end, draft, block, block_len, accept, long_next, append, p),
+        match_end, draft, block, block_len, accept, long_next, append, p, telemetry),
         ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
+
+
+TELE_WORDS = 32
+TELE_FIELDS = ("steps", "hits", "head_lookup", "tail_lookup", "long_steps", "entries", "exits",
+               "emitted", "failed_append")
+TELE_HIST = 9
+
+
+def alloc_telemetry(B: int, device):
+    """Zeroed telemetry rows: int32 [B,32] (the library treats them as uint32)."""
+    import torch
+    return torch.zeros((B, TELE_WORDS), dtype=torch.int32, device=device)
+
+
+def telemetry_update(telemetry, match_len, draft, model_draft, long_mode, block_len, accept,
+                     long_next, params: Params | None = None):
+    """Adds one step (the separate calls' outputs) to the telemetry rows."""
+    import torch
+    p = params or default_params()
+    B = match_len.numel()
+    dev = match_len.device
+    _check("lookup_telemetry_update", load().lookup_telemetry_update(
+        _dev(telemetry, "telemetry", torch.int32, B * TELE_WORDS, dev),
+        _dev(match_len, "match_len", torch.int32, B, dev),
+        _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev),
+        _dev(model_draft, "model_draft", torch.int32, B * Q_STRIDE, dev),
+        _dev(long_mode, "long_mode", torch.int32, B, dev),
+        _dev(block_len, "block_len", torch.int32, B, dev),
+        _dev(accept, "accept", torch.int32, B, dev),
+        _dev(long_next, "long_next", torch.int32, B, dev),
+        ctypes.c_int32(B), ctypes.byref(p), _stream(dev)))
+
+
+def telemetry_reduce(telemetry, class_id, K: int):
+    """Per-class totals of the telemetry rows: int64 [K,32] (uint64 values)."""
+    import torch
+    B = class_id.numel()
+    dev = class_id.device
+    out = torch.empty((K, TELE_WORDS), dtype=torch.int64, device=dev)
+    _check("lookup_telemetry_reduce", load().lookup_telemetry_reduce(
+        _dev(telemetry, "telemetry", torch.int32, B * TELE_WORDS, dev),
+        _dev(class_id, "class_id", torch.int32, B, dev), ctypes.c_int32(B), ctypes.c_int32(K),
+        _dev(out, "out", torch.int64, K * TELE_WORDS, dev), _stream(dev)))
+    return out

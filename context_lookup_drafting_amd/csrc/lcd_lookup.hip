@@ -222,6 +222,7 @@ struct StepIO {
     const int32_t *target;
     lcd_sched_state *state;
     int32_t *block, *block_len, *accept, *long_next;
+    uint32_t *tele;                  // telemetry rows (nullable)
     FuseArgs f;
     SchedArgs s;
     int32_t append;
@@ -259,7 +260,7 @@ __device__ __forceinline__ u64 wave_max(u64 v) {
 // tokens following the match.  Writes the match and draft and, in kStep mode,
 // the rest of the step (sin: the per-lane step inputs).
 template <int kMode>
-__device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin, int lane,
+__device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin, uint32_t tin, int lane,
                                                int64_t ro, int n, int k_max,
                                                int32_t *__restrict__ match_len,
                                                int32_t *__restrict__ match_end,
@@ -302,6 +303,7 @@ __device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin,
                 if (lane == 0) io.len_w[r] = n + acc + 1;
             }
         }
+        const bool was_long = st.long_mode != 0;
         const int ln = schedule_row(st, m, acc, blk, io.s);
         if (lane == 0) {
             io.block_len[r] = blk;
@@ -309,6 +311,10 @@ __device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin,
             io.state[r] = st;
             if (io.long_next) io.long_next[r] = ln;
         }
+        // telemetry: lane k owns counter k of the request's row
+        if (io.tele != nullptr && lane < LCD_TELE_HIST + 16)
+            io.tele[(int64_t)r * LCD_TELE_WORDS + lane] =
+                tin + telemetry_inc(lane, m, head, tail, was_long, ln != 0, acc);
     }
 }
 
@@ -330,13 +336,16 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     const int r = (int)(blockIdx.x / (unsigned)cpr);
     const int c0 = (int)blockIdx.x - r * cpr;
     const int sin = (kMode == kStep && wave == 0) ? load_step_input(r, lane, io) : 0;
+    uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
+    if (kMode == kStep && wave == 0 && io.tele != nullptr)
+        tin = io.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
     const int64_t ro = row_off[r];
     const int32_t lr = len[r];
     const int n = lr > 0 ? lr : 0;
     const int nc = n - 1;             // candidate ends 0..n-2
     if (nc <= 0) {                    // no earlier position: chunk 0 finishes the request
         if (c0 == 0 && wave == 0)
-            finish_request<kMode>(r, 0, 0, sin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
+            finish_request<kMode>(r, 0, 0, sin, tin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
         return;
     }
     if ((int64_t)c0 * T >= nc) return;                  // past the row's last chunk
@@ -599,7 +608,7 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
         if (w != c0) tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
         key = all ? kbest : 0;                      // gathering gave up: report no match
     }
-    finish_request<kMode>(r, key, tok, sin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
+    finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
 }
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
@@ -692,8 +701,8 @@ int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32
                 int32_t max_len, const int32_t *model_draft, const int32_t *target,
                 lcd_sched_state *state, const lcd_params *p, void *workspace, size_t ws_bytes,
                 int32_t *match_len, int32_t *match_end, int32_t *draft, int32_t *block,
-                int32_t *block_len, int32_t *accept, int32_t *long_next, int32_t append,
-                void *stream, hipEvent_t ev0, hipEvent_t ev1) {
+                int32_t *block_len, int32_t *accept, int32_t *long_next, uint32_t *tele,
+                int32_t append, void *stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (B < 0 || p == nullptr || max_len < 0) return LCD_EINVAL;
     if (lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
@@ -706,7 +715,7 @@ int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32
 
     const int pf = p->l_min < 4 ? p->l_min : 4;
     StepIO io{hist, len, cap, model_draft, target, state, block, block_len, accept, long_next,
-              fuse_args(p), sched_args(p), append ? 1 : 0};
+              tele, fuse_args(p), sched_args(p), append ? 1 : 0};
     const hipError_t err = launch_scan<kStep>(pf, hist, row_off, len, B, scan_args(B, max_len, p),
                                               reinterpret_cast<u64 *>(workspace), match_len,
                                               match_end, draft, io,
@@ -747,11 +756,12 @@ extern "C" int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t
                                   lcd_sched_state *state, const lcd_params *p, void *workspace,
                                   size_t workspace_bytes, int32_t *match_len, int32_t *match_end,
                                   int32_t *draft, int32_t *block, int32_t *block_len,
-                                  int32_t *accept, int32_t *long_next, int32_t append,
-                                  void *stream) {
+                                  int32_t *accept, int32_t *long_next, uint32_t *telemetry,
+                                  int32_t append, void *stream) {
     return lcd::decode_step(hist, row_off, len, cap, B, max_len, model_draft, target, state, p,
                             workspace, workspace_bytes, match_len, match_end, draft, block,
-                            block_len, accept, long_next, append, stream, nullptr, nullptr);
+                            block_len, accept, long_next, telemetry, append, stream, nullptr,
+                            nullptr);
 }
 
 extern "C" int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len,
@@ -761,11 +771,11 @@ extern "C" int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, i
                                         void *workspace, size_t workspace_bytes,
                                         int32_t *match_len, int32_t *match_end, int32_t *draft,
                                         int32_t *block, int32_t *block_len, int32_t *accept,
-                                        int32_t *long_next, int32_t append, void *stream,
-                                        void *ev_start, void *ev_stop) {
+                                        int32_t *long_next, uint32_t *telemetry, int32_t append,
+                                        void *stream, void *ev_start, void *ev_stop) {
     return lcd::decode_step(hist, row_off, len, cap, B, max_len, model_draft, target, state, p,
                             workspace, workspace_bytes, match_len, match_end, draft, block,
-                            block_len, accept, long_next, append, stream,
+                            block_len, accept, long_next, telemetry, append, stream,
                             reinterpret_cast<hipEvent_t>(ev_start),
                             reinterpret_cast<hipEvent_t>(ev_stop));
 }

@@ -112,6 +112,25 @@ __device__ inline int schedule_row(lcd_sched_state &st, int m, int a, int blk, c
     return st.long_mode;
 }
 
+// Telemetry increment of counter k for one step (the layout of LCD_TELE_*):
+// match length m, the fusion decisions, the mode used and the next one, and
+// the accepted count a (-1: failed append).
+__device__ inline uint32_t telemetry_inc(int k, int m, bool head, bool tail, bool is_long,
+                                         bool long_next, int a) {
+    switch (k) {
+    case LCD_TELE_STEPS: return 1u;
+    case LCD_TELE_HITS: return m > 0 ? 1u : 0u;
+    case LCD_TELE_HEAD: return head ? 1u : 0u;
+    case LCD_TELE_TAIL: return tail ? 1u : 0u;
+    case LCD_TELE_LONG: return is_long ? 1u : 0u;
+    case LCD_TELE_ENTRIES: return (!is_long && long_next) ? 1u : 0u;
+    case LCD_TELE_EXITS: return (is_long && !long_next) ? 1u : 0u;
+    case LCD_TELE_EMITTED: return a >= 0 ? (uint32_t)(a + 1) : 0u;
+    case LCD_TELE_FAILED: return a < 0 ? 1u : 0u;
+    default: return (k >= LCD_TELE_HIST && k < LCD_TELE_HIST + 16 && a == k - LCD_TELE_HIST) ? 1u : 0u;
+    }
+}
+
 inline FuseArgs fuse_args(const lcd_params *p) {
     return FuseArgs{p->k_max, p->n_head, p->n_block, p->head_full, p->head_agree, p->agree_n,
                     p->tail_min};

@@ -71,6 +71,47 @@ schedule_kernel(lcd_sched_state *__restrict__ state, const int32_t *__restrict__
     long_next[r] = ln;
 }
 
+// Telemetry of one step from the separate calls' outputs, one lane per request.
+__global__ void __launch_bounds__(kStepThreads)
+telemetry_kernel(uint32_t *__restrict__ tele, const int32_t *__restrict__ match_len,
+                 const int32_t *__restrict__ draft, const int32_t *__restrict__ q,
+                 const int32_t *__restrict__ long_mode, const int32_t *__restrict__ accept,
+                 const int32_t *__restrict__ long_next, int32_t B, FuseArgs a) {
+    const int r = blockIdx.x * kStepThreads + threadIdx.x;
+    if (r >= B) return;
+    int dv[LCD_DRAFT_STRIDE], qv[LCD_Q_STRIDE];
+#pragma unroll
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) dv[i] = draft[(int64_t)r * LCD_DRAFT_STRIDE + i];
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = q[(int64_t)r * LCD_Q_STRIDE + i];
+    const int m = match_len[r];
+    const bool is_long = long_mode[r] != 0;
+    bool agree = true;
+#pragma unroll
+    for (int i = 0; i < LCD_Q_STRIDE; ++i)
+        if (i < a.agree_n && qv[i] != dv[i]) agree = false;
+    bool head, tail;
+    fuse_mode(m, agree, is_long, a, head, tail);
+    const bool ln = long_next[r] != 0;
+    const int acc = accept[r];
+    uint32_t *t = tele + (int64_t)r * LCD_TELE_WORDS;
+#pragma unroll
+    for (int k = 0; k < LCD_TELE_HIST + 16; ++k) t[k] += telemetry_inc(k, m, head, tail, is_long, ln, acc);
+}
+
+// Per-class totals: one lane per (class, counter), summing over requests.
+__global__ void __launch_bounds__(kStepThreads)
+telemetry_reduce_kernel(const uint32_t *__restrict__ tele, const int32_t *__restrict__ class_id,
+                        int32_t B, int32_t K, unsigned long long *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * kStepThreads + threadIdx.x;
+    if (i >= (int64_t)K * LCD_TELE_WORDS) return;
+    const int k = (int)(i / LCD_TELE_WORDS), c = (int)(i % LCD_TELE_WORDS);
+    unsigned long long sum = 0;
+    for (int32_t r = 0; r < B; ++r)
+        if (class_id[r] == k) sum += tele[(int64_t)r * LCD_TELE_WORDS + c];
+    out[i] = sum;
+}
+
 inline int blocks_for(int32_t B) { return (B + kStepThreads - 1) / kStepThreads; }
 
 }  // namespace
@@ -148,5 +189,36 @@ extern "C" int lookup_schedule_step(lcd_sched_state *state, const int32_t *match
     hipLaunchKernelGGL(schedule_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), state, match_len, accept, block_len,
                        B, a, long_next);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+
+extern "C" int lookup_telemetry_update(uint32_t *telemetry, const int32_t *match_len,
+                                       const int32_t *draft, const int32_t *model_draft,
+                                       const int32_t *long_mode, const int32_t *block_len,
+                                       const int32_t *accept, const int32_t *long_next, int32_t B,
+                                       const lcd_params *p, void *stream) {
+    using namespace lcd;
+    (void)block_len;
+    if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!telemetry || !match_len || !draft || !model_draft || !long_mode || !accept || !long_next)
+        return LCD_EINVAL;
+    hipLaunchKernelGGL(telemetry_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), telemetry, match_len, draft,
+                       model_draft, long_mode, accept, long_next, B, fuse_args(p));
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+
+extern "C" int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, int32_t B,
+                                       int32_t K, uint64_t *out, void *stream) {
+    using namespace lcd;
+    if (B < 0 || K < 0) return LCD_EINVAL;
+    if (K == 0) return LCD_OK;
+    if (!out || (B > 0 && (!telemetry || !class_id))) return LCD_EINVAL;
+    const int64_t n = (int64_t)K * LCD_TELE_WORDS;
+    if (n > (int64_t)1 << 30) return LCD_EINVAL;
+    hipLaunchKernelGGL(telemetry_reduce_kernel, dim3((unsigned)((n + kStepThreads - 1) / kStepThreads)),
+                       dim3(kStepThreads), 0, reinterpret_cast<hipStream_t>(stream), telemetry,
+                       class_id, B, K, reinterpret_cast<unsigned long long *>(out));
     return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
 }

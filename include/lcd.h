@@ -208,6 +208,7 @@ int lookup_schedule_step(lcd_sched_state *state, const int32_t *match_len,
  *             size, checked.  Concurrent calls must not share it.
  * outputs     match_len, match_end int32[B]; draft, block int32[B*15];
  *             block_len, accept int32[B]; long_next int32[B] (nullable)
+ * telemetry   uint32[B * LCD_TELE_WORDS] (nullable), see lookup_telemetry_update
  */
 size_t lcd_decode_step_workspace_bytes(int32_t B, int32_t max_len, const lcd_params *p);
 
@@ -216,7 +217,8 @@ int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, cons
                        const int32_t *target, lcd_sched_state *state, const lcd_params *p,
                        void *workspace, size_t workspace_bytes, int32_t *match_len,
                        int32_t *match_end, int32_t *draft, int32_t *block, int32_t *block_len,
-                       int32_t *accept, int32_t *long_next, int32_t append, void *stream);
+                       int32_t *accept, int32_t *long_next, uint32_t *telemetry,
+                       int32_t append, void *stream);
 
 /* lookup_decode_step with GPU-stamped events around its scan kernel (see
  * lookup_propose_timed); for profiling only. */
@@ -226,8 +228,58 @@ int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len
                              lcd_sched_state *state, const lcd_params *p, void *workspace,
                              size_t workspace_bytes, int32_t *match_len, int32_t *match_end,
                              int32_t *draft, int32_t *block, int32_t *block_len,
-                             int32_t *accept, int32_t *long_next, int32_t append, void *stream,
-                             void *ev_start, void *ev_stop);
+                             int32_t *accept, int32_t *long_next, uint32_t *telemetry,
+                             int32_t append, void *stream, void *ev_start, void *ev_stop);
+
+/*
+ * Acceptance telemetry -- the diagnostics the article's forum thread asks to
+ * wire up first (hit rate and mean accepted length, with the distribution of
+ * accepted lengths), per task class as in the Polish post's test procedure
+ * ("Jak testować bez mylenia prędkości z jakością", item 5).
+ *
+ * telemetry is uint32[B * LCD_TELE_WORDS], device, caller-owned, zeroed by the
+ * caller when a session starts.  One decode step adds to request r's row:
+ *   LCD_TELE_STEPS        1
+ *   LCD_TELE_HITS         1 if m > 0
+ *   LCD_TELE_HEAD         1 if the head slots took the lookup draft
+ *   LCD_TELE_TAIL         1 if the tail slots took the lookup draft
+ *   LCD_TELE_LONG         1 if the step verified a long block
+ *   LCD_TELE_ENTRIES      1 if this step was short and the next is long
+ *   LCD_TELE_EXITS        1 if this step was long and the next is short
+ *   LCD_TELE_EMITTED      a+1 when a >= 0 (tokens the step emits)
+ *   LCD_TELE_FAILED       1 if the append failed (a = -1)
+ *   LCD_TELE_HIST + i     1 if the step accepted exactly i draft slots, i < 16
+ * Counters wrap modulo 2^32.  lookup_decode_step updates it when its
+ * `telemetry` argument is non-NULL (nothing is read or written otherwise);
+ * lookup_telemetry_update does the same from the outputs of the separate calls
+ * (match_len, draft, model_draft, the mode used, block_len, accept, long_next).
+ */
+#define LCD_TELE_WORDS 32
+#define LCD_TELE_STEPS 0
+#define LCD_TELE_HITS 1
+#define LCD_TELE_HEAD 2
+#define LCD_TELE_TAIL 3
+#define LCD_TELE_LONG 4
+#define LCD_TELE_ENTRIES 5
+#define LCD_TELE_EXITS 6
+#define LCD_TELE_EMITTED 7
+#define LCD_TELE_FAILED 8
+#define LCD_TELE_HIST 9
+
+int lookup_telemetry_update(uint32_t *telemetry, const int32_t *match_len, const int32_t *draft,
+                            const int32_t *model_draft, const int32_t *long_mode,
+                            const int32_t *block_len, const int32_t *accept,
+                            const int32_t *long_next, int32_t B, const lcd_params *p,
+                            void *stream);
+
+/*
+ * Per-class totals: out[k * LCD_TELE_WORDS + c] = sum over requests r with
+ * class_id[r] == k of telemetry[r * LCD_TELE_WORDS + c], as uint64, for
+ * 0 <= k < K; requests with a class outside [0, K) are left out.  out is
+ * uint64[K * LCD_TELE_WORDS], device, overwritten.  One launch.
+ */
+int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, int32_t B,
+                            int32_t K, uint64_t *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -30,6 +30,7 @@ def simulate_oracle(w: Workload, steps: int, params=None, record: bool = True):
     B = w.B
     state = np.zeros((B, 3), np.int32)
     long_mode = np.zeros(B, np.int32)
+    tele = np.zeros((B, 32), np.uint32)
     pos = np.zeros(B, np.int64)
     recs = []
     emitted = [[] for _ in range(B)]
@@ -40,6 +41,7 @@ def simulate_oracle(w: Workload, steps: int, params=None, record: bool = True):
         acc = oracle.greedy_accept(blk, bl, tgt, flat, row_off, lens, cap)
         long_used = long_mode.copy()
         long_mode = oracle.lookup_schedule_step(state, m, acc, bl, params)
+        oracle.telemetry_update(tele, m, d, q, long_used, bl, acc, long_mode, params)
         for r in range(B):
             if acc[r] >= 0:
                 emitted[r].extend(tgt[r, :acc[r] + 1].tolist())
@@ -47,7 +49,7 @@ def simulate_oracle(w: Workload, steps: int, params=None, record: bool = True):
         if record:
             recs.append(dict(m=m, e=e, d=d, q=q, tgt=tgt, long=long_used, block=blk,
                              blk=bl, acc=acc, state=state.copy(), long_next=long_mode.copy()))
-    return dict(recs=recs, emitted=emitted, lens=lens, flat=flat, row_off=row_off)
+    return dict(recs=recs, emitted=emitted, lens=lens, flat=flat, row_off=row_off, tele=tele)
 
 
 def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, device="cuda:0"):
@@ -71,6 +73,7 @@ def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, devi
     bl = torch.empty(B, dtype=torch.int32, device=dev)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     long_next = torch.empty(B, dtype=torch.int32, device=dev)
+    tele = lcd.alloc_telemetry(B, dev)
     pos = np.zeros(B, np.int64)
     recs = []
     emitted = [[] for _ in range(B)]
@@ -84,6 +87,7 @@ def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, devi
         lcd.greedy_accept(block, bl, tgt_d, acc, hist=h_d, row_off=ro_d, lens=len_d, cap=cap_d)
         long_used = long_mode.clone()
         lcd.lookup_schedule_step(state, m, acc, bl, long_next, params)
+        lcd.telemetry_update(tele, m, d, q_d, long_used, bl, acc, long_next, params)
         long_mode.copy_(long_next)
         acc_h = acc.cpu().numpy()
         for r in range(B):
@@ -97,48 +101,13 @@ def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, devi
                              long_next=long_next.cpu().numpy()))
     torch.cuda.synchronize()
     return dict(recs=recs, emitted=emitted, lens=len_d.cpu().numpy(), flat=h_d.cpu().numpy(),
-                row_off=row_off, ws=ws)
+                row_off=row_off, ws=ws, tele=tele.cpu().numpy().view(np.uint32))
 
 
 def simulate_gpu_fused(w: Workload, steps: int, params=None, record: bool = True, device="cuda:0"):
     """Same decode loop through the fused lookup_decode_step entry point (the
     block mode of each step comes from the scheduler state itself)."""
-    import torch
-    import context_lookup_drafting_amd as lcd
-    params = params or lcd.default_params()
-    flat, row_off, lens, cap = pack_rows(w.hists, extra=_extra(steps))
-    B = w.B
-    dev = torch.device(device)
-    h_d = torch.from_numpy(flat).to(dev)
-    ro_d = torch.from_numpy(row_off).to(dev)
-    len_d = torch.from_numpy(lens.copy()).to(dev)
-    cap_d = torch.from_numpy(cap).to(dev)
-    max_len = int(lens.max()) + _extra(steps) if B else 0
-    ws = lcd.alloc_decode_workspace(B, max_len, dev, params)
-    state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
-    out = {k: torch.empty(B, dtype=torch.int32, device=dev)
-           for k in ("m", "e", "blk", "acc", "long_next")}
-    d = torch.empty((B, 15), dtype=torch.int32, device=dev)
-    block = torch.empty((B, 15), dtype=torch.int32, device=dev)
-    pos = np.zeros(B, np.int64)
-    recs = []
-    emitted = [[] for _ in range(B)]
-    for t in range(steps):
-        q, tgt = w.step_inputs(pos, t)
-        long_used = state[:, 0].clone()
-        lcd.lookup_decode_step(h_d, ro_d, len_d, cap_d, max_len, torch.from_numpy(q).to(dev),
-                               torch.from_numpy(tgt).to(dev), state, ws, out["m"], out["e"], d,
-                               block, out["blk"], out["acc"], out["long_next"], True, params)
-        acc_h = out["acc"].cpu().numpy()
-        for r in range(B):
-            if acc_h[r] >= 0:
-                emitted[r].extend(tgt[r, :acc_h[r] + 1].tolist())
-        pos = pos + np.maximum(acc_h, 0) + 1
-        if record:
-            recs.append(dict(m=out["m"].cpu().numpy(), e=out["e"].cpu().numpy(), d=d.cpu().numpy(),
-                             q=q, tgt=tgt, long=long_used.cpu().numpy(), block=block.cpu().numpy(),
-                             blk=out["blk"].cpu().numpy(), acc=acc_h, state=state.cpu().numpy(),
-                             long_next=out["long_next"].cpu().numpy()))
-    torch.cuda.synchronize()
-    return dict(recs=recs, emitted=emitted, lens=len_d.cpu().numpy(), flat=h_d.cpu().numpy(),
-                row_off=row_off)
+    from context_lookup_drafting_amd.decode_sim import run_fused
+    res = run_fused(w, steps, params, device, record)
+    res.pop("tele_d")
+    return res

@@ -132,7 +132,7 @@ def test_decode_step_rejects_misuse_without_launching():
         P = _P
         return L.lookup_decode_step(P(hist), P(f), P(ln), P(cap), B, max_len, P(f), P(f), P(f), prm,
                                     P(ws), ws_bytes, P(f), P(f), P(f), P(f), P(f), P(f), None,
-                                    append, None)
+                                    None, append, None)
     assert call(B=0, hist=None, ln=None, cap=None, ws=None, ws_bytes=0) == lcd.LCD_OK
     assert call(B=-1) == lcd.LCD_EINVAL
     assert call(ws_bytes=need - 8) == lcd.LCD_EINVAL          # workspace too small
@@ -142,3 +142,19 @@ def test_decode_step_rejects_misuse_without_launching():
     assert call(max_len=-5) == lcd.LCD_EINVAL
     bad = lcd.default_params(k_max=16)
     assert call(prm=ctypes.byref(bad)) == lcd.LCD_EINVAL
+
+
+def test_telemetry_entry_points_reject_misuse_without_launching():
+    L = lcd.load()
+    p = lcd.default_params()
+    pp = ctypes.byref(p)
+    f = 0x10000
+    P = _P
+    assert L.lookup_telemetry_update(None, None, None, None, None, None, None, None, 0, pp, None) == lcd.LCD_OK
+    assert L.lookup_telemetry_update(P(f), P(f), P(f), P(f), P(f), P(f), P(f), P(f), -1, pp, None) == lcd.LCD_EINVAL
+    assert L.lookup_telemetry_update(None, P(f), P(f), P(f), P(f), P(f), P(f), P(f), 4, pp, None) == lcd.LCD_EINVAL
+    assert L.lookup_telemetry_update(P(f), P(f), P(f), P(f), P(f), P(f), P(f), P(f), 4, None, None) == lcd.LCD_EINVAL
+    assert L.lookup_telemetry_reduce(P(f), P(f), 4, 0, None, None) == lcd.LCD_OK        # K = 0: no-op
+    assert L.lookup_telemetry_reduce(P(f), P(f), 4, -1, P(f), None) == lcd.LCD_EINVAL
+    assert L.lookup_telemetry_reduce(None, P(f), 4, 2, P(f), None) == lcd.LCD_EINVAL
+    assert L.lookup_telemetry_reduce(P(f), P(f), 4, 2, None, None) == lcd.LCD_EINVAL

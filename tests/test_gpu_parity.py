@@ -134,6 +134,8 @@ def _compare_sims(a, b):
                 raise AssertionError(f"step {t}: field {k} differs for requests {bad[:8]}")
     np.testing.assert_array_equal(a["lens"], b["lens"])
     np.testing.assert_array_equal(a["flat"], b["flat"])
+    if "tele" in a and "tele" in b:                    # acceptance telemetry rows
+        np.testing.assert_array_equal(a["tele"], b["tele"])
 
 
 def test_config2_simulation_200_steps(gpu):
@@ -344,3 +346,60 @@ def test_accept_append_capacity_parity(gpu):
     np.testing.assert_array_equal(ln_d.cpu().numpy(), o_ln)
     np.testing.assert_array_equal(h_d.cpu().numpy(), o_flat)
     assert (oacc == -1).any() and (oacc >= 0).any()
+
+
+def test_telemetry_reduce_matches_oracle(gpu):
+    import torch
+    import context_lookup_drafting_amd as lcd
+    rng = np.random.Generator(np.random.PCG64(11))
+    for B, K in ((0, 3), (1, 1), (300, 5), (4096, 2)):
+        tele = rng.integers(0, 2**32, (B, 32), dtype=np.uint64).astype(np.uint32)
+        cls = rng.integers(-1, K + 1, B).astype(np.int32)
+        got = lcd.telemetry_reduce(torch.from_numpy(tele.view(np.int32)).cuda(),
+                                   torch.from_numpy(cls).cuda(), K)
+        want = oracle.telemetry_reduce(tele, cls, K)
+        np.testing.assert_array_equal(got.cpu().numpy().view(np.uint64), want)
+
+
+def test_telemetry_per_class_config3(gpu):
+    """Per-class totals of a 256-step config-3 decode through the fused step
+    equal the oracle's; the copy-mode class hits and accepts far more."""
+    import torch
+    import context_lookup_drafting_amd as lcd
+    from simulate import simulate_gpu_fused, simulate_oracle
+    w = wl.config3()
+    g = simulate_gpu_fused(w, 256)
+    o = simulate_oracle(w, 256)
+    np.testing.assert_array_equal(g["tele"], o["tele"])
+    cls = w.class_ids
+    got = lcd.telemetry_reduce(torch.from_numpy(g["tele"].view(np.int32)).cuda(),
+                               torch.from_numpy(cls).cuda(), 2).cpu().numpy().view(np.uint64)
+    np.testing.assert_array_equal(got, oracle.telemetry_reduce(o["tele"], cls, 2))
+    copy, plain = got[0].astype(np.float64), got[1].astype(np.float64)
+    assert copy[1] / copy[0] > 0.4 and plain[1] / plain[0] < 0.05         # hit rates
+    assert copy[7] / copy[0] > 1.5 * (plain[7] / plain[0])                # tokens per step
+    assert copy[4] > 0 and plain[4] == 0                                  # long-block steps
+
+
+def test_decode_replay_report_config3(gpu):
+    """The package's decode replay emits exactly the target's stream and its
+    per-class report is the oracle's per-class totals, restated."""
+    from context_lookup_drafting_amd.decode_sim import run_fused, summarise
+    from simulate import simulate_oracle
+    w = wl.config3()
+    steps = 96
+    g = run_fused(w, steps, record=False)
+    for r in range(w.B):
+        em = g["emitted"][r]
+        assert em == w.truths[r][:len(em)].tolist()
+    rep = summarise(g["tele_d"], w.class_ids, w.CLASS_NAMES)
+    tot = oracle.telemetry_reduce(simulate_oracle(w, steps)["tele"], w.class_ids, 2)
+    for k, name in enumerate(w.CLASS_NAMES):
+        t = tot[k].astype(np.int64)
+        c = rep[name]
+        assert c["requests"] == int((w.class_ids == k).sum())
+        assert c["steps"] == t[0] == c["requests"] * steps
+        assert c["hit_rate"] == round(t[1] / t[0], 4)
+        assert c["tokens_per_step"] == round(t[7] / t[0], 3)
+        assert c["long_entries"] == t[5] and c["long_exits"] == t[6]
+        assert c["accepted_hist"] == t[9:25].tolist()
