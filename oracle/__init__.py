@@ -62,14 +62,16 @@ def lib():
         i32 = ctypes.c_int32
         pp = ctypes.POINTER(OracleParams)
         L.oracle_lookup_propose.argtypes = [P, P, P, i32, pp, P, P, P]
-        L.oracle_fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P]
+        L.oracle_fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P]
         L.oracle_greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P]
         L.oracle_lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P]
         L.oracle_telemetry_update.argtypes = [P, P, P, P, P, P, P, P, i32, pp]
         L.oracle_telemetry_reduce.argtypes = [P, P, i32, i32, P]
+        L.oracle_rejection_accept.argtypes = [P, P, P, P, P, i32, P, P, i32, P, P, P, P, P, P]
         for f in (L.oracle_lookup_propose, L.oracle_fuse_verify_block,
                   L.oracle_greedy_accept, L.oracle_lookup_schedule_step,
-                  L.oracle_telemetry_update, L.oracle_telemetry_reduce):
+                  L.oracle_telemetry_update, L.oracle_telemetry_reduce,
+                  L.oracle_rejection_accept):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -108,7 +110,9 @@ def lookup_one(h, params=None):
     return int(m[0]), int(e[0]), d[0]
 
 
-def fuse_verify_block(draft, match_len, q, long_mode, params=None):
+def fuse_verify_block(draft, match_len, q, long_mode, params=None, with_mask=False):
+    """Returns (block [B,15], block_len [B]) and, with ``with_mask``, the
+    uint32 [B] mask of slots holding the draft model's own token."""
     params = params or default_params()
     draft = _c(draft, np.int32).reshape(-1, DRAFT_STRIDE)
     match_len = _c(match_len, np.int32)
@@ -117,10 +121,11 @@ def fuse_verify_block(draft, match_len, q, long_mode, params=None):
     B = len(match_len)
     blk = np.zeros((B, DRAFT_STRIDE), np.int32)
     bl = np.zeros(B, np.int32)
+    mask = np.zeros(B, np.uint32) if with_mask else None
     if B:
         lib().oracle_fuse_verify_block(_ptr(draft), _ptr(match_len), _ptr(q), _ptr(long_mode),
-                                       B, ctypes.byref(params), _ptr(blk), _ptr(bl))
-    return blk, bl
+                                       B, ctypes.byref(params), _ptr(blk), _ptr(bl), _ptr(mask))
+    return (blk, bl, mask) if with_mask else (blk, bl)
 
 
 def greedy_accept(block, block_len, target, hist=None, row_off=None, lens=None, cap=None):
@@ -186,3 +191,35 @@ def telemetry_reduce(tele, class_id, K):
     out = np.zeros((K, TELE_WORDS), np.uint64)
     lib().oracle_telemetry_reduce(_ptr(tele), _ptr(class_id), len(class_id), K, _ptr(out))
     return out
+
+
+def rejection_accept(block, block_len, target_probs, u_accept, u_sample, model_mask=None,
+                     model_probs=None, hist=None, row_off=None, lens=None, cap=None):
+    """Sampled verification with point-mass lookup proposals.
+
+    target_probs float32 [B,16,V]; model_probs float32 [B,7,V] or None;
+    u_accept float64 [B,15]; u_sample uint64 [B]; model_mask uint32 [B] or None.
+    Returns (accept [B], emitted [B,16]); when ``hist`` is given the emitted
+    tokens are appended in place (``hist`` and ``lens`` are modified)."""
+    block = _c(block, np.int32).reshape(-1, DRAFT_STRIDE)
+    block_len = _c(block_len, np.int32)
+    B = len(block_len)
+    tp = _c(target_probs, np.float32).reshape(B, TARGET_STRIDE, -1)
+    V = tp.shape[2]
+    assert V < (1 << 23)
+    mp = None if model_probs is None else _c(model_probs, np.float32).reshape(B, Q_STRIDE, V)
+    mm = None if model_mask is None else _c(model_mask, np.uint32)
+    ua = _c(u_accept, np.float64).reshape(B, DRAFT_STRIDE)
+    us = _c(u_sample, np.uint64).reshape(B)
+    acc = np.zeros(B, np.int32)
+    em = np.full((B, TARGET_STRIDE), PAD, np.int32)
+    if hist is not None:
+        for a in (hist, lens):
+            assert a.dtype == np.int32 and a.flags.c_contiguous
+        row_off = _c(row_off, np.int64)
+        cap = _c(cap, np.int32)
+    if B:
+        lib().oracle_rejection_accept(_ptr(block), _ptr(block_len), _ptr(mm), _ptr(tp), _ptr(mp),
+                                      V, _ptr(ua), _ptr(us), B, _ptr(acc), _ptr(em), _ptr(hist),
+                                      _ptr(row_off), _ptr(lens), _ptr(cap))
+    return acc, em

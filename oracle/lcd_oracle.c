@@ -104,10 +104,16 @@ int oracle_lookup_propose(const int32_t *hist, const int64_t *row_off, const int
  * draft whenever the match is at least tail_min tokens, independently of the
  * head decision, and PAD otherwise.  Slots beyond the verified length, and
  * draft slots at or past k_max, are never taken from the lookup.
+  *
+ * model_mask (may be NULL): bit i is set when slot i holds the draft model's own
+ * token q[i] (a head slot the lookup did not replace), so that a sampled
+ * verifier knows which slots carry the draft model's distribution; every other
+ * non-PAD slot is a lookup token.
  */
 int oracle_fuse_verify_block(const int32_t *draft, const int32_t *match_len,
                              const int32_t *q, const int32_t *long_mode, int32_t B,
-                             const oracle_params *p, int32_t *block, int32_t *block_len)
+                             const oracle_params *p, int32_t *block, int32_t *block_len,
+                             uint32_t *model_mask)
 {
     for (int32_t r = 0; r < B; ++r) {
         const int32_t *d = draft + (int64_t)r * ORACLE_DRAFT_STRIDE;
@@ -123,17 +129,26 @@ int oracle_fuse_verify_block(const int32_t *draft, const int32_t *match_len,
         int tail = is_long && (m >= p->tail_min);
         int32_t blk = is_long ? p->n_block : p->n_head;
 
+        uint32_t from_model = 0;   /* bit i: slot i holds the draft model's proposal */
         for (int32_t i = 0; i < ORACLE_DRAFT_STRIDE; ++i) {
             int32_t v;
-            if (i >= blk)
+            if (i >= blk) {
                 v = ORACLE_PAD;
-            else if (i < p->n_head)
-                v = (head && i < p->k_max) ? d[i] : qr[i];
-            else
+            } else if (i < p->n_head) {
+                if (head && i < p->k_max) {
+                    v = d[i];
+                } else {
+                    v = qr[i];
+                    from_model |= 1u << i;
+                }
+            } else {
                 v = (tail && i < p->k_max) ? d[i] : ORACLE_PAD;
+            }
             out[i] = v;
         }
         block_len[r] = blk;
+        if (model_mask != NULL)
+            model_mask[r] = from_model;
     }
     return 0;
 }
@@ -169,6 +184,171 @@ int oracle_greedy_accept(const int32_t *block, const int32_t *block_len,
             }
             for (int32_t i = 0; i <= a; ++i)
                 hist[row_off[r] + have + i] = t[i];
+            len[r] = (int32_t)(have + a + 1);
+        }
+        accept[r] = a;
+    }
+    return 0;
+}
+
+/*
+ * Sampled verification with point-mass lookup proposals (article, closing
+ * paragraph on losslessness: for sampled requests each lookup-filled slot is
+ * rewritten as a point mass on its token, a legal proposal distribution for the
+ * speculative rejection sampler, so the output distribution is unchanged; the
+ * Polish speculative-decoding post, on verification: the first rejected
+ * proposal ends the run).
+ *
+ * Per request, the verified slots are i < L, L = block_len clamped to 0..15.
+ * target_probs holds 16 rows of V probabilities, row i being the target's
+ * distribution for the token after the block's first i slots; model_probs (may
+ * be NULL) holds the draft model's 7 head rows.  Slot i's proposal
+ * distribution is the draft model's row i when bit i of model_mask is set, i < 7
+ * and model_probs is given; otherwise (lookup slots, or a draft model that gives
+ * no distribution) it is the point mass on block[i].
+ *
+ * Walking i = 0, 1, ...: a slot whose token is PAD or outside [0, V) ends the
+ * run with nothing proposed there.  Otherwise, with P = p_i(x) and Q = q_i(x)
+ * (Q = 1 for a point mass), the slot is accepted iff u_i * Q < P, i.e. with
+ * probability min(1, P/Q) for u_i uniform on [0,1).  The first rejection ends
+ * the run; its token is drawn from the residual max(p_i - q_i, 0) renormalised
+ * (for a point mass: p_i with x removed).  When the run ends without a
+ * rejection (all L slots accepted, or a slot with nothing proposed), the token
+ * is drawn from p_a itself (the bonus token).  So a = accepted slots, and the
+ * step emits block[0..a-1] followed by the drawn token.
+ *
+ * Precision (the token is an integer decided by floating point, so the
+ * arithmetic is fixed here and the kernel takes the same decisions):
+ *  - probabilities are read as fp32 and clamped into [0, 1] (NaN reads as 0);
+ *  - the acceptance test is evaluated in fp64 (u_i is fp64; u_i * Q is the only
+ *    rounding step);
+ *  - the residual difference p - q is an fp32 subtraction, negative -> 0;
+ *  - drawing: each weight w_j becomes the integer W_j = floor(w_j * 2^40), the
+ *    total S = sum W_j is exact in 64 bits (V < 2^23), t = floor(u_s * S / 2^64)
+ *    for the request's 64-bit uniform word u_s, and the token is the smallest j
+ *    whose running total W_0 + ... + W_j exceeds t.  A probability below 2^-40
+ *    gets weight 0; the drawn distribution is W_j / S.
+ * An all-zero residual falls back to p_a; if that is all zero too the request
+ * emits nothing: accept = -1, the emitted row is all PAD and nothing is appended.
+ *
+ * emitted int32 [B*16]: the a+1 emitted tokens, then PAD.  With hist non-NULL
+ * the emitted tokens are appended exactly as greedy_accept appends them.
+ */
+static float prob01(float x)
+{
+    if (!(x > 0.0f)) return 0.0f;   /* negative, zero or NaN */
+    if (x > 1.0f) return 1.0f;
+    return x;
+}
+
+static uint64_t fixed40(float w)   /* floor(w * 2^40) for w in [0, 1] */
+{
+    return (uint64_t)((double)w * 1099511627776.0);
+}
+
+int oracle_rejection_accept(const int32_t *block, const int32_t *block_len,
+                            const uint32_t *model_mask, const float *target_probs,
+                            const float *model_probs, int32_t V, const double *u_accept,
+                            const uint64_t *u_sample, int32_t B, int32_t *accept,
+                            int32_t *emitted, int32_t *hist, const int64_t *row_off,
+                            int32_t *len, const int32_t *cap)
+{
+    for (int32_t r = 0; r < B; ++r) {
+        const int32_t *blkr = block + (int64_t)r * ORACLE_DRAFT_STRIDE;
+        int32_t *em = emitted + (int64_t)r * ORACLE_TARGET_STRIDE;
+        int32_t L = block_len[r];
+        if (L < 0) L = 0;
+        if (L > ORACLE_DRAFT_STRIDE) L = ORACLE_DRAFT_STRIDE;
+
+        /* 1. walk the slots */
+        int32_t a = 0;
+        int rejected = 0;
+        int rej_model = 0;   /* the rejected slot's proposal was the draft model's row */
+        int32_t rej_tok = 0;
+        while (a < L) {
+            int32_t x = blkr[a];
+            if (x < 0 || x >= V)
+                break;
+            const float *pr = target_probs + ((int64_t)r * ORACLE_TARGET_STRIDE + a) * V;
+            int use_model = model_probs != NULL && model_mask != NULL &&
+                            a < ORACLE_Q_STRIDE && ((model_mask[r] >> a) & 1u);
+            double P = prob01(pr[x]);
+            double Q = 1.0;
+            if (use_model)
+                Q = prob01(model_probs[((int64_t)r * ORACLE_Q_STRIDE + a) * V + x]);
+            if (u_accept[(int64_t)r * ORACLE_DRAFT_STRIDE + a] * Q < P) {
+                a++;
+                continue;
+            }
+            rejected = 1;
+            rej_model = use_model;
+            rej_tok = x;
+            break;
+        }
+
+        /* 2. the distribution the last token is drawn from, as integer weights */
+        const float *pr = target_probs + ((int64_t)r * ORACLE_TARGET_STRIDE + a) * V;
+        const float *qr = rej_model
+            ? model_probs + ((int64_t)r * ORACLE_Q_STRIDE + a) * V : NULL;
+        uint64_t S = 0;
+        if (rejected) {
+            for (int32_t j = 0; j < V; ++j) {
+                float w;
+                if (qr != NULL) {
+                    w = prob01(pr[j]) - prob01(qr[j]);
+                    if (!(w > 0.0f)) w = 0.0f;
+                } else {
+                    w = (j == rej_tok) ? 0.0f : prob01(pr[j]);
+                }
+                S += fixed40(w);
+            }
+        }
+        int plain = !rejected || S == 0;
+        if (plain) {
+            S = 0;
+            for (int32_t j = 0; j < V; ++j)
+                S += fixed40(prob01(pr[j]));
+        }
+        for (int32_t i = 0; i < ORACLE_TARGET_STRIDE; ++i)
+            em[i] = ORACLE_PAD;
+        if (S == 0) {
+            accept[r] = -1;
+            continue;
+        }
+
+        /* 3. inverse-CDF draw on the integer weights */
+        uint64_t t = (uint64_t)(((unsigned __int128)u_sample[r] * S) >> 64);
+        uint64_t run = 0;
+        int32_t z = -1;
+        for (int32_t j = 0; j < V; ++j) {
+            float w;
+            if (plain) {
+                w = prob01(pr[j]);
+            } else if (qr != NULL) {
+                w = prob01(pr[j]) - prob01(qr[j]);
+                if (!(w > 0.0f)) w = 0.0f;
+            } else {
+                w = (j == rej_tok) ? 0.0f : prob01(pr[j]);
+            }
+            run += fixed40(w);
+            if (run > t) {
+                z = j;
+                break;
+            }
+        }
+
+        /* 4. emit, and append as the greedy verifier does */
+        for (int32_t i = 0; i < a; ++i)
+            em[i] = blkr[i];
+        em[a] = z;
+        if (hist != NULL) {
+            int64_t have = len[r] > 0 ? len[r] : 0;
+            if (have + a + 1 > (int64_t)cap[r]) {
+                accept[r] = -1;
+                continue;
+            }
+            for (int32_t i = 0; i <= a; ++i)
+                hist[row_off[r] + have + i] = em[i];
             len[r] = (int32_t)(have + a + 1);
         }
         accept[r] = a;
