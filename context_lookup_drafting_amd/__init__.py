@@ -10,8 +10,11 @@ Entry points (same names as the C ABI):
   lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end, draft, params)
   lookup_decode_step(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
                      match_len, match_end, draft, block, block_len, accept, long_next, append, params)
-  fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len, params)
+  fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len, params,
+                    model_mask=None)
   greedy_accept(block, block_len, target, accept, hist=None, row_off=None, lens=None, cap=None)
+  rejection_accept(block, block_len, target_probs, u_accept, u_sample, workspace, accept, emitted,
+                   model_mask=None, model_probs=None, hist=None, row_off=None, lens=None, cap=None)
   lookup_schedule_step(state, match_len, accept, block_len, long_next, params)
 """
 
@@ -73,7 +76,7 @@ def load():
         L.lcd_workspace_bytes.restype = ctypes.c_size_t
         L.lookup_propose.argtypes = [P, P, P, i32, i32, pp, P, P, P, P, P]
         L.lookup_propose_timed.argtypes = [P, P, P, i32, i32, pp, P, P, P, P, P, P, P]
-        L.fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P]
+        L.fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P, P]
         L.lcd_decode_step_workspace_bytes.argtypes = [i32, i32, pp]
         L.lcd_decode_step_workspace_bytes.restype = ctypes.c_size_t
         dec = [P, P, P, P, i32, i32, P, P, P, pp, P, ctypes.c_size_t, P, P, P, P, P, P, P, P, i32, P]
@@ -83,10 +86,15 @@ def load():
         L.lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P, P]
         L.lookup_telemetry_update.argtypes = [P, P, P, P, P, P, P, P, i32, pp, P]
         L.lookup_telemetry_reduce.argtypes = [P, P, i32, i32, P, P]
+        L.rejection_accept_workspace_bytes.argtypes = [i32, i32]
+        L.rejection_accept_workspace_bytes.restype = ctypes.c_size_t
+        rej = [P, P, P, P, P, i32, P, P, i32, i32, P, ctypes.c_size_t, P, P, P, P, P, P, P]
+        L.rejection_accept.argtypes = rej
+        L.rejection_accept_timed.argtypes = rej + [P, P]
         for f in (L.lookup_propose, L.lookup_propose_timed, L.fuse_verify_block,
                   L.greedy_accept, L.lookup_schedule_step, L.lookup_decode_step,
                   L.lookup_decode_step_timed, L.lookup_telemetry_update,
-                  L.lookup_telemetry_reduce):
+                  L.lookup_telemetry_reduce, L.rejection_accept, L.rejection_accept_timed):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,7 +195,9 @@ def lookup_propose_timed(hist, row_off, lens, max_len, workspace, match_len, mat
 
 
 def fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len,
-                      params: Params | None = None):
+                      params: Params | None = None, model_mask=None):
+    """Verify block of every request; ``model_mask`` (int32 [B], optional)
+    gets bit i set for each slot keeping the draft model's token."""
     import torch
     p = params or default_params()
     B = match_len.numel()
@@ -200,6 +210,8 @@ def fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len
         ctypes.c_int32(B), ctypes.byref(p),
         _dev(block, "block", torch.int32, B * DRAFT_STRIDE, dev),
         _dev(block_len, "block_len", torch.int32, B, dev),
+        ctypes.c_void_p(None) if model_mask is None
+        else _dev(model_mask, "model_mask", torch.int32, B, dev),
         _stream(dev)))
 
 
@@ -351,3 +363,79 @@ def telemetry_reduce(telemetry, class_id, K: int):
         _dev(class_id, "class_id", torch.int32, B, dev), ctypes.c_int32(B), ctypes.c_int32(K),
         _dev(out, "out", torch.int64, K * TELE_WORDS, dev), _stream(dev)))
     return out
+
+
+SAMPLE_MAX_VOCAB = 1 << 22
+
+
+def rejection_accept_workspace_bytes(B: int, V: int) -> int:
+    return int(load().rejection_accept_workspace_bytes(int(B), int(V)))
+
+
+def alloc_rejection_workspace(B: int, V: int, device):
+    """Zero-filled rejection_accept workspace (kept zero by every call)."""
+    import torch
+    n = max(rejection_accept_workspace_bytes(B, V), 16)
+    return torch.zeros((n + 7) // 8, dtype=torch.int64, device=device)
+
+
+def _rejection_args(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
+                    emitted, model_mask, model_probs, hist, row_off, lens, cap, wg_units):
+    import torch
+    B = block_len.numel()
+    dev = block_len.device
+    if target_probs.dim() != 3 or target_probs.shape[0] != B or target_probs.shape[1] != TARGET_STRIDE:
+        raise ValueError("target_probs must be [B, 16, V]")
+    V = target_probs.shape[2]
+    if model_probs is not None and tuple(model_probs.shape) != (B, Q_STRIDE, V):
+        raise ValueError("model_probs must be [B, 7, V]")
+    if workspace.numel() * workspace.element_size() < rejection_accept_workspace_bytes(B, V):
+        raise ValueError("workspace too small")
+    none = ctypes.c_void_p(None)
+    if hist is None:
+        h = ro = ln = cp = none
+    else:
+        h = _dev(hist, "hist", torch.int32, device=dev)
+        ro = _dev(row_off, "row_off", torch.int64, B, dev)
+        ln = _dev(lens, "lens", torch.int32, B, dev)
+        cp = _dev(cap, "cap", torch.int32, B, dev)
+    return (
+        _dev(block, "block", torch.int32, B * DRAFT_STRIDE, dev),
+        _dev(block_len, "block_len", torch.int32, B, dev),
+        none if model_mask is None else _dev(model_mask, "model_mask", torch.int32, B, dev),
+        _dev(target_probs, "target_probs", torch.float32, B * TARGET_STRIDE * V, dev),
+        none if model_probs is None
+        else _dev(model_probs, "model_probs", torch.float32, B * Q_STRIDE * V, dev),
+        ctypes.c_int32(V),
+        _dev(u_accept, "u_accept", torch.float64, B * DRAFT_STRIDE, dev),
+        _dev(u_sample, "u_sample", torch.int64, B, dev),
+        ctypes.c_int32(B), ctypes.c_int32(int(wg_units)),
+        _dev(workspace, "workspace", workspace.dtype, device=dev),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _dev(accept, "accept", torch.int32, B, dev),
+        _dev(emitted, "emitted", torch.int32, B * TARGET_STRIDE, dev),
+        h, ro, ln, cp, _stream(dev),
+    )
+
+
+def rejection_accept(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
+                     emitted, model_mask=None, model_probs=None, hist=None, row_off=None,
+                     lens=None, cap=None, wg_units: int = 0):
+    """Sampled verification with point-mass lookup proposals (include/lcd.h,
+    rejection_accept).  target_probs float32 [B,16,V], model_probs float32
+    [B,7,V] or None, u_accept float64 [B,15], u_sample int64 [B] (the bits of
+    uniform 64-bit words), model_mask int32 [B] or None; writes accept int32
+    [B] and emitted int32 [B,16]; appends when ``hist`` is given."""
+    args = _rejection_args(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
+                           emitted, model_mask, model_probs, hist, row_off, lens, cap, wg_units)
+    _check("rejection_accept", load().rejection_accept(*args))
+
+
+def rejection_accept_timed(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
+                           emitted, ev_start, ev_stop, model_mask=None, model_probs=None,
+                           wg_units: int = 0):
+    """rejection_accept with GPU-stamped start/stop events, for profiling."""
+    args = _rejection_args(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
+                           emitted, model_mask, model_probs, None, None, None, None, wg_units)
+    _check("rejection_accept_timed", load().rejection_accept_timed(
+        *args, ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))

@@ -45,18 +45,29 @@ __device__ inline int fuse_slot(int i, int d, int q, bool head, bool tail, int b
     return LCD_PAD;
 }
 
-// Verify block of one request.  Returns the number of draft slots verified.
+// True when verify slot i keeps the draft model's own token (a head slot the
+// lookup draft does not replace); every other non-PAD slot is a lookup token.
+__device__ inline bool fuse_slot_from_model(int i, bool head, const FuseArgs &a) {
+    return i < a.n_head && !(head && i < a.k_max);
+}
+
+// Verify block of one request.  Returns the number of draft slots verified;
+// from_model gets bit i set for each slot that keeps the draft model's token.
 __device__ inline int fuse_row(const int (&d)[LCD_DRAFT_STRIDE], int m, const int (&q)[LCD_Q_STRIDE],
-                               bool is_long, const FuseArgs &a, int (&out)[LCD_DRAFT_STRIDE]) {
+                               bool is_long, const FuseArgs &a, int (&out)[LCD_DRAFT_STRIDE],
+                               uint32_t &from_model) {
     bool agree = true;
 #pragma unroll
     for (int i = 0; i < LCD_Q_STRIDE; ++i)
         if (i < a.agree_n && q[i] != d[i]) agree = false;
     bool head, tail;
     const int blk = fuse_mode(m, agree, is_long, a, head, tail);
+    from_model = 0;
 #pragma unroll
-    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i)
+    for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) {
         out[i] = fuse_slot(i, d[i], i < LCD_Q_STRIDE ? q[i] : LCD_PAD, head, tail, blk, a);
+        if (fuse_slot_from_model(i, head, a)) from_model |= 1u << i;
+    }
     return blk;
 }
 

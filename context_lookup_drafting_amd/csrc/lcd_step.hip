@@ -25,7 +25,8 @@ constexpr int kStepThreads = 256;
 __global__ void __launch_bounds__(kStepThreads)
 fuse_kernel(const int32_t *__restrict__ draft, const int32_t *__restrict__ match_len,
             const int32_t *__restrict__ q, const int32_t *__restrict__ long_mode, int32_t B,
-            FuseArgs a, int32_t *__restrict__ block, int32_t *__restrict__ block_len) {
+            FuseArgs a, int32_t *__restrict__ block, int32_t *__restrict__ block_len,
+            uint32_t *__restrict__ model_mask) {
     const int r = blockIdx.x * kStepThreads + threadIdx.x;
     if (r >= B) return;
     int dv[LCD_DRAFT_STRIDE], qv[LCD_Q_STRIDE], out[LCD_DRAFT_STRIDE];
@@ -33,10 +34,12 @@ fuse_kernel(const int32_t *__restrict__ draft, const int32_t *__restrict__ match
     for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) dv[i] = draft[(int64_t)r * LCD_DRAFT_STRIDE + i];
 #pragma unroll
     for (int i = 0; i < LCD_Q_STRIDE; ++i) qv[i] = q[(int64_t)r * LCD_Q_STRIDE + i];
-    const int blk = fuse_row(dv, match_len[r], qv, long_mode[r] != 0, a, out);
+    uint32_t from_model;
+    const int blk = fuse_row(dv, match_len[r], qv, long_mode[r] != 0, a, out, from_model);
 #pragma unroll
     for (int i = 0; i < LCD_DRAFT_STRIDE; ++i) block[(int64_t)r * LCD_DRAFT_STRIDE + i] = out[i];
     block_len[r] = blk;
+    if (model_mask != nullptr) model_mask[r] = from_model;
 }
 
 __global__ void __launch_bounds__(kStepThreads)
@@ -150,7 +153,7 @@ extern "C" int lcd_check_params(const lcd_params *p) {
 extern "C" int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
                                  const int32_t *model_draft, const int32_t *long_mode, int32_t B,
                                  const lcd_params *p, int32_t *block, int32_t *block_len,
-                                 void *stream) {
+                                 uint32_t *model_mask, void *stream) {
     using namespace lcd;
     if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
@@ -159,7 +162,7 @@ extern "C" int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
     const FuseArgs a = fuse_args(p);
     hipLaunchKernelGGL(fuse_kernel, dim3(blocks_for(B)), dim3(kStepThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), draft, match_len, model_draft,
-                       long_mode, B, a, block, block_len);
+                       long_mode, B, a, block, block_len, model_mask);
     return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
 }
 

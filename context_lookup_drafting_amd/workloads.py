@@ -347,3 +347,94 @@ def all_strings(alphabet: int, n: int) -> np.ndarray:
         out[:, j] = idx % alphabet
         idx //= alphabet
     return out
+
+
+# ---------------------------------------------------------------------------
+# Sampled verification inputs
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class SampledBatch:
+    """Inputs of one sampled verification step for B requests.
+
+    block / block_len / model_mask have the fused verify block's layout (15
+    slots, PAD past the verified length, bit i of the mask set for a slot that
+    keeps the draft model's token).  target_probs [B,16,V] and model_probs
+    [B,7,V] are float32 rows that sum to 1 up to float32 rounding; u_accept
+    [B,15] holds float64 uniforms on [0,1) and u_sample [B] uniform 64-bit
+    words, the random numbers the verifier consumes."""
+
+    name: str
+    seed: int
+    V: int
+    block: np.ndarray
+    block_len: np.ndarray
+    model_mask: np.ndarray
+    target_probs: np.ndarray
+    model_probs: Optional[np.ndarray]
+    u_accept: np.ndarray
+    u_sample: np.ndarray
+    classes: List[str]
+
+    @property
+    def B(self) -> int:
+        return len(self.block_len)
+
+
+def _background_rows(rng, n_rows: int, V: int, zipf_w: np.ndarray) -> np.ndarray:
+    """n_rows float32 rows: the Zipf profile zipf_w over a different
+    pseudo-permutation of the vocabulary per row (token = (rank * a + b) mod V
+    with a odd and coprime to V), each row summing to 1."""
+    out = np.empty((n_rows, V), np.float32)
+    ranks = np.arange(V, dtype=np.int64)
+    for i in range(n_rows):
+        while True:
+            a = int(rng.integers(1, V)) | 1
+            if math.gcd(a, V) == 1:
+                break
+        b = int(rng.integers(0, V))
+        out[i, (ranks * a + b) % V] = zipf_w
+    return out
+
+
+def sampled_batch(seed: int = 1006, B: int = 64, V: int = 248_320, with_model: bool = True,
+                  name: Optional[str] = None) -> SampledBatch:
+    """Half copy-mode requests (long blocks, lookup tokens that the target
+    gives most of its mass: 0.75-0.99), half ordinary (short blocks, draft-model
+    tokens with target mass 0.02-0.6 and draft-model mass 0.3-0.9).  Every row
+    mixes that point mass with a Zipf(1.1) background; bonus rows and PAD slots'
+    rows are background only.  Vocabulary 248,320 by default (the full
+    vocabulary the pages name); V must be a multiple of 4."""
+    assert V % 4 == 0 and V >= 4
+    rng = np.random.Generator(np.random.PCG64(seed))
+    zw = np.arange(1, V + 1, dtype=np.float64) ** -1.1
+    zw = (zw / zw.sum()).astype(np.float32)
+    classes = ["copy" if r < (B + 1) // 2 else "ordinary" for r in range(B)]
+    block = np.full((B, N_DRAFT), PAD, np.int32)
+    block_len = np.zeros(B, np.int32)
+    model_mask = np.zeros(B, np.uint32)
+    tp = _background_rows(rng, B * N_TARGET, V, zw).reshape(B, N_TARGET, V)
+    mp = _background_rows(rng, B * N_Q, V, zw).reshape(B, N_Q, V) if with_model else None
+    for r in range(B):
+        copy = classes[r] == "copy"
+        blk = N_DRAFT if (copy and rng.random() < 0.7) else N_Q
+        block_len[r] = blk
+        from_model = (not copy) or rng.random() < 0.2        # head kept the draft model's tokens
+        if from_model:
+            model_mask[r] = (1 << N_Q) - 1
+        n_tok = blk if (copy or blk == N_Q) else N_Q          # ordinary long blocks: tail PAD
+        block[r, :n_tok] = rng.integers(0, V, n_tok)
+        for i in range(n_tok):
+            x = int(block[r, i])
+            model_slot = bool((model_mask[r] >> i) & 1)
+            m = rng.uniform(0.75, 0.99) if (copy and not model_slot) else rng.uniform(0.02, 0.6)
+            tp[r, i] *= np.float32(1.0 - m)
+            tp[r, i, x] += np.float32(m)
+            if mp is not None and model_slot:
+                w = rng.uniform(0.3, 0.9)
+                mp[r, i] *= np.float32(1.0 - w)
+                mp[r, i, x] += np.float32(w)
+    u_accept = rng.random((B, N_DRAFT))
+    u_sample = rng.integers(0, 2 ** 64, B, dtype=np.uint64)
+    return SampledBatch(name or f"sampled_b{B}_v{V}", seed, V, block, block_len, model_mask, tp,
+                        mp, u_accept, u_sample, classes)

@@ -141,13 +141,19 @@ int lookup_propose_timed(const int32_t *hist, const int64_t *row_off, const int3
  * Slots n_head <= i < blk (tail, long blocks only): draft[i] if m >= tail_min
  * and i < k_max, else LCD_PAD.  Slots i >= blk: LCD_PAD.
  *
+ * model_mask (nullable) gets bit i set for each slot i that keeps the draft
+ * model's own token (i < n_head and not replaced by the lookup draft); every
+ * other non-PAD slot holds a lookup token.  rejection_accept uses it to pick
+ * each slot's proposal distribution.
+ *
  * draft int32[B*15], match_len int32[B], model_draft (q) int32[B*7],
  * long_mode int32[B] (non-zero = long block) -> block int32[B*15],
- * block_len int32[B].
+ * block_len int32[B], model_mask uint32[B] (nullable).
  */
 int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
                       const int32_t *model_draft, const int32_t *long_mode, int32_t B,
-                      const lcd_params *p, int32_t *block, int32_t *block_len, void *stream);
+                      const lcd_params *p, int32_t *block, int32_t *block_len,
+                      uint32_t *model_mask, void *stream);
 
 /*
  * greedy_accept -- article, closing paragraph (greedy verification never reads
@@ -280,6 +286,88 @@ int lookup_telemetry_update(uint32_t *telemetry, const int32_t *match_len, const
  */
 int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, int32_t B,
                             int32_t K, uint64_t *out, void *stream);
+
+/* Largest vocabulary rejection_accept takes (2^22). */
+#define LCD_SAMPLE_MAX_VOCAB 4194304
+
+/*
+ * rejection_accept_workspace_bytes -- bytes of the rejection_accept workspace
+ * for B requests over a vocabulary of V: B * 8 * (2 + 2 * ceil(V / 1024)).
+ * 0 when B <= 0 or V <= 0.
+ */
+size_t rejection_accept_workspace_bytes(int32_t B, int32_t V);
+
+/*
+ * rejection_accept -- sampled verification with point-mass lookup proposals.
+ * Article, closing paragraph on losslessness (for sampled requests each
+ * lookup-filled slot is rewritten as a point mass on its token, a legal
+ * proposal distribution for speculative rejection sampling, so the output
+ * distribution is unchanged); the Polish speculative-decoding post, on
+ * verification (the first rejected proposal ends the run).
+ *
+ * Per request r, slots i < L are verified, L = block_len[r] clamped to 0..15.
+ * target_probs[r, i, :] is the target's distribution for the token after the
+ * block's first i slots (row L is the bonus row).  Slot i's proposal
+ * distribution is model_probs[r, i, :] when model_probs is non-NULL, i < 7 and
+ * bit i of model_mask[r] is set (fuse_verify_block's model_mask); otherwise it
+ * is the point mass on block[r, i].  Walking i = 0, 1, ...:
+ *   - a token that is PAD or outside [0, V) ends the run, nothing proposed;
+ *   - with P = p_i(x), Q = q_i(x) (1 for a point mass), the slot is accepted
+ *     iff u_accept[r, i] * Q < P, i.e. with probability min(1, P/Q);
+ *   - the first rejection ends the run, and the token is drawn from the
+ *     residual max(p_i - q_i, 0) (for a point mass: p_i without x);
+ *   - a run that ends without a rejection draws from p_a itself.
+ * accept[r] = a, the accepted slots; emitted[r] = block[0..a-1], the drawn
+ * token, then PAD.
+ *
+ * Arithmetic (the drawn token is an integer decided by floating point, so it
+ * is fixed here): probabilities are read as fp32 clamped into [0, 1] (NaN reads
+ * as 0); the acceptance test is in fp64; p - q is an fp32 subtraction, negative
+ * results 0; each weight w becomes the integer floor(w * 2^40), their total S
+ * is exact, t = floor(u_sample[r] * S / 2^64), and the token is the smallest j
+ * whose running total of weights exceeds t.  An all-zero residual falls back to
+ * p_a; an all-zero p_a draws nothing: accept[r] = -1 and emitted[r] is all PAD.
+ * The result is independent of the launch shape and bit-identical to the plain
+ * definition.
+ *
+ * With hist non-NULL the a+1 emitted tokens are appended exactly as
+ * greedy_accept appends the target's tokens (n = max(len[r], 0); if
+ * n+a+1 > cap[r] nothing is written and accept[r] = -1, emitted[r] still
+ * holding the drawn tokens).
+ *
+ * block int32[B*15], block_len int32[B], model_mask uint32[B] (nullable),
+ * target_probs float32[B*16*V], model_probs float32[B*7*V] (nullable), both
+ * 16-byte aligned; u_accept float64[B*15]; u_sample uint64[B] (uniform 64-bit
+ * words); accept int32[B]; emitted int32[B*16]; hist / row_off / len / cap as
+ * for greedy_accept.  V must be a multiple of 4 in [4, LCD_SAMPLE_MAX_VOCAB]
+ * (pad a vocabulary with zero-probability entries).  wg_units: vocabulary
+ * units of 1024 per workgroup, 0 = automatic (launch tuning only).
+ * workspace: device memory of at least rejection_accept_workspace_bytes(B, V),
+ * 8-byte aligned, zero before the first call and left zero by every call;
+ * calls that share a workspace must not overlap.  Returns LCD_EINVAL for a
+ * bad size, alignment, pointer or too small a workspace, before launching.
+ * One launch, no allocation.
+ */
+int rejection_accept(const int32_t *block, const int32_t *block_len, const uint32_t *model_mask,
+                     const float *target_probs, const float *model_probs, int32_t V,
+                     const double *u_accept, const uint64_t *u_sample, int32_t B,
+                     int32_t wg_units, void *workspace, size_t workspace_bytes,
+                     int32_t *accept, int32_t *emitted, int32_t *hist, const int64_t *row_off,
+                     int32_t *len, const int32_t *cap, void *stream);
+
+/*
+ * rejection_accept_timed -- for profiling only: rejection_accept launched so
+ * that the GPU stamps the kernel's start into ev_start and its end into
+ * ev_stop (hipEvent_t, either may be NULL).
+ */
+int rejection_accept_timed(const int32_t *block, const int32_t *block_len,
+                           const uint32_t *model_mask, const float *target_probs,
+                           const float *model_probs, int32_t V, const double *u_accept,
+                           const uint64_t *u_sample, int32_t B, int32_t wg_units,
+                           void *workspace, size_t workspace_bytes, int32_t *accept,
+                           int32_t *emitted, int32_t *hist, const int64_t *row_off,
+                           int32_t *len, const int32_t *cap, void *stream, void *ev_start,
+                           void *ev_stop);
 
 #ifdef __cplusplus
 }

@@ -84,7 +84,7 @@ def test_entry_points_reject_misuse_without_launching():
     assert L.lookup_propose(_P(fake), _P(fake), _P(fake), 4, 10, None, _P(fake),
                             _P(fake), _P(fake), _P(fake), s) == lcd.LCD_EINVAL
     assert L.fuse_verify_block(None, _P(fake), _P(fake), _P(fake), 3, pp, _P(fake), _P(fake),
-                               s) == lcd.LCD_EINVAL
+                               None, s) == lcd.LCD_EINVAL
     assert L.greedy_accept(_P(fake), _P(fake), _P(fake), 3, None, None, None, None, None,
                            s) == lcd.LCD_EINVAL
     # appending needs row offsets, lengths and capacities
@@ -99,7 +99,9 @@ def test_empty_batch_is_a_noop():
     p = lcd.default_params()
     pp = ctypes.byref(p)
     assert L.lookup_propose(None, None, None, 0, 0, pp, None, None, None, None, None) == lcd.LCD_OK
-    assert L.fuse_verify_block(None, None, None, None, 0, pp, None, None, None) == lcd.LCD_OK
+    assert L.fuse_verify_block(None, None, None, None, 0, pp, None, None, None, None) == lcd.LCD_OK
+    assert L.rejection_accept(None, None, None, None, None, 64, None, None, 0, 0, None, 0, None,
+                              None, None, None, None, None, None) == lcd.LCD_OK
     assert L.greedy_accept(None, None, None, 0, None, None, None, None, None, None) == lcd.LCD_OK
     assert L.lookup_schedule_step(None, None, None, None, 0, pp, None, None) == lcd.LCD_OK
 
@@ -158,3 +160,35 @@ def test_telemetry_entry_points_reject_misuse_without_launching():
     assert L.lookup_telemetry_reduce(P(f), P(f), 4, -1, P(f), None) == lcd.LCD_EINVAL
     assert L.lookup_telemetry_reduce(None, P(f), 4, 2, P(f), None) == lcd.LCD_EINVAL
     assert L.lookup_telemetry_reduce(P(f), P(f), 4, 2, None, None) == lcd.LCD_EINVAL
+
+
+def test_rejection_accept_rejects_misuse_without_launching():
+    """Host-checkable misuse returns LCD_EINVAL before any launch (the fake
+    device pointers are never dereferenced)."""
+    L = lcd.load()
+    fake = 0x1000                      # 16-byte aligned, never touched
+    s = None
+    need = lcd.rejection_accept_workspace_bytes(3, 64)
+    assert need == 3 * 8 * (2 + 2 * 1)
+    assert lcd.rejection_accept_workspace_bytes(3, 1 << 20) == 3 * 8 * (2 + 2 * 1024)
+    assert lcd.rejection_accept_workspace_bytes(0, 64) == 0
+
+    def call(B=3, V=64, wg=0, ws_bytes=need, tp=fake, mp=None, ua=fake, hist=None, ro=None,
+             ln=None, cp=None, ws=fake, block=fake):
+        return L.rejection_accept(_P(block), _P(fake), None, _P(tp), _P(mp) if mp else None, V,
+                                  _P(ua), _P(fake), B, wg, _P(ws), ws_bytes, _P(fake), _P(fake),
+                                  _P(hist) if hist else None, _P(ro) if ro else None,
+                                  _P(ln) if ln else None, _P(cp) if cp else None, s)
+
+    assert call(V=62) == lcd.LCD_EINVAL                    # not a multiple of 4
+    assert call(V=0) == lcd.LCD_EINVAL
+    assert call(V=lcd.SAMPLE_MAX_VOCAB + 4) == lcd.LCD_EINVAL
+    assert call(B=-1) == lcd.LCD_EINVAL
+    assert call(wg=-1) == lcd.LCD_EINVAL
+    assert call(ws_bytes=need - 8) == lcd.LCD_EINVAL        # workspace too small
+    assert call(tp=fake + 4) == lcd.LCD_EINVAL              # target rows not 16-byte aligned
+    assert call(mp=fake + 8) == lcd.LCD_EINVAL
+    assert call(ws=fake + 4) == lcd.LCD_EINVAL
+    assert call(ua=0) == lcd.LCD_EINVAL
+    assert call(block=0) == lcd.LCD_EINVAL
+    assert call(hist=fake, ro=fake, ln=None, cp=fake) == lcd.LCD_EINVAL   # append needs len

@@ -69,19 +69,21 @@ def gpu_fuse_accept(draft, m, q, long_mode, target, params=None):
     blk = torch.empty((B, 15), dtype=torch.int32, device=dev)
     bl = torch.empty(B, dtype=torch.int32, device=dev)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
-    lcd.fuse_verify_block(t(draft), t(m), t(q), t(long_mode), blk, bl, p)
+    mask = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    lcd.fuse_verify_block(t(draft), t(m), t(q), t(long_mode), blk, bl, p, model_mask=mask)
     lcd.greedy_accept(blk, bl, t(target), acc)
     torch.cuda.synchronize()
-    return blk.cpu().numpy(), bl.cpu().numpy(), acc.cpu().numpy()
+    return blk.cpu().numpy(), bl.cpu().numpy(), acc.cpu().numpy(), mask.cpu().numpy().view(np.uint32)
 
 
 def assert_step_parity(w, d, m, long_mode, params=None):
     lcd = _lcd()
     p = params or lcd.default_params()
     q, tgt = w.step_inputs(np.zeros(w.B, np.int64), 0)
-    blk, bl, acc = gpu_fuse_accept(d, m, q, long_mode, tgt, p)
-    oblk, obl = oracle.fuse_verify_block(d, m, q, long_mode, _oparams(p))
+    blk, bl, acc, mask = gpu_fuse_accept(d, m, q, long_mode, tgt, p)
+    oblk, obl, omask = oracle.fuse_verify_block(d, m, q, long_mode, _oparams(p), with_mask=True)
     oacc = oracle.greedy_accept(oblk, obl, tgt)
+    np.testing.assert_array_equal(mask, omask)
     np.testing.assert_array_equal(blk, oblk)
     np.testing.assert_array_equal(bl, obl)
     np.testing.assert_array_equal(acc, oacc)
@@ -317,8 +319,9 @@ def test_fuse_accept_parity_random(gpu):
         q = rng.integers(0, 3, (B, 7)).astype(np.int32)
         lg = rng.integers(0, 2, B).astype(np.int32)
         tgt = rng.integers(0, 3, (B, 16)).astype(np.int32)
-        blk, bl, acc = gpu_fuse_accept(d, m, q, lg, tgt, p)
-        oblk, obl = oracle.fuse_verify_block(d, m, q, lg, _oparams(p))
+        blk, bl, acc, mask = gpu_fuse_accept(d, m, q, lg, tgt, p)
+        oblk, obl, omask = oracle.fuse_verify_block(d, m, q, lg, _oparams(p), with_mask=True)
+        np.testing.assert_array_equal(mask, omask)
         np.testing.assert_array_equal(blk, oblk)
         np.testing.assert_array_equal(bl, obl)
         np.testing.assert_array_equal(acc, oracle.greedy_accept(oblk, obl, tgt))

@@ -71,41 +71,53 @@ def _target_law(rows, drafts):
     return {k: v for k, v in law.items() if v != 0}
 
 
-def test_point_mass_verification_is_lossless_exactly():
-    """Two lookup slots plus the bonus row; every accept uniform and every draw
-    word on its grid; the emitted sequence's law equals the target's."""
-    rows = [[F(1, 8), F(1, 2), F(1, 4), F(1, 8)],     # draft 1: accept 1/2, residual mass 1/2
-            [F(1, 8), F(1, 8), F(3, 4), F(0)],        # draft 2: accept 3/4, residual mass 1/4
-            [F(3, 8), F(1, 8), F(1, 4), F(1, 4)]]     # bonus row
-    drafts = [1, 2]
+POINT_ROWS = [[F(1, 8), F(1, 2), F(1, 4), F(1, 8)],   # draft 1: accept 1/2, residual mass 1/2
+              [F(1, 8), F(1, 8), F(3, 4), F(0)],      # draft 2: accept 3/4, residual mass 1/4
+              [F(3, 8), F(1, 8), F(1, 4), F(1, 4)]]   # bonus row
+POINT_DRAFTS = [1, 2]
+
+
+def point_mass_grid_batch():
+    """Two lookup slots and the bonus row over V = 4, one request per grid
+    point (accept uniforms of both slots x draw word).  Returns the inputs and
+    each request's weight (the grid cell's mass)."""
     V = 4
     us, ws = _grid_u(3), _grid_words(4)
     combos = list(itertools.product(range(len(us)), range(len(us)), range(len(ws))))
     B = len(combos)
     blk, bl, tp, ua, usm = _mk(B, V)
-    blk[:, 0], blk[:, 1] = drafts
+    blk[:, 0], blk[:, 1] = POINT_DRAFTS
     bl[:] = 2
-    for i, row in enumerate(rows):
+    for i, row in enumerate(POINT_ROWS):
         tp[:, i, :] = np.array([float(x) for x in row], np.float32)
     for b, (i0, i1, k) in enumerate(combos):
         ua[b, 0], ua[b, 1], usm[b] = us[i0], us[i1], ws[k]
+    return (blk, bl, tp, ua, usm), [F(1, len(us) ** 2 * len(ws))] * B
+
+
+def test_point_mass_verification_is_lossless_exactly():
+    """Two lookup slots plus the bonus row; every accept uniform and every draw
+    word on its grid; the emitted sequence's law equals the target's."""
+    (blk, bl, tp, ua, usm), weights = point_mass_grid_batch()
+    B = len(bl)
     acc, em = oracle.rejection_accept(blk, bl, tp, ua, usm)
-    w = F(1, len(us) ** 2 * len(ws))
-    assert _law(acc, em, [w] * B) == _target_law(rows, drafts)
+    assert _law(acc, em, weights) == _target_law(POINT_ROWS, POINT_DRAFTS)
     # the accept counts' law: a = 0, 1, 2 with 1/2, 1/2 * 1/4, 1/2 * 3/4
     cnt = np.bincount(acc, minlength=3) / B
     assert cnt.tolist() == [0.5, 0.125, 0.375]
 
 
-def test_model_slot_verification_is_lossless_exactly():
-    """Slot 0 carries the draft model's own proposal x ~ q (so the
-    enumeration also runs over x with weight q(x)); slot 1 is a lookup slot.
-    The law of the emitted tokens is still the target's."""
+MODEL_Q0 = [F(1, 4), F(1, 2), F(1, 4), F(0)]          # powers of two: u*Q is exact
+MODEL_ROWS = [[F(1, 2), F(1, 4), F(1, 4), F(0)],      # residual max(p-q,0) = [1/4,0,0,0]
+              [F(1, 4), F(1, 4), F(1, 2), F(0)],      # lookup draft 2: accept 1/2
+              [F(1, 8), F(1, 8), F(1, 4), F(1, 2)]]
+
+
+def model_grid_batch():
+    """Slot 0 holds the draft model's token x (enumerated with weight q(x)),
+    slot 1 the lookup token 2, over V = 4; one request per grid point."""
     V = 4
-    q0 = [F(1, 4), F(1, 2), F(1, 4), F(0)]            # powers of two: u*Q is exact
-    rows = [[F(1, 2), F(1, 4), F(1, 4), F(0)],        # residual max(p-q,0) = [1/4,0,0,0]
-            [F(1, 4), F(1, 4), F(1, 2), F(0)],        # lookup draft 2: accept 1/2
-            [F(1, 8), F(1, 8), F(1, 4), F(1, 2)]]
+    q0, rows = MODEL_Q0, MODEL_ROWS
     us, ws = _grid_u(3), _grid_words(4)
     xs = [x for x in range(V) if q0[x] > 0]
     combos = list(itertools.product(xs, range(len(us)), range(len(us)), range(len(ws))))
@@ -123,6 +135,16 @@ def test_model_slot_verification_is_lossless_exactly():
         ua[b, 0], ua[b, 1], usm[b] = us[i0], us[i1], ws[k]
         weights.append(q0[x] / (len(us) ** 2 * len(ws)))
     mask = np.ones(B, np.uint32)
+    return (blk, bl, tp, ua, usm, mask, mp), weights
+
+
+def test_model_slot_verification_is_lossless_exactly():
+    """Slot 0 carries the draft model's own proposal x ~ q (so the
+    enumeration also runs over x with weight q(x)); slot 1 is a lookup slot.
+    The law of the emitted tokens is still the target's."""
+    (blk, bl, tp, ua, usm, mask, mp), weights = model_grid_batch()
+    q0, rows = MODEL_Q0, MODEL_ROWS
+    xs = [x for x in range(4) if q0[x] > 0]
     acc, em = oracle.rejection_accept(blk, bl, tp, ua, usm, model_mask=mask, model_probs=mp)
     law = _law(acc, em, weights)
     # the first emitted token is distributed as the target's row 0
@@ -189,14 +211,15 @@ def test_one_hot_target_rows_reduce_to_greedy_accept(with_model):
         assert em[r, :acc[r] + 1].tolist() == tgt[r, :acc[r] + 1].tolist()
 
 
-def test_draw_boundaries_match_big_integer_arithmetic():
-    """The bonus draw picks token j exactly for the words u with
-    ceil(C_{j-1} 2^64 / S) <= u < ceil(C_j 2^64 / S), where C_j is the running
-    total of the weights floor(p * 2^40) and S their sum (Python integers)."""
+def boundary_batch(V=37, pad_to=None):
+    """Bonus draws at both ends of every token's range of words (computed with
+    Python integers); the row may be padded with zero-probability entries."""
     rng = np.random.Generator(np.random.PCG64(11))
-    V = 37
     p = rng.dirichlet(np.full(V, 0.3)).astype(np.float32)
     p[5] = 0.0
+    if pad_to is not None:
+        p = np.concatenate([p, np.zeros(pad_to - V, np.float32)])
+        V = pad_to
     W = [int(np.floor(float(x) * 2 ** 40)) for x in p]   # float32 -> exact double
     C = np.cumsum([0] + W).tolist()
     S = C[-1]
@@ -212,6 +235,14 @@ def test_draw_boundaries_match_big_integer_arithmetic():
     blk, bl, tp, ua, usm = _mk(B, V)
     tp[:, 0, :] = p
     usm[:] = np.array(words, np.uint64)
+    return (blk, bl, tp, ua, usm), want
+
+
+def test_draw_boundaries_match_big_integer_arithmetic():
+    """The bonus draw picks token j exactly for the words u with
+    ceil(C_{j-1} 2^64 / S) <= u < ceil(C_j 2^64 / S), where C_j is the running
+    total of the weights floor(p * 2^40) and S their sum (Python integers)."""
+    (blk, bl, tp, ua, usm), want = boundary_batch()
     acc, em = oracle.rejection_accept(blk, bl, tp, ua, usm)
     assert (acc == 0).all()
     assert em[:, 0].tolist() == want
@@ -255,7 +286,8 @@ def test_draw_counts_on_evenly_spaced_words():
         assert np.abs(got - n * W / W.sum()).max() <= 1.0
 
 
-def test_edge_cases():
+def edge_batch():
+    """One request per edge case the definition names (V = 4)."""
     V = 4
     B = 9
     blk, bl, tp, ua, usm = _mk(B, V)
@@ -300,6 +332,12 @@ def test_edge_cases():
     mp[6, 0] = [0.5, 0.25, 0.25, 0.0]
     mask = np.zeros(B, np.uint32)
     mask[6] = 1
+    return blk, bl, tp, ua, usm, mask, mp
+
+
+def test_edge_cases():
+    blk, bl, tp, ua, usm, mask, mp = edge_batch()
+    B = len(bl)
     acc, em = oracle.rejection_accept(blk, bl, tp, ua, usm, model_mask=mask, model_probs=mp)
     assert acc[0] == 0 and em[0, 0] == 3
     assert acc[1] == 15 and em[1, :15].tolist() == [2] * 15 and em[1, 15] == 3
