@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 METRIC = "history tokens scanned/s (HBM GB/s, % peak) + lookups/s at B=64, 25k ctx"
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 320 << 20
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "lookup_scan_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
 def parse():
@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "sampled"])
     ap.add_argument("--cpu-work-seconds", type=float, default=20.0,
                     help="CPU work (seconds summed over threads) for the oracle baseline; 0 = skip")
     ap.add_argument("--scan-wgs", type=int, default=0, help="lookup launch tuning (0 = auto)")
@@ -87,15 +87,18 @@ KERNEL_SOURCES = ("context_lookup_drafting_amd/csrc/lcd_lookup.hip",
                   "context_lookup_drafting_amd/csrc/lcd_rules.h", "include/lcd.h")
 
 
-def kernel_source_hash():
-    """sha256[:16] over the sources the fused step kernel is compiled from."""
+SAMPLE_SOURCES = ("context_lookup_drafting_amd/csrc/lcd_sample.hip", "include/lcd.h")
+
+
+def kernel_source_hash(sources=KERNEL_SOURCES):
+    """sha256[:16] over the sources a kernel is compiled from."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         h.update(open(os.path.join(ROOT, rel), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name, launches_per_step=1):
+def load_traffic(workload_name, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source and this workload; otherwise None."""
     try:
@@ -103,7 +106,7 @@ def load_traffic(workload_name, launches_per_step=1):
     except (OSError, ValueError):
         return None
     ent = rec.get("workloads", {}).get(workload_name)
-    if not ent or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash(sources):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -198,6 +201,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.workload == "sampled":
+        bench_sampled(args)
         return
 
     import numpy as np
@@ -386,6 +392,221 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_work_seconds)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+SAMPLED_METRIC = ("vocabulary probabilities scanned/s (HBM GB/s, % peak) + verified requests/s, "
+                  "sampled verification at B=64, V=248,320")
+
+
+def sampled_draw_rows(sb, acc):
+    """Vocabulary rows each request's draw must read (1, or 2 for a draft-model
+    residual) and the slots its walk tested, from the accepted counts."""
+    import numpy as np
+    rows = np.ones(sb.B, np.int64)
+    tested = np.zeros(sb.B, np.int64)
+    for r in range(sb.B):
+        L = min(max(int(sb.block_len[r]), 0), 15)
+        a = int(acc[r])
+        if a < 0:
+            continue
+        tested[r] = min(a + 1, L)
+        if a < L and 0 <= sb.block[r, a] < sb.V and sb.model_probs is not None \
+                and a < 7 and (int(sb.model_mask[r]) >> a) & 1:
+            rows[r] = 2
+    return rows, tested
+
+
+def sampled_alg_bytes(sb, acc):
+    """Algorithmic bytes of one launch: the draw rows (4 bytes per entry), per
+    tested slot the target probability, the uniform and (draft-model slot) the
+    draft probability (16), and per request the block, its length, the mask, the
+    draw word and the outputs (60 + 4 + 4 + 8 + 4 + 64 = 144)."""
+    rows, tested = sampled_draw_rows(sb, acc)
+    return int(4 * sb.V * rows.sum() + 16 * tested.sum() + 144 * sb.B), int(rows.sum())
+
+
+def cpu_baseline_sampled(sb, work_seconds):
+    """The CPU oracle (as it is) over the same sampled batch, threads over
+    requests; bounded to about `work_seconds` of CPU time summed over threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    if not os.path.exists(os.path.join(ROOT, "oracle", "liblcd_oracle.so")):
+        oracle.build()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    chunks = [list(range(i, sb.B, cores)) for i in range(cores)]
+
+    def run_chunk(idx):
+        for r in idx:
+            s = slice(r, r + 1)
+            oracle.rejection_accept(sb.block[s], sb.block_len[s], sb.target_probs[s], sb.u_accept[s],
+                                    sb.u_sample[s], sb.model_mask[s],
+                                    None if sb.model_probs is None else sb.model_probs[s])
+        return len(idx)
+
+    acc, _ = oracle.rejection_accept(sb.block, sb.block_len, sb.target_probs, sb.u_accept,
+                                     sb.u_sample, sb.model_mask, sb.model_probs)
+    rows, _ = sampled_draw_rows(sb, acc)
+    probs = int(rows.sum()) * sb.V
+    batches = 0
+    cpu0 = time.process_time()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as pool:
+        while True:
+            list(pool.map(run_chunk, chunks))
+            batches += 1
+            if time.process_time() - cpu0 >= work_seconds or time.perf_counter() - t0 > 120:
+                break
+    wall = time.perf_counter() - t0
+    return {
+        "value": round(batches * probs / wall, 1),
+        "unit": "vocabulary probabilities/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{batches} full sampled-verification steps of the {sb.B}-request batch "
+                   f"({probs} probabilities scanned each), threads over requests, "
+                   f"{wall:.1f} s wall"),
+    }
+
+
+def bench_sampled(args):
+    """rejection_accept over the sampled batch (64 requests, 248,320-entry
+    vocabulary, draft-model rows given), replayed from a HIP graph over enough
+    device copies of the probability tensors that no launch finds its rows in
+    the Infinity Cache."""
+    import numpy as np
+    import torch
+
+    import context_lookup_drafting_amd as lcd
+    from context_lookup_drafting_amd import workloads as wl
+
+    lib = lcd.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sb = wl.sampled_batch()
+    B, V = sb.B, sb.V
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+    blk_d, bl_d = t(sb.block, np.int32), t(sb.block_len, np.int32)
+    mask_d = t(sb.model_mask.view(np.int32), np.int32)
+    ua_d, us_d = t(sb.u_accept, np.float64), t(sb.u_sample.view(np.int64), np.int64)
+    tp0, mp0 = t(sb.target_probs, np.float32), t(sb.model_probs, np.float32)
+    ws = lcd.alloc_rejection_workspace(B, V, dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    em = torch.empty((B, 16), dtype=torch.int32, device=dev)
+
+    def launch(tp, mp, timed=None):
+        if timed is None:
+            lcd.rejection_accept(blk_d, bl_d, tp, ua_d, us_d, ws, acc, em, model_mask=mask_d,
+                                 model_probs=mp, wg_units=args.scan_wgs)
+        else:
+            lcd.rejection_accept_timed(blk_d, bl_d, tp, ua_d, us_d, ws, acc, em, timed[0], timed[1],
+                                       model_mask=mask_d, model_probs=mp, wg_units=args.scan_wgs)
+
+    launch(tp0, mp0)
+    torch.cuda.synchronize()
+    acc_h = acc.cpu().numpy()
+    ref = (acc.clone(), em.clone())
+    alg_bytes, rows = sampled_alg_bytes(sb, acc_h)
+    read_bytes = 4 * V * rows
+    R = max(2, -(-ROTATE_BYTES // read_bytes))
+    sets = [(tp0, mp0)] + [(tp0.clone(), mp0.clone()) for _ in range(R - 1)]
+
+    if args.kernel_only:
+        for i in range(args.kernel_only):
+            launch(*sets[i % R])
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_only_launches": args.kernel_only, "workload": sb.name,
+                          "alg_bytes_per_launch": alg_bytes, "rotating_sets": R}), flush=True)
+        return
+
+    def capture(nsteps):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(nsteps):
+                    launch(*sets[i % R])
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    K, W = args.steps, args.warmup
+    g_full = capture(R)
+    g_tail = capture(K % R) if K % R else None
+    for _ in range(max(1, -(-W // R))):
+        g_full.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K // R):
+        g_full.replay()
+    if g_tail is not None:
+        g_tail.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if not (torch.equal(acc, ref[0]) and torch.equal(em, ref[1])):
+        print("bench.py: graph replay disagrees with the eager launch", file=sys.stderr)
+        sys.exit(3)
+
+    hev = HipEvents(lib)
+    n_k = min(K, 400)
+    evs = [(hev.create(), hev.create()) for _ in range(n_k)]
+    for i in range(n_k):
+        launch(*sets[i % R], timed=evs[i])
+    torch.cuda.synchronize()
+    durs = np.array([hev.elapsed_ms(a, b) for a, b in evs]) * 1e-3
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    k_avg = float(durs.mean())
+    achieved = alg_bytes / k_avg / 1e9
+    probs = rows * V
+    value = K * probs / elapsed
+    out = {
+        "metric": SAMPLED_METRIC,
+        "value": round(value, 1),
+        "unit": "vocabulary probabilities/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed / K * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": sb.name,
+            "batch": B,
+            "vocab": V,
+            "draw_rows_per_step": rows,
+            "model_rows": True,
+            "rotating_sets": R,
+            "rotating_bytes": R * (sb.target_probs.nbytes + sb.model_probs.nbytes),
+            "launch": f"HIP graph of {R} steps, rejection_accept (1 kernel) per step",
+        },
+        "requests_per_s": round(K * B / elapsed, 1),
+        "step_hbm_gbps": round(value * 4 / 1e9, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(sb.name, SAMPLE_SOURCES),
+            "kernel": "rejection_accept_kernel",
+            "kernel_us_mean": round(k_avg * 1e6, 3),
+            "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, x)) * 1e6, 3)
+                                      for x in (10, 50, 90)],
+            "alg_bytes_per_launch": alg_bytes,
+            "launches_timed": n_k,
+        },
+        "cpu_baseline": (cpu_baseline_sampled(sb, args.cpu_work_seconds)
+                         if args.cpu_work_seconds > 0 else None),
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -50,47 +50,69 @@ constexpr int kBufferWord3 = 0x00020000;    // gfx9 buffer descriptor, dword 3
 constexpr int kPlain = 0;                   // the target row p_a itself
 constexpr int kPointResidual = 1;           // p_a without the rejected token x
 constexpr int kModelResidual = 2;           // max(p_a - q_a, 0)
+constexpr int kKeep = 4;                    // unit sums a lane keeps in registers (U <= 256)
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Probabilities are read clamped into [0, 1]; NaN reads as 0.
-__device__ __forceinline__ float prob01(float x) { return x > 0.0f ? fminf(x, 1.0f) : 0.0f; }
+// Probabilities are read clamped into [0, 1], NaN as 0: one v_med3_f32
+// against 0 and 1, which on this part sends every NaN (quiet or signalling,
+// either sign), -inf and negative values (and -0) to +0, values above 1 and
+// +inf to 1, and keeps subnormals.
+__device__ __forceinline__ float prob01(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 1.0f); }
 
-// floor(w * 2^40) for w in [0, 1], from the float's fields: w = M * 2^(e-150)
-// with the 24-bit significand M, so w * 2^40 = M * 2^(e-110).
-__device__ __forceinline__ u64 fixed40(float w) {
-    const uint32_t b = __float_as_uint(w);
-    const int e = (int)(b >> 23);
-    const u64 M = (u64)((b & 0x7FFFFFu) | 0x800000u);
-    if (e >= 110) return M << (e - 110);
-    if (e <= 86) return 0;                  // below 2^-40 (and zero, subnormals)
-    return M >> (110 - e);
+// floor(c * 2^40) for c in [0, 1], as A * 2^24 + B with A = floor(c * 2^16)
+// and B = floor(fract(c * 2^16) * 2^24): c * 2^16 and the fraction times 2^24
+// are exact in fp32, and float-to-unsigned conversion truncates.
+__device__ __forceinline__ void split40(float c, uint32_t &a, uint32_t &b) {
+    const float y = c * 65536.0f;
+    a = (uint32_t)y;
+    b = (uint32_t)(__builtin_amdgcn_fractf(y) * 16777216.0f);
 }
 
-__device__ __forceinline__ float weight(int kind, float p, float q, int j, int x) {
-    const float pc = prob01(p);
-    if (kind == kModelResidual) {
-        const float d = pc - prob01(q);
-        return d > 0.0f ? d : 0.0f;
-    }
-    return (kind == kPointResidual && j == x) ? 0.0f : pc;
+__device__ __forceinline__ u64 fixed40(float c) {
+    uint32_t a, b;
+    split40(c, a, b);
+    return ((u64)a << 24) + b;
 }
 
-__device__ __forceinline__ u64 wave_sum(u64 v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+// max(p - q, 0) of two clamped probabilities (fp32 subtraction; the median on
+// the bits sends negative differences, and -0, to 0).
+__device__ __forceinline__ float residual01(float pc, float qc) {
+    int b = __float_as_int(pc - qc);
+    b = min(max(b, 0), 0x3F800000);
+    return __int_as_float(b);
+}
+
+// One DPP step on a 64-bit value: both halves move with the same lane pattern;
+// lanes without a source (and rows outside the row mask) read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ u64 dpp64(u64 v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kCtrl, kRowMask, 0xF, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), kCtrl, kRowMask, 0xF, true);
+    return ((u64)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the wave's lanes, on DPP: shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then row 0's and row 1's last lanes broadcast
+// into the rows above (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows
+// 2 and 3).  Exact for 64-bit integers.
+__device__ __forceinline__ u64 wave_scan(u64 v) {
+    v += dpp64<0x111, 0xF>(v);
+    v += dpp64<0x112, 0xF>(v);
+    v += dpp64<0x114, 0xF>(v);
+    v += dpp64<0x118, 0xF>(v);
+    v += dpp64<0x142, 0xA>(v);
+    v += dpp64<0x143, 0xC>(v);
     return v;
 }
 
-// Inclusive prefix sum over the wave's lanes.
-__device__ __forceinline__ u64 wave_scan(u64 v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const u64 o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    return v;
+__device__ __forceinline__ u64 lane_value(u64 v, int l) {
+    return ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
 }
+
+// Sum over the wave's lanes, in every lane.
+__device__ __forceinline__ u64 wave_sum(u64 v) { return lane_value(wave_scan(v), 63); }
 
 struct SampleArgs {
     int32_t V;                   // vocabulary size, a multiple of 4
@@ -117,7 +139,7 @@ struct SampleIO {
 
 // The walk over the verify block, identical in every wave of every workgroup
 // of the request: lane k < 15 tests slot k.  Returns a; sets the draw's kind,
-// the rejected token and the lane-k block token.
+// the rejected token, its clamped target probability and the lane-k token.
 __device__ __forceinline__ int walk_block(int r, int lane, const SampleArgs &sa, const SampleIO &io,
                                           int &kind, int &x_rej, int &xk, float &p_rej) {
     int L = io.block_len[r];
@@ -126,21 +148,55 @@ __device__ __forceinline__ int walk_block(int r, int lane, const SampleArgs &sa,
     const uint32_t mm = (io.model_mask != nullptr && io.model_probs != nullptr) ? io.model_mask[r] : 0u;
     const bool valid = lane < L && xk >= 0 && xk < sa.V;
     const bool use_model = valid && lane < LCD_Q_STRIDE && ((mm >> lane) & 1u);
+    const double u = lane < LCD_DRAFT_STRIDE ? io.u_accept[(int64_t)r * LCD_DRAFT_STRIDE + lane] : 0.0;
     float P = 0.0f, Q = 1.0f;
-    double u = 0.0;
-    if (valid) {
-        P = prob01(io.target_probs[((int64_t)r * LCD_TARGET_STRIDE + lane) * sa.V + xk]);
-        u = io.u_accept[(int64_t)r * LCD_DRAFT_STRIDE + lane];
-    }
+    if (valid) P = prob01(io.target_probs[((int64_t)r * LCD_TARGET_STRIDE + lane) * sa.V + xk]);
     if (use_model) Q = prob01(io.model_probs[((int64_t)r * LCD_Q_STRIDE + lane) * sa.V + xk]);
     const bool ok = valid && (u * (double)Q < (double)P);
     const u64 stop = __ballot(lane < L && !ok);
     const int a = stop ? (int)__builtin_ctzll(stop) : L;
     const bool rejected = a < L && ((__ballot(valid) >> a) & 1ull);
     kind = !rejected ? kPlain : (((__ballot(use_model) >> a) & 1ull) ? kModelResidual : kPointResidual);
-    x_rej = __shfl(xk, a < 63 ? a : 63);
-    p_rej = __shfl(P, a < 63 ? a : 63);
+    const int al = a < 63 ? a : 63;
+    x_rej = __builtin_amdgcn_readlane(xk, al);
+    p_rej = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P), al));
     return a;
+}
+
+// Weight sum of unit u of the row for one wave (every lane gets it).  The
+// point-mass residual is summed as the plain row, and the caller takes out the
+// rejected token's weight from the unit that holds it.
+__device__ __forceinline__ u64 unit_sum(__amdgpu_buffer_rsrc_t prs, __amdgpu_buffer_rsrc_t qrs,
+                                        int u, int lane, bool model) {
+    float4 pv[4], qv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        pv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               prs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, 0));
+    if (model) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            qv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   qrs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, 0));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    uint32_t sa = 0, sb = 0;               // <= 16 * 2^16 and < 16 * 2^24
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float f[4] = {pv[k].x, pv[k].y, pv[k].z, pv[k].w};
+        const float g[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float c = model ? residual01(prob01(f[i]), prob01(g[i])) : prob01(f[i]);
+            uint32_t a, b;
+            split40(c, a, b);
+            sa += a;
+            sb += b;
+        }
+    }
+    return wave_sum(((u64)sa << 24) + sb);
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -150,7 +206,7 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uni(tid >> 6);
-    const int words = 2 + 2 * sa.U;         // counter, pad, U draw sums, U plain sums
+    const int words = 2 + sa.U;             // counter, pad, U unit sums
     u64 *__restrict__ req = ws + (int64_t)r * words;
     u64 *__restrict__ sums = req + 2;
 
@@ -158,18 +214,25 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     if (tid == 0)
         ticket = __hip_atomic_fetch_add(req, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+    // the request's draw word, needed only by the last workgroup: loaded now so
+    // that its round trip overlaps the walk and the stream
+    const u64 u_draw = io.u_sample[r];
+
     int kind, x_rej, xk;
     float p_rej;
     const int a = walk_block(r, lane, sa, io, kind, x_rej, xk, p_rej);
     kind = uni(kind);
     x_rej = uni(x_rej);
+    const bool model = kind == kModelResidual;
+    // the rejected token's weight, taken out of its unit for a point-mass residual
+    const u64 w_rej = kind == kPointResidual ? fixed40(p_rej) : 0;
+    const int u_rej = kind == kPointResidual ? (x_rej >> 10) : -1;
 
     // The row the draw reads: target row a, and the draft model's row a for a
     // draft-model residual.  Both rows are 16-byte aligned (V % 4 == 0) and
     // the descriptors cover exactly V floats, so loads past the row read 0.
     const float *prow = io.target_probs + ((int64_t)r * LCD_TARGET_STRIDE + a) * sa.V;
-    const float *qrow = kind == kModelResidual
-                            ? io.model_probs + ((int64_t)r * LCD_Q_STRIDE + a) * sa.V : prow;
+    const float *qrow = model ? io.model_probs + ((int64_t)r * LCD_Q_STRIDE + a) * sa.V : prow;
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(prow), 0, sa.V * 4, kBufferWord3);
     const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -179,40 +242,10 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     const int u0 = c * sa.upw;
     const int u1 = min(u0 + sa.upw, sa.U);
     for (int u = u0 + wave; u < u1; u += kWaves) {
-        float4 pv[4], qv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            pv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   prs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, 0));
-        if (kind == kModelResidual) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                qv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                       qrs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, 0));
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        u64 s = 0, sp = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int j = u * kUnit + 4 * (lane + 64 * k);
-            s += fixed40(weight(kind, pv[k].x, qv[k].x, j + 0, x_rej));
-            s += fixed40(weight(kind, pv[k].y, qv[k].y, j + 1, x_rej));
-            s += fixed40(weight(kind, pv[k].z, qv[k].z, j + 2, x_rej));
-            s += fixed40(weight(kind, pv[k].w, qv[k].w, j + 3, x_rej));
-            if (kind == kModelResidual)
-                sp += fixed40(prob01(pv[k].x)) + fixed40(prob01(pv[k].y)) +
-                      fixed40(prob01(pv[k].z)) + fixed40(prob01(pv[k].w));
-        }
-        s = wave_sum(s);
-        if (kind == kModelResidual) sp = wave_sum(sp);
-        if (lane == 0) {
+        u64 s = unit_sum(prs, qrs, u, lane, model);
+        if (u == u_rej) s -= w_rej;
+        if (lane == 0)
             __hip_atomic_store(sums + u, kSumValid | s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (kind == kModelResidual)
-                __hip_atomic_store(sums + sa.U + u, kSumValid | sp, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
 
     // ---- only the last workgroup of the request to start goes on ------------
@@ -223,85 +256,117 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
 
     // Every other workgroup of the request has started and publishes without
     // waiting for anything, so this gathering ends (bounded all the same).
-    // Lane l owns units [l*n, l*n + n).
+    // Lane l owns units [l*n, l*n + n); up to kKeep of them stay in registers.
     const int n = (sa.U + 63) / 64;
     const int ua = min(lane * n, sa.U), ub = min(ua + n, sa.U);
-    const int nsets = kind == kModelResidual ? 2 : 1;
-    u64 lsum[2] = {0, 0};
+    u64 kept[kKeep];
+    u64 lsum = 0;
     bool all = false;
     for (int tries = 0; tries < kPollMax && !all; ++tries) {
         bool ok = true;
-        for (int set = 0; set < nsets; ++set) {
-            u64 acc = 0;
-            for (int u = ua; u < ub; ++u) {
-                const u64 v = __hip_atomic_load(sums + set * sa.U + u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-                ok = ok && (v != 0);
-                acc += v & ~kSumValid;
+        lsum = 0;
+        if (n <= kKeep) {
+            // all of a lane's loads in flight at once
+#pragma unroll
+            for (int k = 0; k < kKeep; ++k)
+                kept[k] = ua + k < ub ? __hip_atomic_load(sums + ua + k, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT)
+                                      : kSumValid;
+#pragma unroll
+            for (int k = 0; k < kKeep; ++k) {
+                ok = ok && (kept[k] != 0);
+                kept[k] &= ~kSumValid;
+                lsum += kept[k];
             }
-            lsum[set] = acc;
+        } else {
+            for (int u = ua; u < ub; ++u) {
+                const u64 v = __hip_atomic_load(sums + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && (v != 0);
+                lsum += v & ~kSumValid;
+            }
         }
         all = __ballot(!ok) == 0;
     }
+    u64 incl = wave_scan(lsum);
+    u64 S = lane_value(incl, 63);
 
-    // Total of the draw's weights; a draft-model residual with no mass falls
-    // back to the target row (its plain sums were published alongside), a
-    // point-mass residual with no mass means every weight of p_a sits on the
-    // rejected token.
-    int set = 0;
+    // Draws with no weight.  A draft-model residual with none falls back to the
+    // target row: recompute the row's plain unit sums here (rare: it needs
+    // p <= q everywhere and a rejection), overwriting the published ones.  A
+    // point-mass residual with none means every weight of p_a is the rejected
+    // token's.
     int draw_kind = kind;
-    u64 incl = wave_scan(lsum[0], lane);
-    u64 S = __shfl(incl, 63);
     int z = -1;
-    bool search = true;
-    if (S == 0 && kind == kModelResidual) {
-        set = 1;
+    bool search = all;
+    if (all && S == 0 && kind == kModelResidual) {
         draw_kind = kPlain;
-        incl = wave_scan(lsum[1], lane);
-        S = __shfl(incl, 63);
-    } else if (S == 0 && kind == kPointResidual) {
-        z = fixed40(p_rej) != 0 ? x_rej : -1;
+        lsum = 0;
+#pragma unroll
+        for (int k = 0; k < kKeep; ++k) kept[k] = 0;
+        for (int u = 0; u < sa.U; ++u) {
+            const u64 s = unit_sum(prs, qrs, u, lane, false);
+            if (lane == 0)
+                __hip_atomic_store(sums + u, kSumValid | s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (u >= ua && u < ub) {
+                lsum += s;
+#pragma unroll
+                for (int k = 0; k < kKeep; ++k)
+                    if (u - ua == k) kept[k] = s;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+        incl = wave_scan(lsum);
+        S = lane_value(incl, 63);
+    } else if (all && S == 0 && kind == kPointResidual) {
+        z = w_rej != 0 ? x_rej : -1;
         search = false;
     }
     if (S == 0) search = false;
 
-    if (search && all) {
-        const u64 t = __umul64hi(io.u_sample[r], S);
+    if (search) {
+        const u64 t = __umul64hi(u_draw, S);
         // lane range holding t, then the unit, then the lane's 16 floats
-        const u64 lane_at = __ballot(incl > t);
-        const int l0 = (int)__builtin_ctzll(lane_at);
-        const u64 before_l = __shfl(incl - lsum[set], l0);
+        const int l0 = (int)__builtin_ctzll(__ballot(incl > t));
+        const u64 before_l = lane_value(incl - lsum, l0);
         const int ub0 = min(l0 * n, sa.U);
-        const int uu = ub0 + lane;
         u64 us = 0;
-        if (lane < n && uu < sa.U)
-            us = __hip_atomic_load(sums + set * sa.U + uu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+        if (n <= kKeep) {
+#pragma unroll
+            for (int k = 0; k < kKeep; ++k) {
+                const u64 v = lane_value(kept[k], l0);
+                if (lane == k) us = v;
+            }
+        } else if (lane < n && ub0 + lane < sa.U) {
+            us = __hip_atomic_load(sums + ub0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
                  ~kSumValid;
-        const u64 uincl = wave_scan(us, lane) + before_l;
+        }
+        if (lane >= n || ub0 + lane >= sa.U) us = 0;
+        const u64 uincl = wave_scan(us) + before_l;
         const int lu = (int)__builtin_ctzll(__ballot(uincl > t));
         const int unit = ub0 + lu;
-        const u64 before_u = __shfl(uincl - us, lu);
+        const u64 before_u = lane_value(uincl - us, lu);
         // lane k holds floats [16k, 16k+16) of the unit
-        float f[16], g[16];
         const int base = unit * kUnit + 16 * lane;
+        const bool dm = draw_kind == kModelResidual;
+        u64 w[16], ls = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float4 pv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
                                                           prs, (base + 4 * k) * 4, 0, 0));
-            const float4 qv = draw_kind == kModelResidual
-                                  ? __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+            const float4 qv = dm ? __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
                                                                    qrs, (base + 4 * k) * 4, 0, 0))
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-            f[4 * k + 0] = pv.x; f[4 * k + 1] = pv.y; f[4 * k + 2] = pv.z; f[4 * k + 3] = pv.w;
-            g[4 * k + 0] = qv.x; g[4 * k + 1] = qv.y; g[4 * k + 2] = qv.z; g[4 * k + 3] = qv.w;
-        }
-        u64 w[16], ls = 0;
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float f[4] = {pv.x, pv.y, pv.z, pv.w};
+            const float g[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            w[i] = fixed40(weight(draw_kind, f[i], g[i], base + i, x_rej));
-            ls += w[i];
+            for (int i = 0; i < 4; ++i) {
+                const float cw = dm ? residual01(prob01(f[i]), prob01(g[i])) : prob01(f[i]);
+                const u64 wi = (draw_kind == kPointResidual && base + 4 * k + i == x_rej) ? 0 : fixed40(cw);
+                w[4 * k + i] = wi;
+                ls += wi;
+            }
         }
-        const u64 lincl = wave_scan(ls, lane) + before_u;
+        const u64 lincl = wave_scan(ls) + before_u;
         const int lz = (int)__builtin_ctzll(__ballot(lincl > t));
         u64 run = lincl - ls;
         int jz = -1;
@@ -310,12 +375,12 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
             run += w[i];
             if (jz < 0 && run > t) jz = base + i;
         }
-        z = __shfl(jz, lz);
+        z = __builtin_amdgcn_readlane(jz, lz);
     }
     if (!all) z = -1;                       // gathering gave up: the request emits nothing
 
     // re-zero the request's workspace for the next call
-    for (int u = lane; u < 2 * sa.U; u += 64)
+    for (int u = lane; u < sa.U; u += 64)
         __hip_atomic_store(sums + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -397,7 +462,7 @@ int sample_entry(const int32_t *block, const int32_t *block_len, const uint32_t 
 extern "C" size_t rejection_accept_workspace_bytes(int32_t B, int32_t V) {
     if (B <= 0 || V <= 0) return 0;
     const int64_t U = (V + lcd::kUnit - 1) / lcd::kUnit;
-    return (size_t)B * (size_t)(2 + 2 * U) * sizeof(unsigned long long);
+    return (size_t)B * (size_t)(2 + U) * sizeof(unsigned long long);
 }
 
 extern "C" int rejection_accept(const int32_t *block, const int32_t *block_len,

@@ -292,7 +292,7 @@ int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, 
 
 /*
  * rejection_accept_workspace_bytes -- bytes of the rejection_accept workspace
- * for B requests over a vocabulary of V: B * 8 * (2 + 2 * ceil(V / 1024)).
+ * for B requests over a vocabulary of V: B * 8 * (2 + ceil(V / 1024)).
  * 0 when B <= 0 or V <= 0.
  */
 size_t rejection_accept_workspace_bytes(int32_t B, int32_t V);

@@ -169,8 +169,8 @@ def test_rejection_accept_rejects_misuse_without_launching():
     fake = 0x1000                      # 16-byte aligned, never touched
     s = None
     need = lcd.rejection_accept_workspace_bytes(3, 64)
-    assert need == 3 * 8 * (2 + 2 * 1)
-    assert lcd.rejection_accept_workspace_bytes(3, 1 << 20) == 3 * 8 * (2 + 2 * 1024)
+    assert need == 3 * 8 * (2 + 1)
+    assert lcd.rejection_accept_workspace_bytes(3, 1 << 20) == 3 * 8 * (2 + 1024)
     assert lcd.rejection_accept_workspace_bytes(0, 64) == 0
 
     def call(B=3, V=64, wg=0, ws_bytes=need, tp=fake, mp=None, ua=fake, hist=None, ro=None,
