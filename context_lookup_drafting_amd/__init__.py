@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
   greedy_accept(block, block_len, target, accept, hist=None, row_off=None, lens=None, cap=None)
   rejection_accept(block, block_len, target_probs, u_accept, u_sample, workspace, accept, emitted,
                    model_mask=None, model_probs=None, hist=None, row_off=None, lens=None, cap=None)
+  LookupIndex(cap, device, params).build(hist, row_off, lens, max_len)
+  LookupIndex.propose(hist, row_off, lens, match_len, match_end, draft)
+                                          (lookup_index_plan / _build / _propose)
   lookup_schedule_step(state, match_len, accept, block_len, long_next, params)
 """
 
@@ -88,13 +91,18 @@ def load():
         L.lookup_telemetry_reduce.argtypes = [P, P, i32, i32, P, P]
         L.rejection_accept_workspace_bytes.argtypes = [i32, i32]
         L.rejection_accept_workspace_bytes.restype = ctypes.c_size_t
+        L.lookup_index_plan.argtypes = [P, i32, pp, P, P]
+        L.lookup_index_plan.restype = ctypes.c_int64
+        L.lookup_index_build.argtypes = [P, P, P, i32, pp, i32, P, P, P, ctypes.c_size_t, P, P, i32, P]
+        L.lookup_index_propose.argtypes = [P, P, P, i32, pp, i32, P, P, P, P, P, P, P, P]
         rej = [P, P, P, P, P, i32, P, P, i32, i32, P, ctypes.c_size_t, P, P, P, P, P, P, P]
         L.rejection_accept.argtypes = rej
         L.rejection_accept_timed.argtypes = rej + [P, P]
         for f in (L.lookup_propose, L.lookup_propose_timed, L.fuse_verify_block,
                   L.greedy_accept, L.lookup_schedule_step, L.lookup_decode_step,
                   L.lookup_decode_step_timed, L.lookup_telemetry_update,
-                  L.lookup_telemetry_reduce, L.rejection_accept, L.rejection_accept_timed):
+                  L.lookup_telemetry_reduce, L.rejection_accept, L.rejection_accept_timed,
+                  L.lookup_index_build, L.lookup_index_propose):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -439,3 +447,60 @@ def rejection_accept_timed(block, block_len, target_probs, u_accept, u_sample, w
                            emitted, model_mask, model_probs, None, None, None, None, wg_units)
     _check("rejection_accept_timed", load().rejection_accept_timed(
         *args, ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
+
+
+class LookupIndex:
+    """Device n-gram index of a batch (include/lcd.h, lookup_index_*): the
+    lookup of lookup_propose without scanning the histories.  ``cap`` are the
+    rows' capacities (the longest each history may grow to)."""
+
+    def __init__(self, cap, device, params: Params | None = None, fp_bits: int = 0):
+        import numpy as np
+        import torch
+        self.p = params or default_params()
+        self.fp_bits = int(fp_bits)
+        cap = np.ascontiguousarray(cap, dtype=np.int32)
+        self.B = len(cap)
+        off = np.zeros(max(self.B, 1), np.int64)
+        bits = np.zeros(max(self.B, 1), np.int32)
+        nbytes = int(load().lookup_index_plan(cap.ctypes.data_as(ctypes.c_void_p), self.B,
+                                                ctypes.byref(self.p),
+                                                off.ctypes.data_as(ctypes.c_void_p),
+                                                bits.ctypes.data_as(ctypes.c_void_p)))
+        if nbytes < 0:
+            raise LCDError("lookup_index_plan", nbytes)
+        self.device = torch.device(device)
+        self.table_bytes = max(nbytes, 8)
+        self.tables = torch.empty(self.table_bytes // 8, dtype=torch.int64, device=self.device)
+        self.table_off = torch.from_numpy(off[:self.B].copy()).to(self.device)
+        self.table_bits = torch.from_numpy(bits[:self.B].copy()).to(self.device)
+        self.indexed_len = torch.zeros(self.B, dtype=torch.int32, device=self.device)
+        self._scratch = torch.zeros(max(self.B, 1), dtype=torch.int32, device=self.device)
+
+    def build(self, hist, row_off, lens, max_len: int):
+        import torch
+        B, dev = self.B, self.device
+        _check("lookup_index_build", load().lookup_index_build(
+            _dev(hist, "hist", torch.int32, device=dev),
+            _dev(row_off, "row_off", torch.int64, B, dev),
+            _dev(lens, "lens", torch.int32, B, dev), ctypes.c_int32(B), ctypes.byref(self.p),
+            ctypes.c_int32(self.fp_bits), _dev(self.table_off, "table_off", torch.int64, B, dev),
+            _dev(self.table_bits, "table_bits", torch.int32, B, dev),
+            ctypes.c_void_p(self.tables.data_ptr()), ctypes.c_size_t(self.table_bytes),
+            _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
+            ctypes.c_void_p(self._scratch.data_ptr()), ctypes.c_int32(int(max_len)), _stream(dev)))
+
+    def propose(self, hist, row_off, lens, match_len, match_end, draft):
+        import torch
+        B, dev = self.B, self.device
+        _check("lookup_index_propose", load().lookup_index_propose(
+            _dev(hist, "hist", torch.int32, device=dev),
+            _dev(row_off, "row_off", torch.int64, B, dev),
+            _dev(lens, "lens", torch.int32, B, dev), ctypes.c_int32(B), ctypes.byref(self.p),
+            ctypes.c_int32(self.fp_bits), _dev(self.table_off, "table_off", torch.int64, B, dev),
+            _dev(self.table_bits, "table_bits", torch.int32, B, dev),
+            ctypes.c_void_p(self.tables.data_ptr()),
+            _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
+            _dev(match_len, "match_len", torch.int32, B, dev),
+            _dev(match_end, "match_end", torch.int32, B, dev),
+            _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev), _stream(dev)))

@@ -1,0 +1,397 @@
+// lcd_index.hip -- the lookup answered from an incrementally maintained n-gram
+// index instead of a scan of the whole history, for MI355X / gfx950.
+//
+// Method: HyperQwen lookup-drafting article, section "第 1 步" (longest current
+// suffix of 4..12 tokens, latest earlier occurrence, LZ-style draft); the
+// forum thread's reply on the method's pitfalls (the lookup index has to be
+// maintained incrementally: a full scan of a long context at every step costs
+// more and more).  The answer is the same as the scan's, bit for bit.
+//
+// The index of request r is one open-addressed hash table of 8-byte entries
+// keyed by (L, the L tokens ending at position p) for every L in
+// [l_min, l_max]; the entry holds the largest such p.  A position is inserted
+// only once the token after it exists (p <= n-2 for a history of n tokens), so
+// the latest earlier occurrence of the current suffix's L-gram is the entry's
+// position itself, and "longest, then latest" is: the largest L whose suffix
+// L-gram has an entry.  Every hit is checked against the history's tokens; an
+// entry shared by two different L-grams with the same fingerprint (a
+// fingerprint collision, about 2^-31 per probe) can hide the answer, so such a
+// request is answered by an exact scan of its history instead.
+//
+// Entry layout: fingerprint (high 32 bits, never 0) | position + 1 (low 32);
+// 0 = empty.  Inserting is a compare-and-swap into an empty slot, or a 64-bit
+// atomic max into the slot holding the same fingerprint (same high word, so
+// the max is the larger position); linear probing past other fingerprints.
+// Tables hold at most 1/4 of their slots (the plan sizes them from the
+// capacity of each row).
+//
+// lookup_index_propose: one wave per request.  It first inserts the positions
+// appended since the last call (lanes over positions, all lengths of a
+// position issued back to back), then queries all lengths at once (lane k
+// takes L = l_min + k), verifies, and copies the draft.  About six dependent
+// memory round trips per step, whatever the history length.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lcd.h"
+
+namespace lcd {
+namespace {
+
+using u64 = unsigned long long;
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBuildThreads = 256;
+constexpr int kMaxL = LCD_MAX_SUFFIX;            // 16
+constexpr int kMaxProbe = 1 << 20;               // bound on a probe sequence
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Rolling hash of the tokens t_p, t_{p-1}, ... (read backwards from the end
+// position), then a SplitMix64-style finaliser keyed by the length.
+__device__ __forceinline__ u64 roll(u64 h, int32_t t) {
+    h = (h ^ (uint32_t)t) * 0x9E3779B97F4A7C15ull;
+    return h ^ (h >> 32);
+}
+
+__device__ __forceinline__ u64 finish_key(u64 h, int L) {
+    u64 z = h + (u64)L * 0xD6E8FEB86659FD93ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+constexpr u64 kHashSeed = 0x243F6A8885A308D3ull;
+
+struct IndexArgs {
+    int32_t l_min, l_max, k_max;
+    uint32_t fp_mask;        // fingerprint bits
+};
+
+__device__ __forceinline__ uint32_t fingerprint(u64 key, uint32_t mask) {
+    return 1u + ((uint32_t)(key >> 33) & mask);
+}
+
+__device__ __forceinline__ u64 entry_of(u64 key, uint32_t mask, int32_t p) {
+    return ((u64)fingerprint(key, mask) << 32) | (uint32_t)(p + 1);
+}
+
+// Inserts entry `ent` (key's fingerprint | p + 1) into table T of 2^bits slots,
+// probing from slot i; returns false only if the probe bound was hit (never at
+// the planned load).
+__device__ bool insert_from(u64 *__restrict__ T, int bits, u64 ent, u64 i) {
+    const u64 cmask = ((u64)1 << bits) - 1;
+    const u64 fp = ent >> 32;
+    for (int probes = 0; probes < kMaxProbe; ++probes) {
+        const u64 old = atomicCAS(T + i, 0ull, ent);
+        if (old == 0) return true;
+        if ((old >> 32) == fp) {
+            atomicMax(T + i, ent);
+            return true;
+        }
+        i = (i + 1) & cmask;
+    }
+    return false;
+}
+
+__device__ __forceinline__ bool insert_one(u64 *__restrict__ T, int bits, u64 key, uint32_t mask,
+                                           int32_t p) {
+    return insert_from(T, bits, entry_of(key, mask, p), key & (((u64)1 << bits) - 1));
+}
+
+// Exact lookup by scanning the whole history (the slow path): one wave, one
+// candidate end per lane per step, the longest match (capped at l_max) and the
+// latest end among equals.  Returns the packed key (L << 31 | e), 0 = none.
+__device__ u64 exact_scan(const int32_t *__restrict__ h, int n, const IndexArgs &a, int lane) {
+    // suffix token s_j = h[n-1-j] for j < l_max, read by every lane
+    u64 best = 0;
+    for (int e0 = 0; e0 <= n - 2; e0 += 64) {
+        const int e = e0 + lane;
+        int L = 0;
+        if (e <= n - 2) {
+            while (L < a.l_max && L <= e && h[e - L] == h[n - 1 - L]) ++L;
+        }
+        if (L >= a.l_min) {
+            const u64 k = ((u64)L << 31) | (uint32_t)e;
+            best = k > best ? k : best;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const u64 o = __shfl_xor(best, off);
+        best = o > best ? o : best;
+    }
+    return best;
+}
+
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+index_propose_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
+                     const int32_t *__restrict__ len, int32_t B, IndexArgs a,
+                     const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_bits,
+                     u64 *__restrict__ tables, int32_t *__restrict__ indexed_len,
+                     int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
+                     int32_t *__restrict__ draft) {
+    const int lane = threadIdx.x & 63;
+    const int r = uni(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    if (r >= B) return;
+    const int32_t n0 = len[r];
+    const int n = n0 > 0 ? n0 : 0;
+    const int64_t ro = row_off[r];
+    const int il = indexed_len[r];
+    const int bits = table_bits[r];
+    u64 *__restrict__ T = tables + table_off[r];
+    const int32_t *__restrict__ h = hist + ro;
+    const int nL = a.l_max - a.l_min + 1;
+
+    bool exact = il < 0 || il > n;           // stale index: answered by a scan from now on
+    bool overfull = false;
+    // ---- insert the positions appended since the last call ----------------
+    if (!exact) {
+        const int p_lo = il > 0 ? il - 1 : 0;
+        const int p_hi = n - 2;               // positions p <= n-2 are indexed
+        bool ok = true;
+        for (int p0 = p_lo; p0 <= p_hi; p0 += 64) {
+            const int p = p0 + lane;
+            if (p <= p_hi) {
+                int32_t t[kMaxL];
+#pragma unroll
+                for (int j = 0; j < kMaxL; ++j)
+                    t[j] = (j < a.l_max && p - j >= 0) ? h[p - j] : 0;
+                // every length's first compare-and-swap in flight at once
+                const u64 cmask = ((u64)1 << bits) - 1;
+                u64 ent[kMaxL], slot[kMaxL], old[kMaxL];
+                u64 hs = kHashSeed;
+#pragma unroll
+                for (int j = 0; j < kMaxL; ++j) {
+                    hs = roll(hs, t[j]);
+                    const int L = j + 1;
+                    const u64 k = finish_key(hs, L);
+                    ent[j] = entry_of(k, a.fp_mask, p);
+                    slot[j] = k & cmask;
+                    old[j] = (L >= a.l_min && L <= a.l_max && p - j >= 0)
+                                 ? atomicCAS(T + slot[j], 0ull, ent[j]) : 0ull;
+                }
+#pragma unroll
+                for (int j = 0; j < kMaxL; ++j) {
+                    if (old[j] == 0) continue;                      // inserted (or no such length)
+                    if ((old[j] >> 32) == (ent[j] >> 32)) atomicMax(T + slot[j], ent[j]);
+                    else ok = insert_from(T, bits, ent[j], (slot[j] + 1) & cmask) && ok;
+                }
+            }
+        }
+        if (__ballot(!ok) != 0) exact = overfull = true;
+        // this wave's inserts are complete and visible before it queries
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
+    }
+
+    // ---- query: lane k takes length L = l_min + k ------------------------
+    u64 key = 0;
+    if (!exact) {
+        const int L = a.l_min + lane;
+        int e = -1;
+        bool collide = false;
+        if (lane < nL && L <= n - 1) {        // the suffix and an earlier occurrence both fit
+            int32_t s[kMaxL];
+#pragma unroll
+            for (int j = 0; j < kMaxL; ++j) s[j] = (j < L) ? h[n - 1 - j] : 0;
+            u64 hs = kHashSeed;
+#pragma unroll
+            for (int j = 0; j < kMaxL; ++j)
+                if (j < L) hs = roll(hs, s[j]);
+            const u64 k = finish_key(hs, L);
+            const u64 cmask = ((u64)1 << bits) - 1;
+            const uint32_t fp = fingerprint(k, a.fp_mask);
+            u64 i = k & cmask;
+            for (int probes = 0; probes < kMaxProbe; ++probes) {
+                const u64 v = __hip_atomic_load(T + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v == 0) break;                                   // no occurrence
+                if ((uint32_t)(v >> 32) == fp) {
+                    const int pe = (int)(uint32_t)v - 1;
+                    bool same = pe >= L - 1 && pe <= n - 2;
+#pragma unroll
+                    for (int j = 0; j < kMaxL; ++j)
+                        if (j < L && same) same = h[pe - j] == s[j];
+                    if (same) e = pe; else collide = true;
+                    break;
+                }
+                i = (i + 1) & cmask;
+            }
+        }
+        // the longest verified length wins unless a longer one is in doubt
+        const u64 hit = __ballot(e >= 0);
+        const u64 doubt = __ballot(collide);
+        if (hit != 0) {
+            const int kb = 63 - __builtin_clzll(hit);
+            if ((doubt >> (kb + 1)) != 0) exact = true;      // a longer length is in doubt
+            if (!exact) {
+                const int eb = __builtin_amdgcn_readlane(e, kb);
+                key = ((u64)(a.l_min + kb) << 31) | (uint32_t)eb;
+            }
+        } else if (doubt != 0) {
+            exact = true;
+        }
+    }
+    if (exact) {
+        key = exact_scan(h, n, a, lane);
+        if (lane == 0 && (il > n || overfull)) indexed_len[r] = -1;
+    } else if (lane == 0) {
+        indexed_len[r] = n;
+    }
+
+    // ---- match and LZ draft ------------------------------------------------
+    const int m = (int)(key >> 31);
+    const int e = key != 0 ? (int)(key & 0x7FFFFFFFull) : -1;
+    if (lane < LCD_DRAFT_STRIDE) {
+        int d = LCD_PAD;
+        if (m > 0 && lane < a.k_max) {
+            const int D = n - 1 - e;                                  // >= 1
+            d = h[e + 1 + lane % D];
+        }
+        draft[(int64_t)r * LCD_DRAFT_STRIDE + lane] = d;
+    }
+    if (lane == 0) {
+        match_len[r] = m;
+        match_end[r] = e;
+    }
+}
+
+// Build: clear the tables, then insert every position p <= n-2 of every row.
+__global__ void __launch_bounds__(kBuildThreads)
+index_clear_kernel(u64 *__restrict__ tables, int64_t words) {
+    for (int64_t i = blockIdx.x * (int64_t)kBuildThreads + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * kBuildThreads)
+        tables[i] = 0;
+}
+
+__global__ void __launch_bounds__(kBuildThreads)
+clear_flags_kernel(int32_t *__restrict__ flags, int32_t n) {
+    const int i = blockIdx.x * kBuildThreads + threadIdx.x;
+    if (i < n) flags[i] = 0;
+}
+
+__global__ void __launch_bounds__(kBuildThreads)
+index_build_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
+                   const int32_t *__restrict__ len, int32_t B, IndexArgs a,
+                   const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_bits,
+                   u64 *__restrict__ tables, int32_t *__restrict__ indexed_len, int32_t chunk,
+                   int32_t cpr, int32_t *__restrict__ failed) {
+    const int r = blockIdx.x / cpr;
+    const int c = blockIdx.x - r * cpr;
+    if (r >= B) return;
+    const int32_t n0 = len[r];
+    const int n = n0 > 0 ? n0 : 0;
+    const int32_t *__restrict__ h = hist + row_off[r];
+    u64 *__restrict__ T = tables + table_off[r];
+    const int bits = table_bits[r];
+    bool ok = true;
+    // positions 0..n-2, chunks of `chunk` positions per workgroup, strided by cpr
+    for (int p0 = c * chunk; p0 <= n - 2; p0 += cpr * chunk) {
+        for (int p = p0 + threadIdx.x; p < p0 + chunk && p <= n - 2; p += kBuildThreads) {
+            u64 hs = kHashSeed;
+            for (int j = 0; j < a.l_max && p - j >= 0; ++j) {
+                hs = roll(hs, h[p - j]);
+                const int L = j + 1;
+                if (L >= a.l_min) ok = insert_one(T, bits, finish_key(hs, L), a.fp_mask, p) && ok;
+            }
+        }
+    }
+    if (!ok) atomicOr(failed + r, 1);
+    if (c == 0 && threadIdx.x == 0) indexed_len[r] = n;
+}
+
+// A row whose build hit the probe bound is marked stale (answered by scans).
+__global__ void index_mark_kernel(const int32_t *__restrict__ failed, int32_t B,
+                                  int32_t *__restrict__ indexed_len) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r < B && failed[r] != 0) indexed_len[r] = -1;
+}
+
+IndexArgs index_args(const lcd_params *p, int32_t fp_bits) {
+    IndexArgs a;
+    a.l_min = p->l_min;
+    a.l_max = p->l_max;
+    a.k_max = p->k_max;
+    const int fb = fp_bits <= 0 ? 31 : fp_bits;
+    a.fp_mask = fb >= 31 ? 0x7FFFFFFFu : ((1u << fb) - 1u);
+    return a;
+}
+
+int table_bits_for(int32_t cap, int nL) {
+    const int64_t need = 4 * (int64_t)nL * (int64_t)(cap > 1 ? cap : 1);
+    int b = 4;
+    while (((int64_t)1 << b) < need) ++b;
+    return b;
+}
+
+}  // namespace
+}  // namespace lcd
+
+extern "C" int64_t lookup_index_plan(const int32_t *cap, int32_t B, const lcd_params *p,
+                                     int64_t *table_off, int32_t *table_bits) {
+    using namespace lcd;
+    if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    if (B > 0 && (!cap || !table_off || !table_bits)) return LCD_EINVAL;
+    const int nL = p->l_max - p->l_min + 1;
+    int64_t off = 0;
+    for (int32_t r = 0; r < B; ++r) {
+        if (cap[r] < 0) return LCD_EINVAL;
+        const int b = table_bits_for(cap[r], nL);
+        if (b > 34) return LCD_EINVAL;
+        table_off[r] = off;
+        table_bits[r] = b;
+        off += (int64_t)1 << b;
+    }
+    return off * 8;
+}
+
+extern "C" int lookup_index_build(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                                  int32_t B, const lcd_params *p, int32_t fp_bits,
+                                  const int64_t *table_off, const int32_t *table_bits,
+                                  void *tables, size_t table_bytes, int32_t *indexed_len,
+                                  int32_t *scratch, int32_t max_len, void *stream) {
+    using namespace lcd;
+    if (B < 0 || max_len < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK)
+        return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!hist || !row_off || !len || !table_off || !table_bits || !tables || !indexed_len ||
+        !scratch || (reinterpret_cast<uintptr_t>(tables) & 7) != 0 || table_bytes < 8)
+        return LCD_EINVAL;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const IndexArgs a = index_args(p, fp_bits);
+    const int64_t words = (int64_t)(table_bytes / 8);
+    const int64_t clear_blocks = (words + kBuildThreads - 1) / kBuildThreads;
+    hipLaunchKernelGGL(index_clear_kernel, dim3((unsigned)(clear_blocks < 65536 ? clear_blocks : 65536)),
+                       dim3(kBuildThreads), 0, st, static_cast<u64 *>(tables), words);
+    // scratch: B int32 flags of rows whose build hit the probe bound
+    hipLaunchKernelGGL(clear_flags_kernel, dim3((unsigned)((B + kBuildThreads - 1) / kBuildThreads)),
+                       dim3(kBuildThreads), 0, st, scratch, B);
+    const int32_t chunk = 4096;
+    const int64_t per_row = ((int64_t)max_len + chunk - 1) / chunk;
+    const int32_t cpr = (int32_t)(per_row < 1 ? 1 : (per_row > 4096 ? 4096 : per_row));
+    hipLaunchKernelGGL(index_build_kernel, dim3((unsigned)((int64_t)B * cpr)), dim3(kBuildThreads),
+                       0, st, hist, row_off, len, B, a, table_off, table_bits,
+                       static_cast<u64 *>(tables), indexed_len, chunk, cpr, scratch);
+    hipLaunchKernelGGL(index_mark_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st,
+                       scratch, B, indexed_len);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+
+extern "C" int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                                    int32_t B, const lcd_params *p, int32_t fp_bits,
+                                    const int64_t *table_off, const int32_t *table_bits,
+                                    void *tables, int32_t *indexed_len, int32_t *match_len,
+                                    int32_t *match_end, int32_t *draft, void *stream) {
+    using namespace lcd;
+    if (B < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!hist || !row_off || !len || !table_off || !table_bits || !tables || !indexed_len ||
+        !match_len || !match_end || !draft || (reinterpret_cast<uintptr_t>(tables) & 7) != 0)
+        return LCD_EINVAL;
+    const IndexArgs a = index_args(p, fp_bits);
+    hipLaunchKernelGGL(index_propose_kernel, dim3((unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(64 * kWavesPerBlock), 0, reinterpret_cast<hipStream_t>(stream), hist,
+                       row_off, len, B, a, table_off, table_bits, static_cast<u64 *>(tables),
+                       indexed_len, match_len, match_end, draft);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}

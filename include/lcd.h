@@ -287,6 +287,58 @@ int lookup_telemetry_update(uint32_t *telemetry, const int32_t *match_len, const
 int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, int32_t B,
                             int32_t K, uint64_t *out, void *stream);
 
+/*
+ * Incremental n-gram index: the lookup of lookup_propose answered without
+ * scanning the history.  Article, section "第 1 步" (the lookup itself); the
+ * forum thread's reply on the method's pitfalls (the lookup index has to be
+ * maintained incrementally; a full scan at every step of a long context
+ * costs more and more).  Results are identical to lookup_propose's.
+ *
+ * Per request r the index is one hash table of 2^table_bits[r] 8-byte slots at
+ * table_off[r] (in slots) inside `tables`, keyed by every L-gram, L in
+ * [l_min, l_max], that ends at a position p <= len-2, holding the latest such
+ * p; indexed_len[r] (int32, device) is the history length the table covers.
+ * Tables are sized for at most 1/4 occupancy when rows grow up to cap[r].
+ * l_min and l_max must be the same at build and at every propose, and so must
+ * fp_bits (fingerprint bits, 1..31, 0 = 31; fewer bits only make fingerprint
+ * collisions, and with them the slow path, more frequent).
+ */
+
+/*
+ * lookup_index_plan -- host only.  Fills table_off[r] (slots) and
+ * table_bits[r] for B rows of capacities cap[r] (host arrays) and returns the
+ * total table bytes, or LCD_EINVAL (< 0).
+ */
+int64_t lookup_index_plan(const int32_t *cap, int32_t B, const lcd_params *p,
+                          int64_t *table_off, int32_t *table_bits);
+
+/*
+ * lookup_index_build -- clears the tables (table_bytes of them) and indexes
+ * every position p <= len[r]-2 of every row; sets indexed_len[r] = max(len[r],
+ * 0) (or -1 for a row whose table overflowed).  table_off / table_bits are the
+ * plan's arrays, on the device; scratch is int32[B] of device memory;
+ * max_len >= every len[r] (launch sizing).  Several launches on `stream`.
+ */
+int lookup_index_build(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
+                       const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
+                       const int32_t *table_bits, void *tables, size_t table_bytes,
+                       int32_t *indexed_len, int32_t *scratch, int32_t max_len, void *stream);
+
+/*
+ * lookup_index_propose -- the outputs of lookup_propose (match_len, match_end,
+ * draft), from the index.  First indexes the positions appended since the last
+ * call (indexed_len[r]-1 .. len[r]-2; histories only grow between calls), then
+ * looks up every suffix length at once.  A row whose history got shorter than
+ * indexed_len[r], whose table overflowed, or whose answer a fingerprint
+ * collision leaves in doubt is answered by an exact scan of its history (the
+ * first two mark the row stale, indexed_len[r] = -1, until it is rebuilt).
+ * One launch, one wave per request, no allocation.
+ */
+int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
+                         const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
+                         const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                         int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream);
+
 /* Largest vocabulary rejection_accept takes (2^22). */
 #define LCD_SAMPLE_MAX_VOCAB 4194304
 

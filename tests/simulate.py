@@ -52,7 +52,11 @@ def simulate_oracle(w: Workload, steps: int, params=None, record: bool = True):
     return dict(recs=recs, emitted=emitted, lens=lens, flat=flat, row_off=row_off, tele=tele)
 
 
-def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, device="cuda:0"):
+def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, device="cuda:0",
+                 index: bool = False, fp_bits: int = 0):
+    """The decode loop through the four separate entry points; with ``index``
+    the lookup comes from lookup_index_propose (built once from the prompts,
+    updated by every call) instead of lookup_propose."""
     import torch
     import context_lookup_drafting_amd as lcd
     params = params or lcd.default_params()
@@ -78,8 +82,15 @@ def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, devi
     recs = []
     emitted = [[] for _ in range(B)]
     max_len = int(lens.max()) + _extra(steps) if B else 0
+    idx = None
+    if index:
+        idx = lcd.LookupIndex(cap, dev, params, fp_bits=fp_bits)
+        idx.build(h_d, ro_d, len_d, max_len)
     for t in range(steps):
-        lcd.lookup_propose(h_d, ro_d, len_d, max_len, ws, m, e, d, params)
+        if idx is not None:
+            idx.propose(h_d, ro_d, len_d, m, e, d)
+        else:
+            lcd.lookup_propose(h_d, ro_d, len_d, max_len, ws, m, e, d, params)
         q, tgt = w.step_inputs(pos, t)
         q_d = torch.from_numpy(q).to(dev)
         tgt_d = torch.from_numpy(tgt).to(dev)
@@ -101,7 +112,8 @@ def simulate_gpu(w: Workload, steps: int, params=None, record: bool = True, devi
                              long_next=long_next.cpu().numpy()))
     torch.cuda.synchronize()
     return dict(recs=recs, emitted=emitted, lens=len_d.cpu().numpy(), flat=h_d.cpu().numpy(),
-                row_off=row_off, ws=ws, tele=tele.cpu().numpy().view(np.uint32))
+                row_off=row_off, ws=ws, tele=tele.cpu().numpy().view(np.uint32),
+                indexed_len=None if idx is None else idx.indexed_len.cpu().numpy())
 
 
 def simulate_gpu_fused(w: Workload, steps: int, params=None, record: bool = True, device="cuda:0"):

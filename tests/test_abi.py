@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import context_lookup_drafting_amd as lcd
@@ -15,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "lcd.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|void|size_t)\s+\**\s*(\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|void|size_t|int64_t)\s+\**\s*(\w+)\s*\(", src, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -192,3 +193,55 @@ def test_rejection_accept_rejects_misuse_without_launching():
     assert call(ua=0) == lcd.LCD_EINVAL
     assert call(block=0) == lcd.LCD_EINVAL
     assert call(hist=fake, ro=fake, ln=None, cp=fake) == lcd.LCD_EINVAL   # append needs len
+
+
+def test_index_plan_sizes_tables_on_the_host():
+    """lookup_index_plan runs on the host: power-of-two tables of at least
+    4 x (number of lengths) x capacity slots, laid out back to back."""
+    L = lcd.load()
+    p = lcd.default_params()
+    cap = np.array([0, 1, 100, 25_000, 262_144], np.int32)
+    off = np.zeros(5, np.int64)
+    bits = np.zeros(5, np.int32)
+    total = L.lookup_index_plan(cap.ctypes.data_as(ctypes.c_void_p), 5, ctypes.byref(p),
+                                off.ctypes.data_as(ctypes.c_void_p),
+                                bits.ctypes.data_as(ctypes.c_void_p))
+    nL = p.l_max - p.l_min + 1
+    for r in range(5):
+        slots = 1 << int(bits[r])
+        assert slots >= 4 * nL * max(int(cap[r]), 1) and slots // 2 < max(16, 4 * nL * max(int(cap[r]), 1))
+    assert off.tolist() == np.concatenate([[0], np.cumsum(1 << bits.astype(np.int64))[:-1]]).tolist()
+    assert total == 8 * int((1 << bits.astype(np.int64)).sum())
+    # misuse
+    bad_cap = np.array([5, -1], np.int32)
+    assert L.lookup_index_plan(bad_cap.ctypes.data_as(ctypes.c_void_p), 2, ctypes.byref(p),
+                               off.ctypes.data_as(ctypes.c_void_p),
+                               bits.ctypes.data_as(ctypes.c_void_p)) == lcd.LCD_EINVAL
+    bad = lcd.default_params(l_max=20)
+    assert L.lookup_index_plan(cap.ctypes.data_as(ctypes.c_void_p), 5, ctypes.byref(bad),
+                               off.ctypes.data_as(ctypes.c_void_p),
+                               bits.ctypes.data_as(ctypes.c_void_p)) == lcd.LCD_EINVAL
+    assert L.lookup_index_plan(None, 0, ctypes.byref(p), None, None) == 0
+
+
+def test_index_entry_points_reject_misuse_without_launching():
+    L = lcd.load()
+    p = lcd.default_params()
+    pp = ctypes.byref(p)
+    f = _P(0x1000)
+    s = None
+    # build: fingerprint bits out of range, missing scratch, misaligned tables
+    assert L.lookup_index_build(f, f, f, 3, pp, 32, f, f, f, 64, f, f, 10, s) == lcd.LCD_EINVAL
+    assert L.lookup_index_build(f, f, f, 3, pp, 0, f, f, f, 64, f, None, 10, s) == lcd.LCD_EINVAL
+    assert L.lookup_index_build(f, f, f, 3, pp, 0, f, f, _P(0x1004), 64, f, f, 10, s) == lcd.LCD_EINVAL
+    assert L.lookup_index_build(f, f, f, 3, pp, 0, f, f, f, 64, f, f, -1, s) == lcd.LCD_EINVAL
+    assert L.lookup_index_build(None, None, None, 0, pp, 0, None, None, None, 0, None, None, 0,
+                                s) == lcd.LCD_OK
+    # propose
+    assert L.lookup_index_propose(f, f, f, 3, pp, -1, f, f, f, f, f, f, f, s) == lcd.LCD_EINVAL
+    assert L.lookup_index_propose(f, f, f, 3, pp, 0, f, f, f, None, f, f, f, s) == lcd.LCD_EINVAL
+    bad = lcd.default_params(l_min=0)
+    assert L.lookup_index_propose(f, f, f, 3, ctypes.byref(bad), 0, f, f, f, f, f, f, f,
+                                  s) == lcd.LCD_EINVAL
+    assert L.lookup_index_propose(None, None, None, 0, pp, 0, None, None, None, None, None, None,
+                                  None, s) == lcd.LCD_OK
