@@ -52,6 +52,8 @@ def parse():
                     help="time the four separate entry points instead of the fused step")
     ap.add_argument("--telemetry", action="store_true",
                     help="fused step with per-request acceptance telemetry on")
+    ap.add_argument("--lookup", default="scan", choices=["scan", "index"],
+                    help="index: decode steps whose lookup comes from the incremental n-gram index")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="profiling aid: only N eager lookup launches over the rotating sets")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -204,6 +206,9 @@ def main():
         return
     if args.workload == "sampled":
         bench_sampled(args)
+        return
+    if args.lookup == "index":
+        bench_index(args)
         return
 
     import numpy as np
@@ -392,6 +397,142 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_work_seconds)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+INDEX_METRIC = "history tokens served/s by the incremental-index lookup (decode steps with appends)"
+
+
+def bench_index(args):
+    """Decode steps through lookup_index_propose, fuse_verify_block,
+    greedy_accept (appending) and lookup_schedule_step: the histories grow
+    every step and each propose indexes what the previous step appended.  The
+    index is built once from the prompts (timed apart)."""
+    import numpy as np
+    import torch
+
+    import context_lookup_drafting_amd as lcd
+    from context_lookup_drafting_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = {"c3": wl.config3, "c4": wl.config4, "c5": wl.config5}[args.workload]()
+    K, W = args.steps, args.warmup
+    R = 8
+    n_k = 200                                              # event-timed steps after the graph
+    extra = 16 * (K + W + 2 * R + 8 + n_k)
+    flat, ro, ln, cap = wl.pack_rows(w.hists, extra=extra)
+    B = w.B
+    p = lcd.default_params()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    h_d, ro_d, ln_d, cap_d = t(flat), t(ro), t(ln.copy()), t(cap)
+    q, tgt = w.step_inputs(np.zeros(B, np.int64), 0)
+    q_d, tgt_d = t(q), t(tgt)
+    m = torch.empty(B, dtype=torch.int32, device=dev)
+    e = torch.empty_like(m)
+    d = torch.empty((B, 15), dtype=torch.int32, device=dev)
+    blk = torch.empty((B, 15), dtype=torch.int32, device=dev)
+    bl = torch.empty(B, dtype=torch.int32, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
+    longs = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    idx = lcd.LookupIndex(cap, dev, p)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record()
+    idx.build(h_d, ro_d, ln_d, int(ln.max()))
+    b1.record()
+    torch.cuda.synchronize()
+    build_ms = b0.elapsed_time(b1)
+
+    def step(i, ev=None):
+        idx.propose(h_d, ro_d, ln_d, m, e, d, events=ev)
+        lcd.fuse_verify_block(d, m, q_d, longs[i % 2], blk, bl, p)
+        lcd.greedy_accept(blk, bl, tgt_d, acc, hist=h_d, row_off=ro_d, lens=ln_d, cap=cap_d)
+        lcd.lookup_schedule_step(state, m, acc, bl, longs[(i + 1) % 2], p)
+
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(R):
+                step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(max(1, -(-W // R))):
+        g.replay()
+    torch.cuda.synchronize()
+    len0 = int(ln_d.sum())
+    t0 = time.perf_counter()
+    for _ in range(-(-K // R)):
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    steps_run = -(-K // R) * R
+    len1 = int(ln_d.sum())
+    if (acc.cpu().numpy() < 0).any():
+        print("bench.py: a row ran out of capacity", file=sys.stderr)
+        sys.exit(3)
+    hev = HipEvents(lcd.load())
+    evs = [(hev.create(), hev.create()) for _ in range(n_k)]
+    for i in range(n_k):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    durs = np.array([hev.elapsed_ms(a, b) for a, b in evs]) * 1e-3
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    k_avg = float(durs.mean())
+    appended = (len1 - len0) / steps_run / B               # tokens appended per request and step
+    nL = p.l_max - p.l_min + 1
+    # per request: suffix and row metadata (48 + 24), per appended token its
+    # token and nL table read-modify-writes (4 + 16 nL), nL probes (8 nL), the
+    # verified tokens (48), the draft and match outputs (68)
+    alg = int(B * (72 + appended * (4 + 16 * nL) + 8 * nL + 48 + 68))
+    tokens = (len0 + len1) / 2
+    value = steps_run * tokens / elapsed
+    out = {
+        "metric": INDEX_METRIC,
+        "value": round(value, 1),
+        "unit": "history tokens/s",
+        "n_gpus": 1,
+        "steps": steps_run,
+        "warmup": W,
+        "ms_per_step": round(elapsed / steps_run * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": B,
+            "tokens_per_step_mean": round(tokens, 1),
+            "appended_per_request_step": round(appended, 3),
+            "launch": f"HIP graph of {R} steps, 4 entry points per step, lookup from the index",
+            "index_build_ms": round(build_ms, 3),
+            "index_table_bytes": idx.table_bytes,
+        },
+        "lookups_per_s": round(steps_run * B / elapsed, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(alg / k_avg / 1e9, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(alg / k_avg / 1e9 / HBM_PEAK_GBPS, 6),
+            "traffic": None,
+            "kernel": "index_propose_kernel",
+            "kernel_us_mean": round(k_avg * 1e6, 3),
+            "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, x)) * 1e6, 3)
+                                      for x in (10, 50, 90)],
+            "alg_bytes_per_launch": alg,
+            "launches_timed": n_k,
+            "note": "a handful of dependent round trips per request: latency-bound, not bandwidth-bound",
+        },
+        "cpu_baseline": (cpu_baseline(w, args.cpu_work_seconds) if args.cpu_work_seconds > 0 else None),
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -95,6 +95,7 @@ def load():
         L.lookup_index_plan.restype = ctypes.c_int64
         L.lookup_index_build.argtypes = [P, P, P, i32, pp, i32, P, P, P, ctypes.c_size_t, P, P, i32, P]
         L.lookup_index_propose.argtypes = [P, P, P, i32, pp, i32, P, P, P, P, P, P, P, P]
+        L.lookup_index_propose_timed.argtypes = [P, P, P, i32, pp, i32, P, P, P, P, P, P, P, P, P, P]
         rej = [P, P, P, P, P, i32, P, P, i32, i32, P, ctypes.c_size_t, P, P, P, P, P, P, P]
         L.rejection_accept.argtypes = rej
         L.rejection_accept_timed.argtypes = rej + [P, P]
@@ -102,7 +103,7 @@ def load():
                   L.greedy_accept, L.lookup_schedule_step, L.lookup_decode_step,
                   L.lookup_decode_step_timed, L.lookup_telemetry_update,
                   L.lookup_telemetry_reduce, L.rejection_accept, L.rejection_accept_timed,
-                  L.lookup_index_build, L.lookup_index_propose):
+                  L.lookup_index_build, L.lookup_index_propose, L.lookup_index_propose_timed):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -490,10 +491,16 @@ class LookupIndex:
             _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
             ctypes.c_void_p(self._scratch.data_ptr()), ctypes.c_int32(int(max_len)), _stream(dev)))
 
-    def propose(self, hist, row_off, lens, match_len, match_end, draft):
+    def propose(self, hist, row_off, lens, match_len, match_end, draft, events=None):
+        """``events``: optional (start, stop) raw hipEvent_t handles stamped by
+        the GPU around the kernel (profiling)."""
         import torch
         B, dev = self.B, self.device
-        _check("lookup_index_propose", load().lookup_index_propose(
+        L = load()
+        fn = L.lookup_index_propose if events is None else L.lookup_index_propose_timed
+        extra = () if events is None else (ctypes.c_void_p(events[0] or None),
+                                           ctypes.c_void_p(events[1] or None))
+        _check("lookup_index_propose", fn(
             _dev(hist, "hist", torch.int32, device=dev),
             _dev(row_off, "row_off", torch.int64, B, dev),
             _dev(lens, "lens", torch.int32, B, dev), ctypes.c_int32(B), ctypes.byref(self.p),
@@ -503,4 +510,4 @@ class LookupIndex:
             _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
             _dev(match_len, "match_len", torch.int32, B, dev),
             _dev(match_end, "match_end", torch.int32, B, dev),
-            _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev), _stream(dev)))
+            _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev), _stream(dev), *extra))

@@ -25,12 +25,15 @@
 // Tables hold at most 1/4 of their slots (the plan sizes them from the
 // capacity of each row).
 //
-// lookup_index_propose: one wave per request.  It first inserts the positions
-// appended since the last call (lanes over positions, all lengths of a
-// position issued back to back), then queries all lengths at once (lane k
-// takes L = l_min + k), verifies, and copies the draft.  About six dependent
-// memory round trips per step, whatever the history length.
+// lookup_index_propose: one wave per request.  The positions appended since
+// the last call (lanes over positions) are matched against the suffix
+// directly and inserted (every length's compare-and-swap in flight at once);
+// concurrently the table is queried for all lengths at once (lane k takes
+// L = l_min + k) and the hits verified; the answer is the better of the two.
+// About five dependent memory round trips per step, whatever the history
+// length.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -146,90 +149,127 @@ index_propose_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict
 
     bool exact = il < 0 || il > n;           // stale index: answered by a scan from now on
     bool overfull = false;
-    // ---- insert the positions appended since the last call ----------------
-    if (!exact) {
-        const int p_lo = il > 0 ? il - 1 : 0;
-        const int p_hi = n - 2;               // positions p <= n-2 are indexed
-        bool ok = true;
-        for (int p0 = p_lo; p0 <= p_hi; p0 += 64) {
-            const int p = p0 + lane;
-            if (p <= p_hi) {
-                int32_t t[kMaxL];
-#pragma unroll
-                for (int j = 0; j < kMaxL; ++j)
-                    t[j] = (j < a.l_max && p - j >= 0) ? h[p - j] : 0;
-                // every length's first compare-and-swap in flight at once
-                const u64 cmask = ((u64)1 << bits) - 1;
-                u64 ent[kMaxL], slot[kMaxL], old[kMaxL];
-                u64 hs = kHashSeed;
-#pragma unroll
-                for (int j = 0; j < kMaxL; ++j) {
-                    hs = roll(hs, t[j]);
-                    const int L = j + 1;
-                    const u64 k = finish_key(hs, L);
-                    ent[j] = entry_of(k, a.fp_mask, p);
-                    slot[j] = k & cmask;
-                    old[j] = (L >= a.l_min && L <= a.l_max && p - j >= 0)
-                                 ? atomicCAS(T + slot[j], 0ull, ent[j]) : 0ull;
-                }
-#pragma unroll
-                for (int j = 0; j < kMaxL; ++j) {
-                    if (old[j] == 0) continue;                      // inserted (or no such length)
-                    if ((old[j] >> 32) == (ent[j] >> 32)) atomicMax(T + slot[j], ent[j]);
-                    else ok = insert_from(T, bits, ent[j], (slot[j] + 1) & cmask) && ok;
-                }
-            }
-        }
-        if (__ballot(!ok) != 0) exact = overfull = true;
-        // this wave's inserts are complete and visible before it queries
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
-    }
-
-    // ---- query: lane k takes length L = l_min + k ------------------------
     u64 key = 0;
     if (!exact) {
-        const int L = a.l_min + lane;
-        int e = -1;
-        bool collide = false;
-        if (lane < nL && L <= n - 1) {        // the suffix and an earlier occurrence both fit
-            int32_t s[kMaxL];
+        // The suffix s_j = h[n-1-j], in every lane (the same addresses for all
+        // lanes), loaded together with the appended positions' tokens below.
+        int32_t s[kMaxL];
 #pragma unroll
-            for (int j = 0; j < kMaxL; ++j) s[j] = (j < L) ? h[n - 1 - j] : 0;
+        for (int j = 0; j < kMaxL; ++j) s[j] = (j < a.l_max && n - 1 - j >= 0) ? h[n - 1 - j] : 0;
+
+        // ---- the positions appended since the last call: p_lo..p_hi --------
+        // Each is matched against the suffix directly (from its tokens in
+        // registers) and inserted into the table.  The table query does not
+        // wait for these inserts: its first probe is issued together with the
+        // inserts' compare-and-swaps, and the answer is the better of the
+        // table's (old positions, or a new one whose insert it happened to
+        // see) and the direct match over the new positions.
+        const int p_lo = il > 0 ? il - 1 : 0;
+        const int p_hi = n - 2;
+        const u64 cmask = ((u64)1 << bits) - 1;
+        bool ok = true;
+        u64 key_new = 0;
+
+        // the query's key for length L = l_min + lane (ALU only)
+        const int L = a.l_min + lane;
+        const bool qlane = lane < nL && L <= n - 1;   // the suffix and an earlier occurrence both fit
+        u64 qk = 0;
+        {
             u64 hs = kHashSeed;
 #pragma unroll
             for (int j = 0; j < kMaxL; ++j)
                 if (j < L) hs = roll(hs, s[j]);
-            const u64 k = finish_key(hs, L);
-            const u64 cmask = ((u64)1 << bits) - 1;
-            const uint32_t fp = fingerprint(k, a.fp_mask);
-            u64 i = k & cmask;
+            qk = finish_key(hs, L);
+        }
+        const uint32_t qfp = fingerprint(qk, a.fp_mask);
+        u64 qi = qk & cmask;
+        u64 v = 0;
+
+        for (int p0 = p_lo, first = 1; p0 <= p_hi || first; p0 += 64, first = 0) {
+            const int p = p0 + lane;
+            const bool ins = p <= p_hi;
+            int32_t t[kMaxL];
+#pragma unroll
+            for (int j = 0; j < kMaxL; ++j)
+                t[j] = (ins && j < a.l_max && p - j >= 0) ? h[p - j] : 0;
+            // direct match length at end p (capped at l_max)
+            int Lp = 0;
+            bool run = ins;
+#pragma unroll
+            for (int j = 0; j < kMaxL; ++j) {
+                run = run && j < a.l_max && p - j >= 0 && t[j] == s[j];
+                Lp += run ? 1 : 0;
+            }
+            if (Lp >= a.l_min) {
+                const u64 k = ((u64)Lp << 31) | (uint32_t)p;
+                key_new = k > key_new ? k : key_new;
+            }
+            // every length's first compare-and-swap in flight at once ...
+            u64 ent[kMaxL], slot[kMaxL], old[kMaxL];
+            u64 hs = kHashSeed;
+#pragma unroll
+            for (int j = 0; j < kMaxL; ++j) {
+                hs = roll(hs, t[j]);
+                const int Lj = j + 1;
+                const u64 k = finish_key(hs, Lj);
+                ent[j] = entry_of(k, a.fp_mask, p);
+                slot[j] = k & cmask;
+                old[j] = (ins && Lj >= a.l_min && Lj <= a.l_max && p - j >= 0)
+                             ? atomicCAS(T + slot[j], 0ull, ent[j]) : 0ull;
+            }
+            // ... and, on the first pass, the query's first probe with them
+            if (first && qlane) v = __hip_atomic_load(T + qi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int j = 0; j < kMaxL; ++j) {
+                if (old[j] == 0) continue;                          // inserted (or no such length)
+                if ((old[j] >> 32) == (ent[j] >> 32)) atomicMax(T + slot[j], ent[j]);
+                else ok = insert_from(T, bits, ent[j], (slot[j] + 1) & cmask) && ok;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const u64 o = __shfl_xor(key_new, off);
+            key_new = o > key_new ? o : key_new;
+        }
+        if (__ballot(!ok) != 0) exact = overfull = true;
+
+        // ---- table query (continued): lane k takes length L = l_min + k ------
+        int e = -1;
+        bool collide = false;
+        if (qlane) {
             for (int probes = 0; probes < kMaxProbe; ++probes) {
-                const u64 v = __hip_atomic_load(T + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (probes > 0) {
+                    qi = (qi + 1) & cmask;
+                    v = __hip_atomic_load(T + qi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
                 if (v == 0) break;                                   // no occurrence
-                if ((uint32_t)(v >> 32) == fp) {
+                if ((uint32_t)(v >> 32) == qfp) {
                     const int pe = (int)(uint32_t)v - 1;
                     bool same = pe >= L - 1 && pe <= n - 2;
+                    if (same) {
+                        int32_t g[kMaxL];                            // all loads in flight at once
 #pragma unroll
-                    for (int j = 0; j < kMaxL; ++j)
-                        if (j < L && same) same = h[pe - j] == s[j];
+                        for (int j = 0; j < kMaxL; ++j) g[j] = j < L ? h[pe - j] : 0;
+#pragma unroll
+                        for (int j = 0; j < kMaxL; ++j) same = same && (j >= L || g[j] == s[j]);
+                    }
                     if (same) e = pe; else collide = true;
                     break;
                 }
-                i = (i + 1) & cmask;
             }
         }
-        // the longest verified length wins unless a longer one is in doubt
         const u64 hit = __ballot(e >= 0);
         const u64 doubt = __ballot(collide);
+        u64 key_table = 0;
         if (hit != 0) {
             const int kb = 63 - __builtin_clzll(hit);
-            if ((doubt >> (kb + 1)) != 0) exact = true;      // a longer length is in doubt
-            if (!exact) {
-                const int eb = __builtin_amdgcn_readlane(e, kb);
-                key = ((u64)(a.l_min + kb) << 31) | (uint32_t)eb;
-            }
-        } else if (doubt != 0) {
-            exact = true;
+            key_table = ((u64)(a.l_min + kb) << 31) | (uint32_t)__builtin_amdgcn_readlane(e, kb);
+        }
+        key = key_table > key_new ? key_table : key_new;
+        // a length in doubt above the answer's could hold a longer match
+        if (doubt != 0) {
+            const int ld = a.l_min + 63 - __builtin_clzll(doubt);
+            if ((u64)ld > (key >> 31)) exact = true;
         }
     }
     if (exact) {
@@ -377,21 +417,51 @@ extern "C" int lookup_index_build(const int32_t *hist, const int64_t *row_off, c
     return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
 }
 
-extern "C" int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
-                                    int32_t B, const lcd_params *p, int32_t fp_bits,
-                                    const int64_t *table_off, const int32_t *table_bits,
-                                    void *tables, int32_t *indexed_len, int32_t *match_len,
-                                    int32_t *match_end, int32_t *draft, void *stream) {
-    using namespace lcd;
+namespace lcd {
+namespace {
+int index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
+                  const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
+                  const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                  int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream,
+                  void *ev0, void *ev1) {
     if (B < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
     if (!hist || !row_off || !len || !table_off || !table_bits || !tables || !indexed_len ||
         !match_len || !match_end || !draft || (reinterpret_cast<uintptr_t>(tables) & 7) != 0)
         return LCD_EINVAL;
     const IndexArgs a = index_args(p, fp_bits);
-    hipLaunchKernelGGL(index_propose_kernel, dim3((unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock)),
-                       dim3(64 * kWavesPerBlock), 0, reinterpret_cast<hipStream_t>(stream), hist,
-                       row_off, len, B, a, table_off, table_bits, static_cast<u64 *>(tables),
-                       indexed_len, match_len, match_end, draft);
+    const dim3 grid((unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (ev0 != nullptr || ev1 != nullptr)
+        hipExtLaunchKernelGGL(index_propose_kernel, grid, dim3(64 * kWavesPerBlock), 0u, st,
+                              reinterpret_cast<hipEvent_t>(ev0), reinterpret_cast<hipEvent_t>(ev1),
+                              0u, hist, row_off, len, B, a, table_off, table_bits,
+                              static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft);
+    else
+        hipLaunchKernelGGL(index_propose_kernel, grid, dim3(64 * kWavesPerBlock), 0, st, hist,
+                           row_off, len, B, a, table_off, table_bits, static_cast<u64 *>(tables),
+                           indexed_len, match_len, match_end, draft);
     return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+}  // namespace
+}  // namespace lcd
+
+extern "C" int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                                    int32_t B, const lcd_params *p, int32_t fp_bits,
+                                    const int64_t *table_off, const int32_t *table_bits,
+                                    void *tables, int32_t *indexed_len, int32_t *match_len,
+                                    int32_t *match_end, int32_t *draft, void *stream) {
+    return lcd::index_propose(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+                              indexed_len, match_len, match_end, draft, stream, nullptr, nullptr);
+}
+
+extern "C" int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off,
+                                          const int32_t *len, int32_t B, const lcd_params *p,
+                                          int32_t fp_bits, const int64_t *table_off,
+                                          const int32_t *table_bits, void *tables,
+                                          int32_t *indexed_len, int32_t *match_len,
+                                          int32_t *match_end, int32_t *draft, void *stream,
+                                          void *ev_start, void *ev_stop) {
+    return lcd::index_propose(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+                              indexed_len, match_len, match_end, draft, stream, ev_start, ev_stop);
 }

@@ -339,6 +339,17 @@ int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int3
                          const int32_t *table_bits, void *tables, int32_t *indexed_len,
                          int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream);
 
+/*
+ * lookup_index_propose_timed -- for profiling only: lookup_index_propose
+ * launched so that the GPU stamps its kernel's start into ev_start and end into
+ * ev_stop (hipEvent_t, either may be NULL).
+ */
+int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                               int32_t B, const lcd_params *p, int32_t fp_bits,
+                               const int64_t *table_off, const int32_t *table_bits, void *tables,
+                               int32_t *indexed_len, int32_t *match_len, int32_t *match_end,
+                               int32_t *draft, void *stream, void *ev_start, void *ev_stop);
+
 /* Largest vocabulary rejection_accept takes (2^22). */
 #define LCD_SAMPLE_MAX_VOCAB 4194304
 
