@@ -142,6 +142,71 @@ class HipEvents:
         self.h.hipEventDestroy(ctypes.c_void_p(ev))
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_ceiling(lcd, sets, nbytes, n=200, blocks=(1024, 2048, 4096)):
+    """Practical HBM read ceiling at nbytes: lcd_read_probe over the rotating
+    buffers, GPU-stamped; the best mean over a few grid sizes."""
+    import numpy as np
+    import torch
+    nbytes = nbytes // 16 * 16
+    hev = HipEvents(lcd.load())
+    best = None
+    for nb in blocks:
+        out = torch.empty(nb, dtype=torch.float32, device=sets[0].device)
+        evs = [(hev.create(), hev.create()) for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            lcd.read_probe(sets[i % len(sets)], nbytes, nb, out, a, b)
+        torch.cuda.synchronize()
+        us = float(np.mean([hev.elapsed_ms(a, b) for a, b in evs[10:]])) * 1e3
+        for a, b in evs:
+            hev.destroy(a)
+            hev.destroy(b)
+        if best is None or us < best[1]:
+            best = (nb, us)
+    return {"kernel": "lcd_read_probe", "bytes": nbytes, "blocks": best[0],
+            "us": round(best[1], 3), "gbps": round(nbytes / best[1] / 1e3, 1)}
+
+
+def prefilter_survival(w):
+    """Fraction of candidate ends e in [3, n-2] whose 4 tokens equal the
+    suffix's last 4 (what survives the 4-token test), over the batch."""
+    import numpy as np
+    surv = cand = 0
+    for h in w.hists:
+        n = len(h)
+        if n < 5:
+            continue
+        e = np.arange(3, n - 1)
+        ok = np.ones(len(e), bool)
+        for j in range(4):
+            ok &= h[e - j] == h[n - 1 - j]
+        surv += int(ok.sum())
+        cand += len(e)
+    return surv / max(cand, 1)
+
+
+def work_spread(lcd, w, max_len, p):
+    """Candidate ends per workgroup of the lookup launch: max and mean."""
+    cpr, chunk = lcd.launch_shape(w.B, max_len, p)
+    per = []
+    for h in w.hists:
+        nc = max(len(h) - 1, 0)
+        per += [max(0, min(chunk, nc - c * chunk)) for c in range(cpr)]
+    mean = sum(per) / len(per)
+    return {"workgroups": w.B * cpr, "per_request": cpr, "chunk": chunk,
+            "ends_per_wg_max": max(per), "ends_per_wg_mean": round(mean, 1),
+            "max_over_mean": round(max(per) / mean, 3) if mean else None}
+
+
 def cpu_baseline(w, work_seconds):
     """The CPU oracle (as it is) over full steps of the same batch, threads over
     requests; bounded to about `work_seconds` of CPU time summed over threads."""
@@ -181,11 +246,20 @@ def cpu_baseline(w, work_seconds):
             if time.process_time() - cpu0 >= work_seconds or time.perf_counter() - t0 > 120:
                 break
     wall = time.perf_counter() - t0
+    # the same oracle on one thread, over one request after another
+    t1 = time.perf_counter()
+    done = 0
+    while done < w.B and time.perf_counter() - t1 < max(2.0, work_seconds / 4):
+        run_chunk([done])
+        done += 1
+    one = sum(len(hs[r]) for r in range(done)) / (time.perf_counter() - t1)
     return {
         "value": round(batches * tokens / wall, 1),
         "unit": "history tokens/s",
         "cores": cores,
         "kind": "oracle",
+        "value_1thread": round(one, 1),
+        "cpu_model": cpu_model(),
         "sample": (f"{batches} full steps (lookup+fuse+accept+schedule) of the {w.B}-request "
                    f"batch, {tokens} history tokens each, threads over requests, "
                    f"{wall:.2f} s wall / {time.process_time() - cpu0:.1f} s CPU"),
@@ -346,6 +420,8 @@ def main():
 
     alg_bytes = 4 * tokens + per_request_bytes(args.separate, args.telemetry) * B
     achieved = alg_bytes / k_avg / 1e9
+    ceiling = read_ceiling(lcd, hist_sets, set_bytes)
+    ceiling["frac_of_ceiling"] = round(achieved / ceiling["gbps"], 4)
     traffic = None if (args.separate or args.telemetry) else load_traffic(w.name)
     value = K * tokens / elapsed
     out = {
@@ -377,6 +453,9 @@ def main():
         "lookups_per_s": round(K * B / elapsed, 1),
         "step_hbm_gbps": round(value * 4 / 1e9, 2),
         "step_pct_peak": round(value * 4 / 1e9 / HBM_PEAK_GBPS * 100, 2),
+        "read_ceiling": ceiling,
+        "prefilter_survival": round(prefilter_survival(w), 6),
+        "work_spread": work_spread(lcd, w, max_len, p),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

@@ -91,6 +91,10 @@ def load():
         L.lookup_telemetry_reduce.argtypes = [P, P, i32, i32, P, P]
         L.rejection_accept_workspace_bytes.argtypes = [i32, i32]
         L.rejection_accept_workspace_bytes.restype = ctypes.c_size_t
+        L.lookup_launch_shape.argtypes = [i32, i32, pp, P, P]
+        L.lookup_launch_shape.restype = ctypes.c_int
+        L.lcd_read_probe.argtypes = [P, ctypes.c_int64, i32, P, P, P, P]
+        L.lcd_read_probe.restype = ctypes.c_int
         L.lookup_index_plan.argtypes = [P, i32, pp, P, P]
         L.lookup_index_plan.restype = ctypes.c_int64
         L.lookup_index_build.argtypes = [P, P, P, i32, pp, i32, P, P, P, ctypes.c_size_t, P, P, i32, P]
@@ -511,3 +515,28 @@ class LookupIndex:
             _dev(match_len, "match_len", torch.int32, B, dev),
             _dev(match_end, "match_end", torch.int32, B, dev),
             _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev), _stream(dev), *extra))
+
+
+def launch_shape(B: int, max_len: int, params: Params | None = None):
+    """(workgroups per request, chunk length) of the lookup launch."""
+    p = params or default_params()
+    cpr, chunk = ctypes.c_int32(), ctypes.c_int32()
+    _check("lookup_launch_shape", load().lookup_launch_shape(
+        ctypes.c_int32(B), ctypes.c_int32(max_len), ctypes.byref(p), ctypes.byref(cpr),
+        ctypes.byref(chunk)))
+    return cpr.value, chunk.value
+
+
+def read_probe(buf, nbytes: int, blocks: int, out, ev_start=None, ev_stop=None):
+    """Plain streaming read of the first `nbytes` of a device tensor (measurement)."""
+    import torch
+    dev = buf.device
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("read beyond the buffer")
+    _check("lcd_read_probe", load().lcd_read_probe(
+        ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(int(nbytes)), ctypes.c_int32(int(blocks)),
+        _dev(out, "out", torch.float32, int(blocks), dev), _stream(dev),
+        ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
+
+
+from .drafter import LookupDrafter  # noqa: E402  (the stateful wrapper over the calls above)

@@ -728,6 +728,15 @@ int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32
 
 extern "C" size_t lcd_workspace_bytes(int32_t B) { return lcd::workspace_bytes(B); }
 
+extern "C" int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, int32_t *cpr,
+                                   int32_t *chunk) {
+    if (B <= 0 || max_len < 0 || !cpr || !chunk || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    const lcd::ScanArgs sa = lcd::scan_args(B, max_len, p);
+    *cpr = sa.cpr;
+    *chunk = sa.T;
+    return LCD_OK;
+}
+
 extern "C" int lookup_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
                               int32_t B, int32_t max_len, const lcd_params *p, void *workspace,
                               int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream) {

@@ -1,4 +1,4 @@
-"""Replay a synthetic decode through the fused lookup_decode_step on the GPU.
+"""Replay a synthetic decode through a LookupDrafter on the GPU.
 
 Each step: the draft model's proposal and the target's argmax tokens come from
 the workload's truth stream (workloads.Workload.step_inputs), one
@@ -22,10 +22,13 @@ import numpy as np
 from . import workloads as wl
 
 
-def run_fused(w: wl.Workload, steps: int, params=None, device="cuda:0", record=False):
-    """Runs `steps` decode steps; returns a dict with the emitted tokens per
-    request, the final history, lengths and telemetry rows (uint32 [B,32]) and,
-    with record=True, every step's outputs."""
+def run_fused(w: wl.Workload, steps: int, params=None, device="cuda:0", record=False,
+              index: bool = False):
+    """Runs `steps` decode steps through a LookupDrafter (one fused kernel per
+    step, or with ``index`` the lookup from the incremental index); returns a
+    dict with the emitted tokens per request, the final history, lengths and
+    telemetry rows (uint32 [B,32]) and, with record=True, every step's
+    outputs."""
     import torch
     import context_lookup_drafting_amd as lcd
     params = params or lcd.default_params()
@@ -37,36 +40,34 @@ def run_fused(w: wl.Workload, steps: int, params=None, device="cuda:0", record=F
     len_d = torch.from_numpy(lens.copy()).to(dev)
     cap_d = torch.from_numpy(cap).to(dev)
     max_len = int(lens.max()) + wl.N_TARGET * (steps + 1) if B else 0
-    ws = lcd.alloc_decode_workspace(B, max_len, dev, params)
-    state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
-    out = {k: torch.empty(B, dtype=torch.int32, device=dev)
-           for k in ("m", "e", "blk", "acc", "long_next")}
-    d = torch.empty((B, 15), dtype=torch.int32, device=dev)
-    block = torch.empty((B, 15), dtype=torch.int32, device=dev)
-    tele = lcd.alloc_telemetry(B, dev)
+    dr = lcd.LookupDrafter(B, max_len, dev, params, telemetry=True,
+                           index_cap=cap if index else None)
+    if index:
+        dr.build_index(h_d, ro_d, len_d)
     pos = np.zeros(B, np.int64)
     recs = []
     emitted = [[] for _ in range(B)]
     for t in range(steps):
         q, tgt = w.step_inputs(pos, t)
-        long_used = state[:, 0].clone() if record else None
-        lcd.lookup_decode_step(h_d, ro_d, len_d, cap_d, max_len, torch.from_numpy(q).to(dev),
-                               torch.from_numpy(tgt).to(dev), state, ws, out["m"], out["e"], d,
-                               block, out["blk"], out["acc"], out["long_next"], True, params,
-                               telemetry=tele)
-        acc_h = out["acc"].cpu().numpy()
+        long_used = dr.state[:, 0].clone() if record else None
+        out = dr.step(h_d, ro_d, len_d, cap_d, torch.from_numpy(q).to(dev),
+                      torch.from_numpy(tgt).to(dev), append=True)
+        acc_h = out["accept"].cpu().numpy()
         for r in range(B):
             if acc_h[r] >= 0:
                 emitted[r].extend(tgt[r, :acc_h[r] + 1].tolist())
         pos = pos + np.maximum(acc_h, 0) + 1
         if record:
-            recs.append(dict(m=out["m"].cpu().numpy(), e=out["e"].cpu().numpy(), d=d.cpu().numpy(),
-                             q=q, tgt=tgt, long=long_used.cpu().numpy(), block=block.cpu().numpy(),
-                             blk=out["blk"].cpu().numpy(), acc=acc_h, state=state.cpu().numpy(),
+            recs.append(dict(m=out["match_len"].cpu().numpy(), e=out["match_end"].cpu().numpy(),
+                             d=out["draft"].cpu().numpy(), q=q, tgt=tgt,
+                             long=long_used.cpu().numpy(), block=out["block"].cpu().numpy(),
+                             blk=out["block_len"].cpu().numpy(), acc=acc_h,
+                             state=dr.state.cpu().numpy(),
                              long_next=out["long_next"].cpu().numpy()))
     torch.cuda.synchronize()
     return dict(recs=recs, emitted=emitted, lens=len_d.cpu().numpy(), flat=h_d.cpu().numpy(),
-                row_off=row_off, tele=tele.cpu().numpy().view(np.uint32), tele_d=tele)
+                row_off=row_off, tele=dr.telemetry.cpu().numpy().view(np.uint32),
+                tele_d=dr.telemetry)
 
 
 def summarise(tele_d, class_ids, names):
@@ -105,9 +106,10 @@ def main():
     ap = argparse.ArgumentParser(description="fused decode replay with acceptance telemetry")
     ap.add_argument("--config", type=int, default=3, choices=[2, 3])
     ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--index", action="store_true", help="lookup from the incremental index")
     args = ap.parse_args()
     w = wl.make_config(args.config)
-    res = run_fused(w, args.steps)
+    res = run_fused(w, args.steps, index=args.index)
     for r in range(w.B):
         em = res["emitted"][r]
         if em != w.truths[r][:len(em)].tolist():

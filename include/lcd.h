@@ -350,6 +350,26 @@ int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, cons
                                int32_t *indexed_len, int32_t *match_len, int32_t *match_end,
                                int32_t *draft, void *stream, void *ev_start, void *ev_stop);
 
+/*
+ * lookup_launch_shape -- host only: the launch shape lookup_propose and
+ * lookup_decode_step use for B rows of at most max_len tokens: *cpr
+ * workgroups per request, each scanning a chunk of *chunk candidate ends
+ * (a multiple of 256).  For measurement (work spread per workgroup).
+ * LCD_EINVAL for B <= 0, max_len < 0 or bad params.
+ */
+int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, int32_t *cpr,
+                        int32_t *chunk);
+
+/*
+ * lcd_read_probe -- measurement only: a plain streaming read of `bytes`
+ * (a multiple of 16, 16-byte aligned device buffer) by `blocks` workgroups of
+ * 256 threads, each writing one float to out[blocks] (device).  The GPU stamps
+ * the kernel's start and end into ev_start / ev_stop (hipEvent_t, nullable).
+ * It gives the practical HBM read ceiling at a byte count on the running GPU.
+ */
+int lcd_read_probe(const void *buf, int64_t bytes, int32_t blocks, float *out, void *stream,
+                   void *ev_start, void *ev_stop);
+
 /* Largest vocabulary rejection_accept takes (2^22). */
 #define LCD_SAMPLE_MAX_VOCAB 4194304
 

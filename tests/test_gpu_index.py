@@ -165,3 +165,15 @@ def test_empty_negative_and_tiny_rows(gpu):
     ln2[3] = -5
     m, e, d, _ = index_lookup(flat, ro, ln2)
     assert m[3] == 0 and e[3] == -1 and np.all(d[3] == -1)
+
+
+def test_drafter_with_index_matches_the_oracle_decode(gpu):
+    """LookupDrafter answering from the index (build once, propose every
+    step): the whole 128-step decode and its telemetry equal the oracle's."""
+    from context_lookup_drafting_amd.decode_sim import run_fused
+    from simulate import simulate_oracle
+    w = wl.config3()
+    g = run_fused(w, 128, record=True, index=True)
+    g.pop("tele_d")
+    o = simulate_oracle(w, 128)
+    _compare_sims(g, o)
