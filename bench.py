@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-work-seconds", type=float, default=20.0,
                     help="CPU work (seconds summed over threads) for the oracle baseline; 0 = skip")
     ap.add_argument("--scan-wgs", type=int, default=0, help="lookup launch tuning (0 = auto)")
+    ap.add_argument("--balance", action="store_true",
+                    help="lookup launch tuning: token-balanced chunks (ragged batches)")
     ap.add_argument("--separate", action="store_true",
                     help="time the four separate entry points instead of the fused step")
     ap.add_argument("--telemetry", action="store_true",
@@ -195,14 +197,17 @@ def prefilter_survival(w):
 
 
 def work_spread(lcd, w, max_len, p):
-    """Candidate ends per workgroup of the lookup launch: max and mean."""
-    cpr, chunk = lcd.launch_shape(w.B, max_len, p)
+    """Candidate ends per workgroup of the lookup launch: max and mean over
+    the chunks that exist (the launch's other workgroups exit at once)."""
+    lens = [len(h) for h in w.hists]
+    wgs, chunk = lcd.launch_shape(w.B, max_len, p, lens)
     per = []
-    for h in w.hists:
-        nc = max(len(h) - 1, 0)
-        per += [max(0, min(chunk, nc - c * chunk)) for c in range(cpr)]
+    for n in lens:
+        nc = max(n - 1, 0)
+        k = (wgs // w.B) if not p.scan_balance or w.B > 1024 else max(1, -(-nc // chunk))
+        per += [max(0, min(chunk, nc - c * chunk)) for c in range(k)]
     mean = sum(per) / len(per)
-    return {"workgroups": w.B * cpr, "per_request": cpr, "chunk": chunk,
+    return {"workgroups": wgs, "chunk": chunk, "chunks": len(per),
             "ends_per_wg_max": max(per), "ends_per_wg_mean": round(mean, 1),
             "max_over_mean": round(max(per) / mean, 3) if mean else None}
 
@@ -307,7 +312,7 @@ def main():
     set_bytes = flat.nbytes
     R = max(2, -(-ROTATE_BYTES // set_bytes))
     R += R % 2                       # even, so the two long-mode buffers alternate cleanly
-    p = lcd.default_params(scan_wgs=args.scan_wgs)
+    p = lcd.default_params(scan_wgs=args.scan_wgs, scan_balance=int(args.balance))
 
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     hist_sets = [t(flat) for _ in range(R)]
@@ -449,6 +454,7 @@ def main():
                        + ("4 entry points (4 kernels) per step" if args.separate
                           else "lookup_decode_step (1 kernel) per step")),
             "telemetry": args.telemetry,
+            "scan_balance": int(args.balance),
         },
         "lookups_per_s": round(K * B / elapsed, 1),
         "step_hbm_gbps": round(value * 4 / 1e9, 2),

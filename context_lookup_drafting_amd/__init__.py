@@ -51,7 +51,8 @@ class Params(ctypes.Structure):
     """Mirror of ``lcd_params`` (include/lcd.h)."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "l_min", "l_max", "k_max", "n_head", "n_block", "head_full", "head_agree",
-        "agree_n", "tail_min", "entry_steps", "sticky", "near_full_slack", "scan_wgs")]
+        "agree_n", "tail_min", "entry_steps", "sticky", "near_full_slack", "scan_wgs",
+        "scan_balance")]
 
     def __repr__(self):
         return "Params(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -91,7 +92,7 @@ def load():
         L.lookup_telemetry_reduce.argtypes = [P, P, i32, i32, P, P]
         L.rejection_accept_workspace_bytes.argtypes = [i32, i32]
         L.rejection_accept_workspace_bytes.restype = ctypes.c_size_t
-        L.lookup_launch_shape.argtypes = [i32, i32, pp, P, P]
+        L.lookup_launch_shape.argtypes = [i32, i32, pp, P, P, P]
         L.lookup_launch_shape.restype = ctypes.c_int
         L.lcd_read_probe.argtypes = [P, ctypes.c_int64, i32, P, P, P, P]
         L.lcd_read_probe.restype = ctypes.c_int
@@ -517,14 +518,18 @@ class LookupIndex:
             _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev), _stream(dev), *extra))
 
 
-def launch_shape(B: int, max_len: int, params: Params | None = None):
-    """(workgroups per request, chunk length) of the lookup launch."""
+def launch_shape(B: int, max_len: int, params: Params | None = None, lens=None):
+    """(workgroups per launch, chunk length) of the scan; ``lens`` (host array)
+    is needed with scan_balance = 1."""
+    import numpy as np
     p = params or default_params()
-    cpr, chunk = ctypes.c_int32(), ctypes.c_int32()
+    wgs, chunk = ctypes.c_int32(), ctypes.c_int32()
+    lh = None if lens is None else np.ascontiguousarray(lens, dtype=np.int32)
     _check("lookup_launch_shape", load().lookup_launch_shape(
-        ctypes.c_int32(B), ctypes.c_int32(max_len), ctypes.byref(p), ctypes.byref(cpr),
+        ctypes.c_int32(B), ctypes.c_int32(max_len), ctypes.byref(p),
+        None if lh is None else lh.ctypes.data_as(ctypes.c_void_p), ctypes.byref(wgs),
         ctypes.byref(chunk)))
-    return cpr.value, chunk.value
+    return wgs.value, chunk.value
 
 
 def read_probe(buf, nbytes: int, blocks: int, out, ev_start=None, ev_stop=None):

@@ -87,10 +87,32 @@ constexpr int kNoTile = 1 << 19;                          // a tile index past e
 constexpr int kFullAfter = 4;                             // flagged tiles before a wave drops the quick test
 
 struct ScanArgs {
-    int32_t cpr;               // workgroups per request
+    int32_t cpr;               // workgroups per request (equal chunks per row)
     int32_t T;                 // chunk length in candidate ends, a multiple of kTileTok
     int32_t l_min, l_max, k_max;
+    int32_t B;                 // requests
+    int32_t wgs;               // workgroups per launch (token-balanced chunks)
 };
+
+// Token-balanced chunks (ragged batches): one chunk length for the whole
+// batch, from the total and the longest row's candidate ends and the grid of
+// wgs workgroups -- long enough that the chunks of all rows (at least one per
+// row) fit the grid, and that no row has more than kMaxCpr chunks.  The device
+// and the host's launch-shape query use this same rule.
+__host__ __device__ inline int32_t balanced_chunk_len(int64_t total, int64_t longest, int64_t wgs,
+                                                      int64_t B) {
+    const int64_t room = wgs - B > 0 ? wgs - B : 1;
+    int64_t t = (total + room - 1) / room;
+    const int64_t t2 = (longest + 63) / 64;
+    if (t < t2) t = t2;
+    t = (t + 255) / 256 * 256;
+    if (t < 256) t = 256;
+    return (int32_t)(t < (int64_t(1) << 30) ? t : (int64_t(1) << 30));
+}
+
+__host__ __device__ inline int balanced_chunks(int64_t nc, int32_t t) {
+    return nc > 0 ? (int)((nc + t - 1) / t) : 1;   // a row without candidates still has chunk 0
+}
 // (The kernel takes cpr and T as separate leading arguments.)
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -318,7 +340,63 @@ __device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin,
     }
 }
 
-template <int PF, int kMode>
+constexpr int kBalPer = LCD_BALANCE_MAX_B / 64;           // lengths held per lane
+
+__device__ __forceinline__ int wave_scan_int(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Token-balanced assignment of workgroup blockIdx.x: every wave reads all B
+// lengths (one round trip), derives the batch's chunk length and finds its
+// (request, chunk) by a prefix over the rows' chunk counts.  Returns false
+// when the workgroup has no chunk.
+__device__ __forceinline__ bool balanced_assignment(const int32_t *__restrict__ len, int B, int lane,
+                                                    int &r, int &c0, int &P, int &T) {
+    int nc[kBalPer];
+#pragma unroll
+    for (int k = 0; k < kBalPer; ++k) {
+        const int row = k * 64 + lane;
+        const int l = row < B ? len[row] : 0;
+        nc[k] = l > 1 ? l - 1 : 0;
+    }
+    u64 tot = 0;
+    u64 mx = 0;
+#pragma unroll
+    for (int k = 0; k < kBalPer; ++k) {
+        tot += (u64)nc[k];
+        mx = (u64)nc[k] > mx ? (u64)nc[k] : mx;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+    mx = wave_max(mx);
+    T = balanced_chunk_len((int64_t)tot, (int64_t)mx, (int64_t)gridDim.x, (int64_t)B);
+    const int w = (int)blockIdx.x;
+    int base = 0;
+#pragma unroll
+    for (int k = 0; k < kBalPer; ++k) {
+        if (k * 64 >= B) break;
+        const int row = k * 64 + lane;
+        const int kr = row < B ? balanced_chunks(nc[k], T) : 0;
+        const int incl = wave_scan_int(kr, lane);
+        const int gsum = __builtin_amdgcn_readlane(incl, 63);
+        if (w < base + gsum) {
+            const int l = (int)__builtin_ctzll(ballot(base + incl > w));
+            r = k * 64 + l;
+            c0 = w - base - __builtin_amdgcn_readlane(incl - kr, l);
+            P = __builtin_amdgcn_readlane(kr, l);
+            return true;
+        }
+        base += gsum;
+    }
+    return false;
+}
+
+template <int PF, int kMode, bool kBal>
 __global__ void __launch_bounds__(kThreads)
 lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
                    const int32_t *__restrict__ len, int32_t cpr, int32_t T, ScanArgs a,
@@ -333,8 +411,18 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     const int lane = tid & 63;
     const int wave = uni(tid >> 6);   // wave-uniform
     // workgroup = (request r, chunk c0)
-    const int r = (int)(blockIdx.x / (unsigned)cpr);
-    const int c0 = (int)blockIdx.x - r * cpr;
+    int r, c0;
+    if constexpr (kBal) {
+        int P_b, T_b;
+        if (!balanced_assignment(len, a.B, lane, r, c0, P_b, T_b)) return;
+        r = uni(r);
+        c0 = uni(c0);
+        cpr = uni(P_b);               // this row's chunks: one workgroup each
+        T = uni(T_b);
+    } else {
+        r = (int)(blockIdx.x / (unsigned)cpr);
+        c0 = (int)blockIdx.x - r * cpr;
+    }
     const int sin = (kMode == kStep && wave == 0) ? load_step_input(r, lane, io) : 0;
     uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
     if (kMode == kStep && wave == 0 && io.tele != nullptr)
@@ -643,18 +731,28 @@ int32_t chunk_len(int32_t max_len, int cpr) {
     return (int32_t)(T < (int64_t(1) << 30) ? T : (int64_t(1) << 30));
 }
 
+template <int PF, int kMode, bool kBal>
+hipError_t launch_one(const int32_t *hist, const int64_t *row_off, const int32_t *len,
+                      ScanArgs sa, u64 *ws, int32_t *ml, int32_t *me, int32_t *dr,
+                      const StepIO &io, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const dim3 grid((unsigned)(kBal ? (int64_t)sa.wgs : (int64_t)sa.B * sa.cpr));
+    if (ev0 != nullptr || ev1 != nullptr)
+        hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kMode, kBal>, grid, dim3(kThreads), 0u, st, ev0,
+                              ev1, 0u, hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
+    else
+        hipLaunchKernelGGL((lookup_scan_kernel<PF, kMode, kBal>), grid, dim3(kThreads), 0, st,
+                           hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
+    return hipGetLastError();
+}
+
 template <int PF, int kMode>
 hipError_t launch(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
                   ScanArgs sa, u64 *ws, int32_t *ml, int32_t *me, int32_t *dr, const StepIO &io,
                   hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    const dim3 grid((unsigned)((int64_t)B * sa.cpr));
-    if (ev0 != nullptr || ev1 != nullptr)
-        hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kMode>, grid, dim3(kThreads), 0u, st, ev0, ev1,
-                              0u, hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
-    else
-        hipLaunchKernelGGL((lookup_scan_kernel<PF, kMode>), grid, dim3(kThreads), 0, st,
-                           hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
-    return hipGetLastError();
+    (void)B;
+    if (sa.wgs > 0)
+        return launch_one<PF, kMode, true>(hist, row_off, len, sa, ws, ml, me, dr, io, st, ev0, ev1);
+    return launch_one<PF, kMode, false>(hist, row_off, len, sa, ws, ml, me, dr, io, st, ev0, ev1);
 }
 
 template <int kMode>
@@ -669,9 +767,29 @@ hipError_t launch_scan(int pf, const int32_t *hist, const int64_t *row_off, cons
     }
 }
 
+// Workgroups of a token-balanced launch: scan_wgs, or 4 per request within
+// [256, 2048] (on 256 rows of 1k-262k tokens, 4-5 per request measured best:
+// fewer, larger chunks amortise each workgroup's start and merge), at least 2
+// and at most kMaxCpr per request.
+int balanced_wgs(int32_t B, int32_t max_len, int32_t scan_wgs) {
+    (void)max_len;
+    int64_t g;
+    if (scan_wgs > 0) {
+        g = scan_wgs;
+    } else {
+        g = 4 * (int64_t)B;
+        g = g < 256 ? 256 : (g > 2048 ? 2048 : g);
+    }
+    if (g < 2 * (int64_t)B) g = 2 * (int64_t)B;
+    if (g > (int64_t)kMaxCpr * B) g = (int64_t)kMaxCpr * B;
+    return (int)g;
+}
+
 ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
+    if (p->scan_balance == 1 && B <= LCD_BALANCE_MAX_B)
+        return ScanArgs{0, 0, p->l_min, p->l_max, p->k_max, B, balanced_wgs(B, max_len, p->scan_wgs)};
     const int cpr = pick_cpr(B, max_len, p->scan_wgs);
-    return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max};
+    return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max, B, 0};
 }
 
 int propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
@@ -728,12 +846,24 @@ int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32
 
 extern "C" size_t lcd_workspace_bytes(int32_t B) { return lcd::workspace_bytes(B); }
 
-extern "C" int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, int32_t *cpr,
-                                   int32_t *chunk) {
-    if (B <= 0 || max_len < 0 || !cpr || !chunk || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+extern "C" int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p,
+                                   const int32_t *len_host, int32_t *wgs, int32_t *chunk) {
+    if (B <= 0 || max_len < 0 || !wgs || !chunk || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     const lcd::ScanArgs sa = lcd::scan_args(B, max_len, p);
-    *cpr = sa.cpr;
-    *chunk = sa.T;
+    if (sa.wgs > 0) {
+        if (!len_host) return LCD_EINVAL;
+        int64_t tot = 0, mx = 0;
+        for (int32_t r = 0; r < B; ++r) {
+            const int64_t nc = len_host[r] > 1 ? (int64_t)len_host[r] - 1 : 0;
+            tot += nc;
+            mx = nc > mx ? nc : mx;
+        }
+        *wgs = sa.wgs;
+        *chunk = lcd::balanced_chunk_len(tot, mx, sa.wgs, B);
+    } else {
+        *wgs = sa.B * sa.cpr;
+        *chunk = sa.T;
+    }
     return LCD_OK;
 }
 

@@ -59,6 +59,13 @@ extern "C" {
  *   near_full_slack  a step is "nearly full" when accept >= blk - slack, >= 0 (1)
  *   scan_wgs      launch tuning of lookup_propose only: workgroups per launch,
  *                 0 = automatic.  Results never depend on it.
+ *   scan_balance  launch tuning of the scan (lookup_propose, lookup_decode_step)
+ *                 for ragged batches: 1 = chunks of equal token count, sized on
+ *                 the device from the rows' lengths, so long rows get more
+ *                 workgroups than short ones (B <= LCD_BALANCE_MAX_B; larger
+ *                 batches use equal chunks per row); 0 = every row is cut into
+ *                 the same number of chunks, sized from max_len.  Results never
+ *                 depend on it.
  */
 typedef struct lcd_params {
     int32_t l_min, l_max, k_max;
@@ -66,7 +73,11 @@ typedef struct lcd_params {
     int32_t head_full, head_agree, agree_n, tail_min;
     int32_t entry_steps, sticky, near_full_slack;
     int32_t scan_wgs;
+    int32_t scan_balance;
 } lcd_params;
+
+/* Largest batch the token-balanced scan (scan_balance = 1) handles. */
+#define LCD_BALANCE_MAX_B 1024
 
 /* Per-request scheduler state, caller-owned (device), start at {0,0,0}. */
 typedef struct lcd_sched_state {
@@ -351,14 +362,16 @@ int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, cons
                                int32_t *draft, void *stream, void *ev_start, void *ev_stop);
 
 /*
- * lookup_launch_shape -- host only: the launch shape lookup_propose and
- * lookup_decode_step use for B rows of at most max_len tokens: *cpr
- * workgroups per request, each scanning a chunk of *chunk candidate ends
- * (a multiple of 256).  For measurement (work spread per workgroup).
- * LCD_EINVAL for B <= 0, max_len < 0 or bad params.
+ * lookup_launch_shape -- host only: the launch of the scan for B rows of at
+ * most max_len tokens.  *wgs = workgroups per launch and *chunk = candidate
+ * ends per chunk (a multiple of 256).  With scan_balance = 1 (and B <=
+ * LCD_BALANCE_MAX_B) the chunk length depends on the rows' lengths: pass them
+ * in len_host (host array of B); otherwise len_host may be NULL and every row
+ * is cut into *wgs / B chunks.  For measurement (work spread per workgroup).
+ * LCD_EINVAL for B <= 0, max_len < 0, bad params, or balance without lengths.
  */
-int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, int32_t *cpr,
-                        int32_t *chunk);
+int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, const int32_t *len_host,
+                        int32_t *wgs, int32_t *chunk);
 
 /*
  * lcd_read_probe -- measurement only: a plain streaming read of `bytes`

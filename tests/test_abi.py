@@ -34,6 +34,7 @@ def test_default_params_are_the_articles_values():
     assert (p.n_head, p.n_block) == (7, 15)
     assert (p.head_full, p.head_agree, p.agree_n, p.tail_min) == (8, 6, 2, 4)
     assert (p.entry_steps, p.sticky, p.near_full_slack, p.scan_wgs) == (2, 3, 1, 0)
+    assert p.scan_balance == 0
     assert lcd.check_params(p)
 
 
@@ -42,7 +43,7 @@ def test_default_params_are_the_articles_values():
     dict(n_head=0), dict(n_head=8, n_block=15), dict(n_block=6), dict(n_block=16),
     dict(head_full=0), dict(head_agree=0), dict(agree_n=-1), dict(agree_n=8),
     dict(tail_min=0), dict(entry_steps=0), dict(sticky=-1), dict(near_full_slack=-1),
-    dict(scan_wgs=-1),
+    dict(scan_wgs=-1), dict(scan_balance=2), dict(scan_balance=-1),
 ])
 def test_param_ranges_rejected(bad):
     assert not lcd.check_params(lcd.default_params(**bad))
@@ -245,3 +246,21 @@ def test_index_entry_points_reject_misuse_without_launching():
                                   s) == lcd.LCD_EINVAL
     assert L.lookup_index_propose(None, None, None, 0, pp, 0, None, None, None, None, None, None,
                                   None, s) == lcd.LCD_OK
+
+
+def test_launch_shape_query():
+    """Equal chunks per row without lengths; token-balanced chunks need the
+    rows' lengths (host) and cover every row's candidate ends within the grid."""
+    p = lcd.default_params()
+    assert lcd.launch_shape(64, 25_000, p) == (256, 6400)
+    pb = lcd.default_params(scan_balance=1)
+    with pytest.raises(lcd.LCDError):
+        lcd.launch_shape(256, 262_144, pb)
+    lens = np.array([1024 * (1 + (r % 7)) for r in range(255)] + [262_144], np.int32)
+    wgs, T = lcd.launch_shape(256, 262_144, pb, lens)
+    assert T % 256 == 0
+    chunks = sum(max(1, -(-(int(n) - 1) // T)) for n in lens)
+    assert chunks <= wgs and max(-(-(int(n) - 1) // T) for n in lens) <= 64
+    # over the balanced limit the equal-chunk shape is used
+    big = np.full(1100, 100, np.int32)
+    assert lcd.launch_shape(1100, 100, pb, big) == lcd.launch_shape(1100, 100, p)

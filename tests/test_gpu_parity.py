@@ -406,3 +406,70 @@ def test_decode_replay_report_config3(gpu):
         assert c["tokens_per_step"] == round(t[7] / t[0], 3)
         assert c["long_entries"] == t[5] and c["long_exits"] == t[6]
         assert c["accepted_hist"] == t[9:25].tolist()
+
+
+# ---------------------------------------------------------------------------
+# token-balanced chunks (scan_balance = 1): same results, other launch shape
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [3, 4, 5])
+def test_balanced_scan_configs(gpu, k):
+    lcd = _lcd()
+    w = wl.make_config(k)
+    flat, ro, ln, cap = wl.pack_rows(w.hists)
+    for wgs in (0, 1, 3000):
+        assert_lookup_parity(flat, ro, ln, lcd.default_params(scan_balance=1, scan_wgs=wgs))
+
+
+def test_balanced_scan_stress_and_edges(gpu):
+    """Ragged stress rows, empty and tiny rows, rows longer than max_len, and
+    a batch over the balanced limit (which falls back to equal chunks)."""
+    lcd = _lcd()
+    p = lcd.default_params(scan_balance=1)
+    hs = _stress_batch(seed=17, B=300)
+    flat, ro, ln = wl.pack_csr(hs)
+    assert_lookup_parity(flat, ro, ln, p)
+    assert_lookup_parity(flat, ro, ln, p, max_len=0)          # rows longer than max_len
+    hs2 = [np.zeros(0, np.int32), np.array([1], np.int32)] + [np.full(k, 3, np.int32) for k in range(30)]
+    flat2, ro2, ln2 = wl.pack_csr(hs2)
+    assert_lookup_parity(flat2, ro2, ln2, p)
+    big = _stress_batch(seed=19, B=1100)                      # B > 1024
+    flat3, ro3, ln3 = wl.pack_csr(big)
+    assert_lookup_parity(flat3, ro3, ln3, p)
+
+
+def test_balanced_fused_simulation(gpu):
+    """The fused decode step with token-balanced chunks: 128 steps of config 3
+    equal the oracle's simulation."""
+    lcd = _lcd()
+    from context_lookup_drafting_amd.decode_sim import run_fused
+    from simulate import simulate_oracle
+    w = wl.config3()
+    g = run_fused(w, 128, params=lcd.default_params(scan_balance=1), record=True)
+    g.pop("tele_d")
+    _compare_sims(g, simulate_oracle(w, 128))
+
+
+def test_balanced_fused_step_ragged(gpu):
+    """One fused step over the ragged 256-request batch, both launch modes."""
+    import torch
+    lcd = _lcd()
+    w = wl.config5()
+    flat, ro, ln, cap = wl.pack_rows(w.hists, extra=16)
+    q, tgt = w.step_inputs(np.zeros(w.B, np.int64), 0)
+    outs = []
+    for bal in (0, 1):
+        p = lcd.default_params(scan_balance=bal)
+        dev = torch.device("cuda:0")
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        h_d, ln_d = t(flat), t(ln.copy())
+        dr = lcd.LookupDrafter(w.B, int(ln.max()), dev, p)
+        out = dr.step(h_d, t(ro), ln_d, t(cap), t(q), t(tgt))
+        torch.cuda.synchronize()
+        outs.append([out[k].cpu().numpy() for k in ("match_len", "match_end", "draft", "block",
+                                                    "accept")] + [h_d.cpu().numpy(), ln_d.cpu().numpy()])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    om, oe, od = oracle.lookup_propose(flat, ro, ln, _oparams(lcd.default_params()))
+    np.testing.assert_array_equal(outs[1][0], om)
+    np.testing.assert_array_equal(outs[1][1], oe)
