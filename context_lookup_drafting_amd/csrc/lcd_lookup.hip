@@ -55,11 +55,11 @@
 namespace lcd {
 namespace {
 
-#ifndef LCD_WAVES
-#define LCD_WAVES 4
-#endif
-constexpr int kWaves = LCD_WAVES;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup: 4 in general; 16 (one workgroup per CU, 256 per
+// launch) for batches of 32-128 long rows, where it measured 4-7 % faster.
+constexpr int kWavesSmall = 4;
+constexpr int kWavesLarge = 16;
+constexpr int kNumCUs = 256;
 constexpr int kTileTok = 256;   // 64 lanes x 4 tokens
 #ifndef LCD_UNROLL
 #define LCD_UNROLL 4
@@ -92,6 +92,7 @@ struct ScanArgs {
     int32_t l_min, l_max, k_max;
     int32_t B;                 // requests
     int32_t wgs;               // workgroups per launch (token-balanced chunks)
+    int32_t waves;             // waves per workgroup (kWavesSmall or kWavesLarge)
 };
 
 // Token-balanced chunks (ragged batches): one chunk length for the whole
@@ -396,8 +397,8 @@ __device__ __forceinline__ bool balanced_assignment(const int32_t *__restrict__ 
     return false;
 }
 
-template <int PF, int kMode, bool kBal>
-__global__ void __launch_bounds__(kThreads)
+template <int PF, int kMode, bool kBal, int kWaves>
+__global__ void __launch_bounds__(64 * kWaves)
 lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
                    const int32_t *__restrict__ len, int32_t cpr, int32_t T, ScanArgs a,
                    u64 *__restrict__ ws,
@@ -731,16 +732,16 @@ int32_t chunk_len(int32_t max_len, int cpr) {
     return (int32_t)(T < (int64_t(1) << 30) ? T : (int64_t(1) << 30));
 }
 
-template <int PF, int kMode, bool kBal>
+template <int PF, int kMode, bool kBal, int kW>
 hipError_t launch_one(const int32_t *hist, const int64_t *row_off, const int32_t *len,
                       ScanArgs sa, u64 *ws, int32_t *ml, int32_t *me, int32_t *dr,
                       const StepIO &io, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const dim3 grid((unsigned)(kBal ? (int64_t)sa.wgs : (int64_t)sa.B * sa.cpr));
     if (ev0 != nullptr || ev1 != nullptr)
-        hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kMode, kBal>, grid, dim3(kThreads), 0u, st, ev0,
-                              ev1, 0u, hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
+        hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kMode, kBal, kW>, grid, dim3(64 * kW), 0u, st,
+                              ev0, ev1, 0u, hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
     else
-        hipLaunchKernelGGL((lookup_scan_kernel<PF, kMode, kBal>), grid, dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((lookup_scan_kernel<PF, kMode, kBal, kW>), grid, dim3(64 * kW), 0, st,
                            hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr, io);
     return hipGetLastError();
 }
@@ -751,8 +752,13 @@ hipError_t launch(const int32_t *hist, const int64_t *row_off, const int32_t *le
                   hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     (void)B;
     if (sa.wgs > 0)
-        return launch_one<PF, kMode, true>(hist, row_off, len, sa, ws, ml, me, dr, io, st, ev0, ev1);
-    return launch_one<PF, kMode, false>(hist, row_off, len, sa, ws, ml, me, dr, io, st, ev0, ev1);
+        return launch_one<PF, kMode, true, kWavesSmall>(hist, row_off, len, sa, ws, ml, me, dr, io,
+                                                        st, ev0, ev1);
+    if (sa.waves == kWavesLarge)
+        return launch_one<PF, kMode, false, kWavesLarge>(hist, row_off, len, sa, ws, ml, me, dr, io,
+                                                         st, ev0, ev1);
+    return launch_one<PF, kMode, false, kWavesSmall>(hist, row_off, len, sa, ws, ml, me, dr, io, st,
+                                                     ev0, ev1);
 }
 
 template <int kMode>
@@ -787,9 +793,21 @@ int balanced_wgs(int32_t B, int32_t max_len, int32_t scan_wgs) {
 
 ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
     if (p->scan_balance == 1 && B <= LCD_BALANCE_MAX_B)
-        return ScanArgs{0, 0, p->l_min, p->l_max, p->k_max, B, balanced_wgs(B, max_len, p->scan_wgs)};
+        return ScanArgs{0, 0, p->l_min, p->l_max, p->k_max, B, balanced_wgs(B, max_len, p->scan_wgs),
+                        kWavesSmall};
+    // Batches of 32-128 rows of at least 16k tokens: one 16-wave workgroup per
+    // CU (256 workgroups, equal chunks per row).  Measured on 64 rows of 25k and
+    // 150k tokens: 4 % and 7 % faster than 4-wave workgroups at their best grid.
+    if (p->scan_wgs == 0 && B >= 32 && B <= 128 && max_len >= 16384) {
+        int cpr = (kNumCUs + B / 2) / B;
+        const int most = (max_len + 2047) / 2048;
+        if (cpr > most) cpr = most;
+        if (cpr < 1) cpr = 1;
+        return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max, B, 0,
+                        kWavesLarge};
+    }
     const int cpr = pick_cpr(B, max_len, p->scan_wgs);
-    return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max, B, 0};
+    return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max, B, 0, kWavesSmall};
 }
 
 int propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
