@@ -94,6 +94,7 @@ def load():
         L.rejection_accept_workspace_bytes.restype = ctypes.c_size_t
         L.lookup_launch_shape.argtypes = [i32, i32, pp, P, P, P]
         L.lookup_launch_shape.restype = ctypes.c_int
+        L.lookup_scan_occupancy.argtypes = [i32, P]
         L.lcd_read_probe.argtypes = [P, ctypes.c_int64, i32, P, P, P, P]
         L.lcd_read_probe.restype = ctypes.c_int
         L.lookup_index_plan.argtypes = [P, i32, pp, P, P]
@@ -530,6 +531,13 @@ def launch_shape(B: int, max_len: int, params: Params | None = None, lens=None):
         None if lh is None else lh.ctypes.data_as(ctypes.c_void_p), ctypes.byref(wgs),
         ctypes.byref(chunk)))
     return wgs.value, chunk.value
+
+
+def scan_occupancy(waves: int) -> int:
+    """Workgroups of the `waves`-wave scan kernel (4 or 16) one CU holds at once."""
+    n = ctypes.c_int32()
+    _check("lookup_scan_occupancy", load().lookup_scan_occupancy(ctypes.c_int32(waves), ctypes.byref(n)))
+    return n.value
 
 
 def read_probe(buf, nbytes: int, blocks: int, out, ev_start=None, ev_stop=None):

@@ -60,6 +60,15 @@ namespace {
 constexpr int kWavesSmall = 4;
 constexpr int kWavesLarge = 16;
 constexpr int kNumCUs = 256;
+// 4-wave workgroups of the scan resident on one CU at once, as compiled (35
+// VGPRs and 106 SGPRs per wave: 7 waves per SIMD; lookup_scan_occupancy
+// reports the runtime's figure and the GPU tests hold it to this).  Automatic
+// grids stay within 7 x 256 workgroups: a workgroup beyond them is dispatched
+// only when an earlier one ends, and on ragged batches that put a long row's
+// chunks 12 us behind (256 rows of 1k-262k tokens: 24.2 us at 2048 workgroups,
+// 19.9-20.7 us at 1792).  Forcing 8 waves per SIMD with a launch bound cost
+// more in spilled registers than it gained.
+constexpr int kResidentSmall = 7;
 constexpr int kTileTok = 256;   // 64 lanes x 4 tokens
 #ifndef LCD_UNROLL
 #define LCD_UNROLL 4
@@ -702,7 +711,8 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
 // batch's size bound B x max_len, between 256 and 2048 per launch (1 to 8 per
-// CU), with chunks of at least 2048 and at most 32768 tokens of the longest row.
+// CU), with chunks of at least 2048 and at most 32768 tokens of the longest row,
+// and no more workgroups than are resident at once (kResidentSmall per CU).
 int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
     int64_t cpr;
     if (scan_wgs > 0) {
@@ -715,6 +725,8 @@ int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
         const int64_t least = ((int64_t)max_len + 32767) / 32768;
         if (cpr > most) cpr = most;
         if (cpr < least) cpr = least;
+        const int64_t fit = (int64_t)kResidentSmall * kNumCUs / (B > 0 ? B : 1);
+        if (cpr > fit) cpr = fit;                // one dispatch round
     }
     if (cpr < 1) cpr = 1;
     if (cpr > kMaxCpr) cpr = kMaxCpr;
@@ -774,7 +786,7 @@ hipError_t launch_scan(int pf, const int32_t *hist, const int64_t *row_off, cons
 }
 
 // Workgroups of a token-balanced launch: scan_wgs, or 4 per request within
-// [256, 2048] (on 256 rows of 1k-262k tokens, 4-5 per request measured best:
+// [256, kResidentSmall x 256] (on 256 rows of 1k-262k tokens, 4-5 per request measured best:
 // fewer, larger chunks amortise each workgroup's start and merge), at least 2
 // and at most kMaxCpr per request.
 int balanced_wgs(int32_t B, int32_t max_len, int32_t scan_wgs) {
@@ -784,7 +796,7 @@ int balanced_wgs(int32_t B, int32_t max_len, int32_t scan_wgs) {
         g = scan_wgs;
     } else {
         g = 4 * (int64_t)B;
-        g = g < 256 ? 256 : (g > 2048 ? 2048 : g);
+        g = g < 256 ? 256 : (g > kResidentSmall * kNumCUs ? kResidentSmall * kNumCUs : g);
     }
     if (g < 2 * (int64_t)B) g = 2 * (int64_t)B;
     if (g > (int64_t)kMaxCpr * B) g = (int64_t)kMaxCpr * B;
@@ -882,6 +894,46 @@ extern "C" int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params 
         *wgs = sa.B * sa.cpr;
         *chunk = sa.T;
     }
+    return LCD_OK;
+}
+
+namespace lcd {
+namespace {
+// Fewest workgroups of `kW` waves per CU over the scan's instances (every
+// prefilter width and mode; both chunkings for 4-wave workgroups).
+template <int kW>
+hipError_t min_occupancy(int *out) {
+    int best = 1 << 30;
+    hipError_t err = hipSuccess;
+    auto take = [&](const void *fn) {
+        int n = 0;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * kW, 0);
+        if (e != hipSuccess) err = e;
+        else best = n < best ? n : best;
+    };
+#define LCD_OCC(PF)                                                                          \
+    take(reinterpret_cast<const void *>(&lookup_scan_kernel<PF, kPropose, false, kW>));     \
+    take(reinterpret_cast<const void *>(&lookup_scan_kernel<PF, kStep, false, kW>));        \
+    if constexpr (kW == kWavesSmall) {                                                       \
+        take(reinterpret_cast<const void *>(&lookup_scan_kernel<PF, kPropose, true, kW>));  \
+        take(reinterpret_cast<const void *>(&lookup_scan_kernel<PF, kStep, true, kW>));     \
+    }
+    LCD_OCC(1) LCD_OCC(2) LCD_OCC(3) LCD_OCC(4)
+#undef LCD_OCC
+    *out = best;
+    return err;
+}
+}  // namespace
+}  // namespace lcd
+
+extern "C" int lookup_scan_occupancy(int32_t waves, int32_t *workgroups_per_cu) {
+    if (!workgroups_per_cu || (waves != lcd::kWavesSmall && waves != lcd::kWavesLarge))
+        return LCD_EINVAL;
+    int n = 0;
+    const hipError_t err = waves == lcd::kWavesSmall ? lcd::min_occupancy<lcd::kWavesSmall>(&n)
+                                                     : lcd::min_occupancy<lcd::kWavesLarge>(&n);
+    if (err != hipSuccess) return LCD_EHIP;
+    *workgroups_per_cu = n;
     return LCD_OK;
 }
 

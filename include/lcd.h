@@ -362,6 +362,15 @@ int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, cons
                                int32_t *draft, void *stream, void *ev_start, void *ev_stop);
 
 /*
+ * lookup_scan_occupancy -- diagnostics: workgroups of the scan kernel with
+ * `waves` waves (4 or 16) that one compute unit holds at once, as the runtime
+ * computes it for the compiled kernels (the fewest over their instances).
+ * Automatic launches assume 7 for 4-wave workgroups.  LCD_EINVAL for another
+ * wave count or a NULL output, LCD_EHIP when the runtime cannot answer (no GPU).
+ */
+int lookup_scan_occupancy(int32_t waves, int32_t *workgroups_per_cu);
+
+/*
  * lookup_launch_shape -- host only: the launch of the scan for B rows of at
  * most max_len tokens.  *wgs = workgroups per launch and *chunk = candidate
  * ends per chunk (a multiple of 256).  With scan_balance = 1 (and B <=

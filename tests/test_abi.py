@@ -264,3 +264,20 @@ def test_launch_shape_query():
     # over the balanced limit the equal-chunk shape is used
     big = np.full(1100, 100, np.int32)
     assert lcd.launch_shape(1100, 100, pb, big) == lcd.launch_shape(1100, 100, p)
+
+
+def test_automatic_grids_fit_one_dispatch_round():
+    """Automatic grids of 4-wave workgroups stay within the 7 x 256 that are
+    resident at once (the GPU tests check the 7 against the runtime): 256 rows
+    of up to 262k tokens get 7 chunks per row, not 8; explicit scan_wgs and
+    one-chunk-per-row batches are left alone."""
+    p = lcd.default_params()
+    assert lcd.launch_shape(256, 262_144, p)[0] == 1792
+    for B, n in ((200, 262_144), (300, 150_000), (512, 100_000), (1024, 1 << 20)):
+        assert lcd.launch_shape(B, n, p)[0] <= max(1792, B)
+    assert lcd.launch_shape(256, 262_144, lcd.default_params(scan_wgs=2048))[0] == 2048
+    assert lcd.launch_shape(2000, 262_144, p)[0] == 2000
+    pb = lcd.default_params(scan_balance=1)
+    assert lcd.launch_shape(512, 4096, pb, np.full(512, 4096, np.int32))[0] == 1792
+    with pytest.raises(lcd.LCDError):
+        lcd.scan_occupancy(8)

@@ -231,6 +231,18 @@ def test_launch_shapes_do_not_change_results(gpu, wgs):
     assert_lookup_parity(flat, ro, ln, lcd.default_params(scan_wgs=wgs), max_len=0)
 
 
+def test_automatic_grid_is_resident(gpu):
+    """The automatic launch rule assumes 7 resident 4-wave workgroups per CU on
+    a 256-CU part; the runtime's occupancy for the compiled kernels must allow
+    at least that (a kernel change that costs registers would break it)."""
+    import torch
+    lcd = _lcd()
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
+    assert lcd.scan_occupancy(4) >= 7
+    assert lcd.scan_occupancy(16) >= 1
+    assert lcd.launch_shape(256, 262_144)[0] <= lcd.scan_occupancy(4) * 256
+
+
 def test_match_across_workgroup_boundaries(gpu):
     """Rows split over many workgroups with the winning occurrence straddling
     range boundaries at every offset."""
