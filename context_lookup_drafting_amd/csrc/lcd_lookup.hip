@@ -34,11 +34,12 @@
 //  * A packed key (length, end) orders candidates.  Every workgroup of a
 //    request takes an arrival ticket when it starts (one atomic add, in flight
 //    during its scan), and at the end publishes its best key together with the
-//    15 tokens that follow that match (read back while they are still in its
-//    cache) as tagged 8-byte words in its own workspace slot.  The workgroup
-//    holding the last ticket gathers the slots -- it only waits for
-//    workgroups that started before it, so the wait always ends -- and thus
-//    has the winning draft without another dependent load.  It finishes the
+//    15 tokens that follow that match (loaded by the wave that found it, when
+//    it found it, so no load follows the scan) as tagged 8-byte words in its
+//    own workspace slot.  The workgroup holding the last ticket gathers the
+//    slots -- it only waits for workgroups that started before it, so the
+//    wait always ends -- and thus has the winning draft without another
+//    dependent load.  It finishes the
 //    request with one wave (draft copy and, in the decode step, fusion,
 //    acceptance, append and scheduler update) and re-zeroes the workspace.
 //
@@ -415,6 +416,7 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
                    int32_t *__restrict__ draft, StepIO io)
 {
     __shared__ u64 s_wkey[kWaves];
+    __shared__ int s_wtok[kWaves * kSlotWords];
     __shared__ u64 s_units[kMaxCpr * kSlotWords];
 
     const int tid = threadIdx.x;
@@ -472,6 +474,10 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     }
 
     u64 best = 0;                     // this wave's best key over its chunks
+    // lane k < 15: h[e+1+min(k, D-1)], the tokens following the best match
+    // (e its end, D = n-1-e); loaded when the match is found, so the load is
+    // off the path that follows the scan
+    int btok = 0;
     // One chunk per workgroup when every row fits in cpr chunks of T; a longer
     // row is covered by letting each workgroup take every cpr-th chunk.
     for (int ch = c0; ch < contrib; ch += cpr) {
@@ -622,7 +628,11 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
                             }
                             const int64_t e_abs = X0 + kTileTok * (int64_t)kt + ebest;
                             const u64 key = ((u64)L << kLenShift) | (u64)(uint32_t)(e_abs - ro);
-                            best = key > best ? key : best;
+                            if (key > best) {
+                                best = key;
+                                const int D = nc - (int)(e_abs - ro);     // n-1-e >= 1
+                                btok = hist[e_abs + 1 + (lane < D ? lane : D - 1)];
+                            }
                         }
                     }
                 }
@@ -653,18 +663,20 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     }
 
     if (lane == 0) s_wkey[wave] = best;
+    if (lane < kSlotWords) s_wtok[wave * kSlotWords + lane] = btok;
     __syncthreads();
     if (wave != 0) return;
+    // the workgroup's best key and the tokens its wave staged (lanes 0..14)
     u64 key = s_wkey[0];
+    int wbest = 0;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) key = s_wkey[w] > key ? s_wkey[w] : key;
-    // the tokens following this workgroup's best match, lane k: h[e+1+min(k, D-1)]
-    int tok = 0;
-    if (key != 0) {
-        const int e = (int)(key & kEndMask);
-        const int D = nc - e;                                  // n-1-e >= 1
-        tok = hist[ro + e + 1 + (lane < D ? lane : D - 1)];
+    for (int w = 1; w < kWaves; ++w) {
+        if (s_wkey[w] > key) {
+            key = s_wkey[w];
+            wbest = w;
+        }
     }
+    int tok = s_wtok[wbest * kSlotWords + (lane < kSlotWords ? lane : 0)];
     if (P > 1) {
         u64 *__restrict__ slots = req + 2;
         const int my_ticket = uni((int)ticket);    // lane 0 took it (P > 1)
@@ -678,7 +690,7 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
         }
         // Last to start: every other workgroup taking part has started, and
         // publishes without waiting for anything, so the gathering ends.  Its
-        // own key and tokens stay in registers (their load overlaps the polls).
+        // own key and tokens stay in registers.
         const int nu = P * kSlotWords;
         bool all = false;
         for (int tries = 0; tries < kPollMax && !all; ++tries) {
@@ -692,19 +704,31 @@ lookup_scan_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
             }
             all = ballot(!ok) == 0;
         }
-        // re-zero the request's workspace for the next call
-        for (int u = lane; u < nu; u += 64)
-            __hip_atomic_store(slots + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // best key over the slots (keys of different slots differ unless zero)
+        // best key over the slots (keys of different slots differ unless zero):
+        // a scalar pass over the P slot keys, which are few (a 64-bit wave-wide
+        // shuffle reduction is six dependent LDS round trips)
         const u64 ks = lane >= P ? 0
                        : lane == c0 ? key
                                     : (s_units[lane * kSlotWords + kSlotWords - 1] & ~kKeyValid);
-        const u64 kbest = wave_max(ks);
-        const u64 at = ballot(lane < P && ks == kbest);
-        const int w = at ? (int)__builtin_ctzll(at) : c0;
+        u64 kbest = 0;
+        int w = c0;
+        for (int j = 0; j < P; ++j) {
+            const u64 kj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(ks >> 32), j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ks, j);
+            if (kj > kbest) { kbest = kj; w = j; }
+        }
+        if (kbest == 0) w = c0;
         if (w != c0) tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
         key = all ? kbest : 0;                      // gathering gave up: report no match
+        finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, match_len, match_end,
+                              draft, io);
+        // Re-zero the request's workspace for the next call, after the
+        // outputs: a wait for these stores' acknowledgement must not sit in
+        // front of the finish.
+        for (int u = lane; u < nu; u += 64)
+            __hip_atomic_store(slots + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
     finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, match_len, match_end, draft, io);
 }
