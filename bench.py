@@ -489,9 +489,11 @@ INDEX_METRIC = "history tokens served/s by the incremental-index lookup (decode 
 
 
 def bench_index(args):
-    """Decode steps through lookup_index_propose, fuse_verify_block,
+    """Decode steps through lookup_index_decode_step (one kernel: the lookup
+    from the index, fusion, greedy acceptance with the append, scheduler), or
+    with --separate through lookup_index_propose, fuse_verify_block,
     greedy_accept (appending) and lookup_schedule_step: the histories grow
-    every step and each propose indexes what the previous step appended.  The
+    every step and each lookup indexes what the previous step appended.  The
     index is built once from the prompts (timed apart)."""
     import numpy as np
     import torch
@@ -530,6 +532,10 @@ def bench_index(args):
     build_ms = b0.elapsed_time(b1)
 
     def step(i, ev=None):
+        if not args.separate:
+            idx.decode_step(h_d, ro_d, ln_d, cap_d, q_d, tgt_d, state, m, e, d, blk, bl, acc,
+                            longs[(i + 1) % 2], True, events=ev)
+            return
         idx.propose(h_d, ro_d, ln_d, m, e, d, events=ev)
         lcd.fuse_verify_block(d, m, q_d, longs[i % 2], blk, bl, p)
         lcd.greedy_accept(blk, bl, tgt_d, acc, hist=h_d, row_off=ro_d, lens=ln_d, cap=cap_d)
@@ -574,8 +580,12 @@ def bench_index(args):
     nL = p.l_max - p.l_min + 1
     # per request: suffix and row metadata (48 + 24), per appended token its
     # token and nL table read-modify-writes (4 + 16 nL), nL probes (8 nL), the
-    # verified tokens (48), the draft and match outputs (68)
+    # verified tokens (48), the draft and match outputs (68); the one-kernel
+    # step also moves the rest of the step's per-request bytes (268 - 80), and
+    # writes the appended tokens
     alg = int(B * (72 + appended * (4 + 16 * nL) + 8 * nL + 48 + 68))
+    if not args.separate:
+        alg += int(B * (per_request_bytes(False) - per_request_bytes(True) + 4 * appended))
     tokens = (len0 + len1) / 2
     value = steps_run * tokens / elapsed
     out = {
@@ -596,7 +606,9 @@ def bench_index(args):
             "batch": B,
             "tokens_per_step_mean": round(tokens, 1),
             "appended_per_request_step": round(appended, 3),
-            "launch": f"HIP graph of {R} steps, 4 entry points per step, lookup from the index",
+            "launch": (f"HIP graph of {R} steps, lookup from the index, "
+                       + ("4 entry points per step" if args.separate
+                          else "lookup_index_decode_step (1 kernel) per step")),
             "index_build_ms": round(build_ms, 3),
             "index_table_bytes": idx.table_bytes,
         },
@@ -608,7 +620,8 @@ def bench_index(args):
             "unit": "GB/s",
             "frac": round(alg / k_avg / 1e9 / HBM_PEAK_GBPS, 6),
             "traffic": None,
-            "kernel": "index_propose_kernel",
+            "kernel": ("index_propose_kernel<lookup only>" if args.separate
+                       else "index_propose_kernel<whole step>"),
             "kernel_us_mean": round(k_avg * 1e6, 3),
             "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, x)) * 1e6, 3)
                                       for x in (10, 50, 90)],

@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
                    model_mask=None, model_probs=None, hist=None, row_off=None, lens=None, cap=None)
   LookupIndex(cap, device, params).build(hist, row_off, lens, max_len)
   LookupIndex.propose(hist, row_off, lens, match_len, match_end, draft)
+  LookupIndex.decode_step(hist, row_off, lens, cap, model_draft, target, state, match_len,
+                          match_end, draft, block, block_len, accept, long_next, append, telemetry)
                                           (lookup_index_plan / _build / _propose)
   lookup_schedule_step(state, match_len, accept, block_len, long_next, params)
 """
@@ -102,6 +104,9 @@ def load():
         L.lookup_index_build.argtypes = [P, P, P, i32, pp, i32, P, P, P, ctypes.c_size_t, P, P, i32, P]
         L.lookup_index_propose.argtypes = [P, P, P, i32, pp, i32, P, P, P, P, P, P, P, P]
         L.lookup_index_propose_timed.argtypes = [P, P, P, i32, pp, i32, P, P, P, P, P, P, P, P, P, P]
+        idec = [P, P, P, P, i32, pp, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, i32, P]
+        L.lookup_index_decode_step.argtypes = idec
+        L.lookup_index_decode_step_timed.argtypes = idec + [P, P]
         rej = [P, P, P, P, P, i32, P, P, i32, i32, P, ctypes.c_size_t, P, P, P, P, P, P, P]
         L.rejection_accept.argtypes = rej
         L.rejection_accept_timed.argtypes = rej + [P, P]
@@ -109,7 +114,8 @@ def load():
                   L.greedy_accept, L.lookup_schedule_step, L.lookup_decode_step,
                   L.lookup_decode_step_timed, L.lookup_telemetry_update,
                   L.lookup_telemetry_reduce, L.rejection_accept, L.rejection_accept_timed,
-                  L.lookup_index_build, L.lookup_index_propose, L.lookup_index_propose_timed):
+                  L.lookup_index_build, L.lookup_index_propose, L.lookup_index_propose_timed,
+                  L.lookup_index_decode_step, L.lookup_index_decode_step_timed):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -517,6 +523,43 @@ class LookupIndex:
             _dev(match_len, "match_len", torch.int32, B, dev),
             _dev(match_end, "match_end", torch.int32, B, dev),
             _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev), _stream(dev), *extra))
+
+    def decode_step(self, hist, row_off, lens, cap, model_draft, target, state, match_len,
+                    match_end, draft, block, block_len, accept, long_next=None, append=True,
+                    telemetry=None, events=None):
+        """One whole decode step through the index in one kernel
+        (lookup_index_decode_step): the outputs of decode_step's four calls.
+        ``events`` as for propose."""
+        import torch
+        B, dev = self.B, self.device
+        L = load()
+        fn = L.lookup_index_decode_step if events is None else L.lookup_index_decode_step_timed
+        extra = () if events is None else (ctypes.c_void_p(events[0] or None),
+                                           ctypes.c_void_p(events[1] or None))
+        nul = ctypes.c_void_p(None)
+        _check("lookup_index_decode_step", fn(
+            _dev(hist, "hist", torch.int32, device=dev),
+            _dev(row_off, "row_off", torch.int64, B, dev),
+            _dev(lens, "lens", torch.int32, B, dev),
+            _dev(cap, "cap", torch.int32, B, dev) if cap is not None else nul,
+            ctypes.c_int32(B), ctypes.byref(self.p), ctypes.c_int32(self.fp_bits),
+            _dev(self.table_off, "table_off", torch.int64, B, dev),
+            _dev(self.table_bits, "table_bits", torch.int32, B, dev),
+            ctypes.c_void_p(self.tables.data_ptr()),
+            _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
+            _dev(model_draft, "model_draft", torch.int32, B * Q_STRIDE, dev),
+            _dev(target, "target", torch.int32, B * TARGET_STRIDE, dev),
+            _dev(state, "state", torch.int32, 3 * B, dev),
+            _dev(match_len, "match_len", torch.int32, B, dev),
+            _dev(match_end, "match_end", torch.int32, B, dev),
+            _dev(draft, "draft", torch.int32, B * DRAFT_STRIDE, dev),
+            _dev(block, "block", torch.int32, B * DRAFT_STRIDE, dev),
+            _dev(block_len, "block_len", torch.int32, B, dev),
+            _dev(accept, "accept", torch.int32, B, dev),
+            _dev(long_next, "long_next", torch.int32, B, dev) if long_next is not None else nul,
+            (_dev(telemetry, "telemetry", torch.int32, B * TELE_WORDS, dev)
+             if telemetry is not None else nul),
+            ctypes.c_int32(1 if append else 0), _stream(dev), *extra))
 
 
 def launch_shape(B: int, max_len: int, params: Params | None = None, lens=None):

@@ -32,12 +32,18 @@
 // L = l_min + k) and the hits verified; the answer is the better of the two.
 // About five dependent memory round trips per step, whatever the history
 // length.
+//
+// lookup_index_decode_step: the same kernel, whose wave then also does the
+// rest of the decode step for its request (fusion, greedy acceptance with the
+// append, scheduler, telemetry; lcd_finish.h), so a decode step through the
+// index is one launch.  The step inputs are loaded when the wave starts.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "lcd.h"
+#include "lcd_finish.h"
 
 namespace lcd {
 namespace {
@@ -128,16 +134,23 @@ __device__ u64 exact_scan(const int32_t *__restrict__ h, int n, const IndexArgs 
     return best;
 }
 
+// kStep: the wave also finishes its request's decode step (io).
+template <bool kStep>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 index_propose_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
                      const int32_t *__restrict__ len, int32_t B, IndexArgs a,
                      const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_bits,
                      u64 *__restrict__ tables, int32_t *__restrict__ indexed_len,
                      int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
-                     int32_t *__restrict__ draft) {
+                     int32_t *__restrict__ draft, StepIO io) {
     const int lane = threadIdx.x & 63;
     const int r = uni(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
     if (r >= B) return;
+    // the rest of the step's inputs, in flight during the lookup
+    const int sin = kStep ? load_step_input(r, lane, io) : 0;
+    uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
+    if (kStep && io.tele != nullptr)
+        tin = io.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
     const int32_t n0 = len[r];
     const int n = n0 > 0 ? n0 : 0;
     const int64_t ro = row_off[r];
@@ -282,18 +295,17 @@ index_propose_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict
     // ---- match and LZ draft ------------------------------------------------
     const int m = (int)(key >> 31);
     const int e = key != 0 ? (int)(key & 0x7FFFFFFFull) : -1;
-    if (lane < LCD_DRAFT_STRIDE) {
-        int d = LCD_PAD;
-        if (m > 0 && lane < a.k_max) {
-            const int D = n - 1 - e;                                  // >= 1
-            d = h[e + 1 + lane % D];
-        }
-        draft[(int64_t)r * LCD_DRAFT_STRIDE + lane] = d;
+    int d = LCD_PAD;                          // lane k < 15: draft slot k
+    if (lane < LCD_DRAFT_STRIDE && m > 0 && lane < a.k_max) {
+        const int D = n - 1 - e;                                      // >= 1
+        d = h[e + 1 + lane % D];
     }
+    if (lane < LCD_DRAFT_STRIDE) draft[(int64_t)r * LCD_DRAFT_STRIDE + lane] = d;
     if (lane == 0) {
         match_len[r] = m;
         match_end[r] = e;
     }
+    if (kStep) finish_step(r, m, d, sin, tin, lane, ro, n, io);
 }
 
 // Build: clear the tables, then insert every position p <= n-2 of every row.
@@ -419,6 +431,35 @@ extern "C" int lookup_index_build(const int32_t *hist, const int64_t *row_off, c
 
 namespace lcd {
 namespace {
+template <bool kStep>
+int index_launch(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
+                 const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
+                 const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                 int32_t *match_len, int32_t *match_end, int32_t *draft, const StepIO &io,
+                 void *stream, void *ev0, void *ev1) {
+    const IndexArgs a = index_args(p, fp_bits);
+    const dim3 grid((unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (ev0 != nullptr || ev1 != nullptr)
+        hipExtLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(64 * kWavesPerBlock), 0u, st,
+                              reinterpret_cast<hipEvent_t>(ev0), reinterpret_cast<hipEvent_t>(ev1),
+                              0u, hist, row_off, len, B, a, table_off, table_bits,
+                              static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft,
+                              io);
+    else
+        hipLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(64 * kWavesPerBlock), 0, st, hist,
+                           row_off, len, B, a, table_off, table_bits, static_cast<u64 *>(tables),
+                           indexed_len, match_len, match_end, draft, io);
+    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+}
+
+bool index_args_ok(const void *hist, const void *row_off, const void *len, const void *table_off,
+                   const void *table_bits, const void *tables, const void *indexed_len,
+                   const void *match_len, const void *match_end, const void *draft) {
+    return hist && row_off && len && table_off && table_bits && tables && indexed_len && match_len &&
+           match_end && draft && (reinterpret_cast<uintptr_t>(tables) & 7) == 0;
+}
+
 int index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
                   const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
                   const int32_t *table_bits, void *tables, int32_t *indexed_len,
@@ -426,22 +467,31 @@ int index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *le
                   void *ev0, void *ev1) {
     if (B < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
-    if (!hist || !row_off || !len || !table_off || !table_bits || !tables || !indexed_len ||
-        !match_len || !match_end || !draft || (reinterpret_cast<uintptr_t>(tables) & 7) != 0)
+    if (!index_args_ok(hist, row_off, len, table_off, table_bits, tables, indexed_len, match_len,
+                       match_end, draft))
         return LCD_EINVAL;
-    const IndexArgs a = index_args(p, fp_bits);
-    const dim3 grid((unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock));
-    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (ev0 != nullptr || ev1 != nullptr)
-        hipExtLaunchKernelGGL(index_propose_kernel, grid, dim3(64 * kWavesPerBlock), 0u, st,
-                              reinterpret_cast<hipEvent_t>(ev0), reinterpret_cast<hipEvent_t>(ev1),
-                              0u, hist, row_off, len, B, a, table_off, table_bits,
-                              static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft);
-    else
-        hipLaunchKernelGGL(index_propose_kernel, grid, dim3(64 * kWavesPerBlock), 0, st, hist,
-                           row_off, len, B, a, table_off, table_bits, static_cast<u64 *>(tables),
-                           indexed_len, match_len, match_end, draft);
-    return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
+    return index_launch<false>(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+                               indexed_len, match_len, match_end, draft, StepIO{}, stream, ev0, ev1);
+}
+
+int index_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap, int32_t B,
+               const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
+               const int32_t *table_bits, void *tables, int32_t *indexed_len,
+               const int32_t *model_draft, const int32_t *target, lcd_sched_state *state,
+               int32_t *match_len, int32_t *match_end, int32_t *draft, int32_t *block,
+               int32_t *block_len, int32_t *accept, int32_t *long_next, uint32_t *tele,
+               int32_t append, void *stream, void *ev0, void *ev1) {
+    if (B < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
+    if (B == 0) return LCD_OK;
+    if (!index_args_ok(hist, row_off, len, table_off, table_bits, tables, indexed_len, match_len,
+                       match_end, draft))
+        return LCD_EINVAL;
+    if (!model_draft || !target || !state || !block || !block_len || !accept) return LCD_EINVAL;
+    if (append && !cap) return LCD_EINVAL;
+    const StepIO io{hist, len, cap, model_draft, target, state, block, block_len, accept, long_next,
+                    tele, fuse_args(p), sched_args(p), append ? 1 : 0};
+    return index_launch<true>(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+                              indexed_len, match_len, match_end, draft, io, stream, ev0, ev1);
 }
 }  // namespace
 }  // namespace lcd
@@ -464,4 +514,33 @@ extern "C" int lookup_index_propose_timed(const int32_t *hist, const int64_t *ro
                                           void *ev_start, void *ev_stop) {
     return lcd::index_propose(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
                               indexed_len, match_len, match_end, draft, stream, ev_start, ev_stop);
+}
+
+extern "C" int lookup_index_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len,
+                                        const int32_t *cap, int32_t B, const lcd_params *p,
+                                        int32_t fp_bits, const int64_t *table_off,
+                                        const int32_t *table_bits, void *tables,
+                                        int32_t *indexed_len, const int32_t *model_draft,
+                                        const int32_t *target, lcd_sched_state *state,
+                                        int32_t *match_len, int32_t *match_end, int32_t *draft,
+                                        int32_t *block, int32_t *block_len, int32_t *accept,
+                                        int32_t *long_next, uint32_t *telemetry, int32_t append,
+                                        void *stream) {
+    return lcd::index_step(hist, row_off, len, cap, B, p, fp_bits, table_off, table_bits, tables,
+                           indexed_len, model_draft, target, state, match_len, match_end, draft,
+                           block, block_len, accept, long_next, telemetry, append, stream, nullptr,
+                           nullptr);
+}
+
+extern "C" int lookup_index_decode_step_timed(
+    int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap, int32_t B,
+    const lcd_params *p, int32_t fp_bits, const int64_t *table_off, const int32_t *table_bits,
+    void *tables, int32_t *indexed_len, const int32_t *model_draft, const int32_t *target,
+    lcd_sched_state *state, int32_t *match_len, int32_t *match_end, int32_t *draft, int32_t *block,
+    int32_t *block_len, int32_t *accept, int32_t *long_next, uint32_t *telemetry, int32_t append,
+    void *stream, void *ev_start, void *ev_stop) {
+    return lcd::index_step(hist, row_off, len, cap, B, p, fp_bits, table_off, table_bits, tables,
+                           indexed_len, model_draft, target, state, match_len, match_end, draft,
+                           block, block_len, accept, long_next, telemetry, append, stream, ev_start,
+                           ev_stop);
 }

@@ -77,11 +77,18 @@ class LookupDrafter:
         return self.block, self.block_len
 
     # -- whole greedy step ---------------------------------------------------
-    def step(self, hist, row_off, lens, cap, model_draft, target, append: bool = True):
+    def step(self, hist, row_off, lens, cap, model_draft, target, append: bool = True,
+             separate: bool = False):
         """One greedy decode step in one kernel (lookup, fusion, acceptance,
-        append, scheduler update; telemetry when enabled).  With the index,
-        the lookup comes from the index and the rest runs as separate calls."""
-        if self.index is not None:
+        append, scheduler update; telemetry when enabled): lookup_decode_step,
+        or lookup_index_decode_step with the index.  ``separate`` runs the
+        index path as its four entry points instead (same outputs)."""
+        if self.index is not None and not separate:
+            self.index.decode_step(hist, row_off, lens, cap, model_draft, target, self.state,
+                                   self.match_len, self.match_end, self.draft, self.block,
+                                   self.block_len, self.accept, self.long_next, append,
+                                   telemetry=self.telemetry)
+        elif self.index is not None:
             from . import greedy_accept, lookup_schedule_step, telemetry_update
             self.propose(hist, row_off, lens)
             long_used = self.state[:, 0].clone()

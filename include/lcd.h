@@ -362,6 +362,50 @@ int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, cons
                                int32_t *draft, void *stream, void *ev_start, void *ev_stop);
 
 /*
+ * lookup_index_decode_step -- one whole decode step through the index:
+ * lookup_index_propose, then fuse_verify_block under each request's current
+ * mode state[r].long_mode, then greedy_accept (appending the emitted tokens
+ * when `append` is non-zero), then lookup_schedule_step; every output equals
+ * what those four calls produce in that order, and what lookup_decode_step
+ * produces.  (Article sections "第 1 步" to "第 3 步" and the paragraph on
+ * losslessness; the forum thread's reply on keeping the lookup index
+ * incremental.)  One launch, one wave per request: the wave that answers a
+ * request's lookup also fuses, accepts, appends and schedules it.  The
+ * appended tokens are indexed by the next call, as lookup_index_propose does
+ * for any growth of the histories between calls.
+ *
+ * hist, row_off, len, cap   as for lookup_decode_step; hist rows must be padded
+ *                           (row_off[r] + cap[r] <= row_off[r+1]) when appending
+ * p, fp_bits, table_off, table_bits, tables, indexed_len
+ *                           as for lookup_index_propose (the same index)
+ * model_draft, target, state, outputs, telemetry, append
+ *                           as for lookup_decode_step
+ * Errors: LCD_EINVAL for the misuse lookup_index_propose rejects, a NULL
+ * model_draft, target, state, block, block_len or accept, or append != 0 with a
+ * NULL cap; LCD_EHIP on a launch failure.  B = 0 is a no-op.  No allocation.
+ */
+int lookup_index_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len,
+                             const int32_t *cap, int32_t B, const lcd_params *p, int32_t fp_bits,
+                             const int64_t *table_off, const int32_t *table_bits, void *tables,
+                             int32_t *indexed_len, const int32_t *model_draft,
+                             const int32_t *target, lcd_sched_state *state, int32_t *match_len,
+                             int32_t *match_end, int32_t *draft, int32_t *block,
+                             int32_t *block_len, int32_t *accept, int32_t *long_next,
+                             uint32_t *telemetry, int32_t append, void *stream);
+
+/* lookup_index_decode_step with GPU-stamped events around its kernel (see
+ * lookup_propose_timed); for profiling only. */
+int lookup_index_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len,
+                                   const int32_t *cap, int32_t B, const lcd_params *p,
+                                   int32_t fp_bits, const int64_t *table_off,
+                                   const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                                   const int32_t *model_draft, const int32_t *target,
+                                   lcd_sched_state *state, int32_t *match_len, int32_t *match_end,
+                                   int32_t *draft, int32_t *block, int32_t *block_len,
+                                   int32_t *accept, int32_t *long_next, uint32_t *telemetry,
+                                   int32_t append, void *stream, void *ev_start, void *ev_stop);
+
+/*
  * lookup_scan_occupancy -- diagnostics: workgroups of the scan kernel with
  * `waves` waves (4 or 16) that one compute unit holds at once, as the runtime
  * computes it for the compiled kernels (the fewest over their instances).

@@ -123,3 +123,47 @@ def simulate_gpu_fused(w: Workload, steps: int, params=None, record: bool = True
     res = run_fused(w, steps, params, device, record)
     res.pop("tele_d")
     return res
+
+
+def simulate_gpu_index_fused(w: Workload, steps: int, params=None, record: bool = True,
+                             device="cuda:0", fp_bits: int = 0):
+    """The decode loop through lookup_index_decode_step: one kernel per step,
+    the lookup answered from the index (built once from the prompts) and the
+    step's appended tokens indexed by the next call."""
+    import torch
+    import context_lookup_drafting_amd as lcd
+    params = params or lcd.default_params()
+    flat, row_off, lens, cap = pack_rows(w.hists, extra=_extra(steps))
+    B = w.B
+    dev = torch.device(device)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    h_d, ro_d, len_d, cap_d = t(flat), t(row_off), t(lens.copy()), t(cap)
+    state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
+    mk = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
+    m, e, d, block, bl, acc, long_next = mk(B), mk(B), mk(B, 15), mk(B, 15), mk(B), mk(B), mk(B)
+    tele = lcd.alloc_telemetry(B, dev)
+    max_len = int(lens.max()) + _extra(steps) if B else 0
+    idx = lcd.LookupIndex(cap, dev, params, fp_bits=fp_bits)
+    idx.build(h_d, ro_d, len_d, max_len)
+    pos = np.zeros(B, np.int64)
+    recs = []
+    emitted = [[] for _ in range(B)]
+    for step in range(steps):
+        q, tgt = w.step_inputs(pos, step)
+        long_used = state[:, 0].clone()
+        idx.decode_step(h_d, ro_d, len_d, cap_d, t(q), t(tgt), state, m, e, d, block, bl, acc,
+                        long_next, True, telemetry=tele)
+        acc_h = acc.cpu().numpy()
+        for r in range(B):
+            if acc_h[r] >= 0:
+                emitted[r].extend(tgt[r, :acc_h[r] + 1].tolist())
+        pos = pos + np.maximum(acc_h, 0) + 1
+        if record:
+            recs.append(dict(m=m.cpu().numpy(), e=e.cpu().numpy(), d=d.cpu().numpy(), q=q,
+                             tgt=tgt, long=long_used.cpu().numpy(), block=block.cpu().numpy(),
+                             blk=bl.cpu().numpy(), acc=acc_h, state=state.cpu().numpy(),
+                             long_next=long_next.cpu().numpy()))
+    torch.cuda.synchronize()
+    return dict(recs=recs, emitted=emitted, lens=len_d.cpu().numpy(), flat=h_d.cpu().numpy(),
+                row_off=row_off, tele=tele.cpu().numpy().view(np.uint32),
+                indexed_len=idx.indexed_len.cpu().numpy())

@@ -246,6 +246,26 @@ def test_index_entry_points_reject_misuse_without_launching():
                                   s) == lcd.LCD_EINVAL
     assert L.lookup_index_propose(None, None, None, 0, pp, 0, None, None, None, None, None, None,
                                   None, s) == lcd.LCD_OK
+    # the whole step through the index: the propose checks plus the step's own
+    # (hist, row_off, len, cap, B, p, fp_bits, table_off, table_bits, tables,
+    #  indexed_len, model_draft, target, state, match_len, match_end, draft,
+    #  block, block_len, accept, long_next, telemetry, append, stream)
+    step = lambda *a: L.lookup_index_decode_step(*a)
+    ok = [f, f, f, f, 3, pp, 0, f, f, f, f, f, f, f, f, f, f, f, f, f, None, None, 1, s]
+    for i, v in ((6, 32), (9, _P(0x1004)), (10, None), (11, None), (12, None), (13, None),
+                 (17, None), (18, None), (19, None), (3, None)):
+        args = list(ok)
+        args[i] = v
+        assert step(*args) == lcd.LCD_EINVAL, i
+    args = list(ok)
+    args[5] = ctypes.byref(bad)
+    assert step(*args) == lcd.LCD_EINVAL
+    args = list(ok)
+    args[4] = -1
+    assert step(*args) == lcd.LCD_EINVAL
+    args = [None] * 24
+    args[4], args[5], args[6], args[22] = 0, pp, 0, 1
+    assert step(*args) == lcd.LCD_OK                  # B = 0: nothing to do
 
 
 def test_launch_shape_query():

@@ -1,0 +1,144 @@
+"""Parity of lookup_index_decode_step (the whole decode step through the
+incremental index, one kernel) with the CPU oracle: every output of the step
+(lookup, draft, fused block, accept, append, scheduler, telemetry) bit-exact,
+per step, over whole simulated decodes and single-step batches, including
+failed appends, CSR rows without room, stale rows and fingerprint
+collisions."""
+
+import numpy as np
+import pytest
+
+import oracle
+from context_lookup_drafting_amd import workloads as wl
+from test_gpu_parity import _compare_sims, _oparams, _stress_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _index_single_step(hists, q, tgt, long0, params=None, append=False, packed="rows", extra=16,
+                       fp_bits=0, shrink=0):
+    """One lookup_index_decode_step after building the index; ``shrink`` > 0
+    shortens every row by that many tokens after the build (stale rows, which
+    the kernel answers by an exact scan)."""
+    import torch
+    import context_lookup_drafting_amd as lcd
+    p = params or lcd.default_params()
+    if packed == "rows":
+        flat, ro, ln, cap = wl.pack_rows(hists, extra=extra)
+    else:
+        flat, ro, ln = wl.pack_csr(hists)
+        cap = ln.copy()
+    B = len(ln)
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    h_d, ro_d, ln_d, cap_d = t(flat), t(ro), t(ln.copy()), t(cap)
+    idx = lcd.LookupIndex(cap, dev, p, fp_bits=fp_bits)
+    idx.build(h_d, ro_d, ln_d, int(ln.max()) if B else 0)
+    if shrink:
+        ln = np.maximum(ln - shrink, 0).astype(np.int32)
+        ln_d = t(ln.copy())
+    state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
+    state[:, 0] = t(long0)
+    outs = [torch.full((B,), 77, dtype=torch.int32, device=dev) for _ in range(5)]
+    d = torch.full((B, 15), 77, dtype=torch.int32, device=dev)
+    blk = torch.full((B, 15), 77, dtype=torch.int32, device=dev)
+    tele = lcd.alloc_telemetry(B, dev)
+    idx.decode_step(h_d, ro_d, ln_d, cap_d if append else None, t(q), t(tgt), state, outs[0],
+                    outs[1], d, blk, outs[2], outs[3], outs[4], append, telemetry=tele)
+    torch.cuda.synchronize()
+    got = dict(m=outs[0], e=outs[1], d=d, block=blk, blk=outs[2], acc=outs[3], ln=outs[4],
+               state=state, lens=ln_d, flat=h_d, tele=tele)
+    got = {k: v.cpu().numpy() for k, v in got.items()}
+    got["tele"] = got["tele"].view(np.uint32)
+
+    op = _oparams(p)
+    om, oe, od = oracle.lookup_propose(flat, ro, ln, op)
+    oblk, obl = oracle.fuse_verify_block(od, om, q, long0, op)
+    o_flat, o_ln = flat.copy(), ln.copy()
+    if append:
+        oacc = oracle.greedy_accept(oblk, obl, tgt, o_flat, ro, o_ln, cap)
+    else:
+        oacc = oracle.greedy_accept(oblk, obl, tgt)
+    ost = np.zeros((B, 3), np.int32)
+    ost[:, 0] = long0
+    oln = oracle.lookup_schedule_step(ost, om, oacc, obl, op)
+    otele = np.zeros((B, 32), np.uint32)
+    oracle.telemetry_update(otele, om, od, q, long0, obl, oacc, oln, op)
+    exp = dict(m=om, e=oe, d=od, block=oblk, blk=obl, acc=oacc, ln=oln, state=ost, lens=o_ln,
+               flat=o_flat, tele=otele)
+    for k in exp:
+        np.testing.assert_array_equal(got[k], exp[k], err_msg=k)
+    return got, idx
+
+
+def test_index_step_config1(gpu):
+    w = wl.config1()
+    for lg in (0, 1):
+        _index_single_step(w.hists, w.q0, w.target0, np.array([lg], np.int32), append=True)
+    # every prefix of the history as one ragged batch, without and with append
+    hs = wl.prefix_batch(w.hists[0])[::7]
+    B = len(hs)
+    q = np.tile(w.q0, (B, 1)).astype(np.int32)
+    tgt = np.tile(w.target0, (B, 1)).astype(np.int32)
+    lg = (np.arange(B) % 2).astype(np.int32)
+    _index_single_step(hs, q, tgt, lg)
+    _, idx = _index_single_step(hs, q, tgt, lg, append=True)
+    # the call indexed every row up to its length before the append
+    assert (idx.indexed_len.cpu().numpy() == np.array([len(h) for h in hs])).all()
+
+
+@pytest.mark.parametrize("k", [4, 5])
+def test_index_step_full_size_configs(gpu, k):
+    w = wl.make_config(k)
+    for lg in (0, 1):
+        _index_single_step(w.hists, w.q0, w.target0, np.full(w.B, lg, np.int32), append=lg == 1)
+
+
+def test_index_step_ragged_params_and_capacity(gpu):
+    import context_lookup_drafting_amd as lcd
+    rng = np.random.Generator(np.random.PCG64(41))
+    hs = _stress_batch(seed=5, B=200)
+    B = len(hs)
+    q = rng.integers(0, 5, (B, 7)).astype(np.int32)
+    tgt = rng.integers(0, 5, (B, 16)).astype(np.int32)
+    lg = rng.integers(0, 2, B).astype(np.int32)
+    for prm in (dict(), dict(l_min=2, l_max=7, k_max=9, n_head=5, n_block=11),
+                dict(l_min=1, l_max=16), dict(k_max=0), dict(sticky=0, entry_steps=1)):
+        p = lcd.default_params(**prm)
+        _index_single_step(hs, q, tgt, lg, p, packed="csr")
+        _index_single_step(hs, q, tgt, lg, p, append=True)
+        _index_single_step(hs, q, tgt, lg, p, append=True, extra=4)   # many appends fail
+
+
+def test_index_step_stale_rows_and_collisions(gpu):
+    rng = np.random.Generator(np.random.PCG64(43))
+    hs = _stress_batch(seed=7, B=120)
+    B = len(hs)
+    q = rng.integers(0, 5, (B, 7)).astype(np.int32)
+    tgt = rng.integers(0, 5, (B, 16)).astype(np.int32)
+    lg = rng.integers(0, 2, B).astype(np.int32)
+    _, idx = _index_single_step(hs, q, tgt, lg, append=True, shrink=3)
+    il = idx.indexed_len.cpu().numpy()
+    lens = np.array([len(h) for h in hs])
+    assert (il[lens >= 3] == -1).all()          # shrunk rows are marked stale
+    for bits in (1, 3):
+        _index_single_step(hs, q, tgt, lg, append=True, fp_bits=bits)
+
+
+@pytest.mark.parametrize("k,steps,fp_bits", [(2, 200, 0), (3, 256, 0), (3, 48, 2)])
+def test_index_step_decode_simulation(gpu, k, steps, fp_bits):
+    """Whole decode loops with one lookup_index_decode_step per step: every
+    step, the final histories and the telemetry equal the oracle's."""
+    from simulate import simulate_gpu_index_fused, simulate_oracle
+    w = wl.make_config(k)
+    g = simulate_gpu_index_fused(w, steps, fp_bits=fp_bits)
+    _compare_sims(g, simulate_oracle(w, steps))
+    if fp_bits == 0:
+        # the last call indexed the history it read; its own append comes after
+        # (a call that fell back to the exact scan on a fingerprint collision
+        # leaves indexed_len where it was, so this holds without collisions)
+        gap = g["lens"] - g["indexed_len"]
+        assert ((gap >= 1) & (gap <= 16)).all()
+    for r in range(w.B):
+        em = g["emitted"][r]
+        assert em == w.truths[r][:len(em)].tolist()
