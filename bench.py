@@ -88,6 +88,7 @@ def per_request_bytes(separate, telemetry=False):
 
 
 KERNEL_SOURCES = ("context_lookup_drafting_amd/csrc/lcd_lookup.hip",
+                  "context_lookup_drafting_amd/csrc/lcd_finish.h",
                   "context_lookup_drafting_amd/csrc/lcd_rules.h", "include/lcd.h")
 
 
