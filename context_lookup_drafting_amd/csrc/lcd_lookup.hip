@@ -190,6 +190,10 @@ __device__ __forceinline__ void survivors(const int4 &t, const int4 &pt, const i
 // load in flight at its header.
 template <int PF>
 __device__ __forceinline__ int extend(const int4 &t, const int4 &pt, int sv, int J, u64 (&M)[4]) {
+    // J is opaque here, so the compiler cannot hoist the per-length tests
+    // j < J out of the tile loop: held there, they took about twenty scalar
+    // registers for the whole scan and were spilled into vector lanes.
+    asm volatile("" : "+s"(J));
     int L = PF;
     bool alive = true;
 #pragma unroll
@@ -334,22 +338,27 @@ __device__ __forceinline__ bool balanced_assignment(const int32_t *__restrict__ 
     return false;
 }
 
+// The lookup's outputs and the rest of the step's inputs and outputs: the
+// scan kernel's first argument, read where it is used (see the kernel).
+struct ScanOut {
+    int32_t *match_len, *match_end, *draft;
+    StepIO io;
+};
+
 template <int PF, int kMode, bool kBal, int kWaves>
 __global__ void __launch_bounds__(64 * kWaves)
-lookup_scan_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
+lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
                    const int32_t *__restrict__ len, int32_t cpr, int32_t T, ScanArgs a,
-                   u64 *__restrict__ ws,
-                   int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
-                   int32_t *__restrict__ draft)
+                   u64 *__restrict__ ws)
 {
-    // The rest of the step's pointers and rules are read from the
-    // kernel-argument segment (io_arg is the first argument, at its start)
-    // only where they are used, by the waves that use them: as an ordinary
-    // argument they were loaded by every wave at entry and held in scalar
-    // registers through the scan, which spilled dozens of values into vector
-    // lanes ahead of the first tile loads.
-    (void)io_arg;
-    const StepIO *iop = (const StepIO *)__builtin_amdgcn_kernarg_segment_ptr();
+    // The lookup's output pointers and the rest of the step's pointers and
+    // rules are read from the kernel-argument segment (out_arg is the first
+    // argument, at its start) only where they are used, by the waves that use
+    // them: as ordinary arguments they were loaded by every wave at entry and
+    // held in scalar registers through the scan, which spilled dozens of
+    // values into vector lanes ahead of the first tile loads.
+    (void)out_arg;
+    const ScanOut *op = (const ScanOut *)__builtin_amdgcn_kernarg_segment_ptr();
     __shared__ u64 s_wkey[kWaves];
     __shared__ int s_wtok[kWaves * kSlotWords];
     __shared__ u64 s_units[kMaxCpr * kSlotWords];
@@ -373,7 +382,7 @@ lookup_scan_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int64_
     int sin = 0;
     uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
     if (kMode == kStep && wave == 0) {
-        const StepIO io0 = *iop;
+        const StepIO io0 = op->io;
         sin = load_step_input(r, lane, io0);
         if (io0.tele != nullptr)
             tin = io0.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
@@ -384,7 +393,7 @@ lookup_scan_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int64_
     const int nc = n - 1;             // candidate ends 0..n-2
     if (nc <= 0) {                    // no earlier position: chunk 0 finishes the request
         if (c0 == 0 && wave == 0)
-            finish_request<kMode>(r, 0, 0, sin, tin, lane, ro, n, a.k_max, match_len, match_end, draft, *iop);
+            finish_request<kMode>(r, 0, 0, sin, tin, lane, ro, n, a.k_max, op->match_len, op->match_end, op->draft, op->io);
         return;
     }
     if ((int64_t)c0 * T >= nc) return;                  // past the row's last chunk
@@ -659,8 +668,8 @@ lookup_scan_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int64_
         if (kbest == 0) w = c0;
         if (w != c0) tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
         key = all ? kbest : 0;                      // gathering gave up: report no match
-        finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, match_len, match_end,
-                              draft, *iop);
+        finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, op->match_len,
+                              op->match_end, op->draft, op->io);
         // Re-zero the request's workspace for the next call, after the
         // outputs: a wait for these stores' acknowledgement must not sit in
         // front of the finish.
@@ -669,7 +678,7 @@ lookup_scan_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int64_
         if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, match_len, match_end, draft, *iop);
+    finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, op->match_len, op->match_end, op->draft, op->io);
 }
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
@@ -714,10 +723,10 @@ hipError_t launch_one(const int32_t *hist, const int64_t *row_off, const int32_t
     const dim3 grid((unsigned)(kBal ? (int64_t)sa.wgs : (int64_t)sa.B * sa.cpr));
     if (ev0 != nullptr || ev1 != nullptr)
         hipExtLaunchKernelGGL(lookup_scan_kernel<PF, kMode, kBal, kW>, grid, dim3(64 * kW), 0u, st,
-                              ev0, ev1, 0u, io, hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr);
+                              ev0, ev1, 0u, ScanOut{ml, me, dr, io}, hist, row_off, len, sa.cpr, sa.T, sa, ws);
     else
         hipLaunchKernelGGL((lookup_scan_kernel<PF, kMode, kBal, kW>), grid, dim3(64 * kW), 0, st,
-                           io, hist, row_off, len, sa.cpr, sa.T, sa, ws, ml, me, dr);
+                           ScanOut{ml, me, dr, io}, hist, row_off, len, sa.cpr, sa.T, sa, ws);
     return hipGetLastError();
 }
 
