@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="c3", choices=["c3", "c4", "c5", "sampled"])
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5", "sampled"])
     ap.add_argument("--cpu-work-seconds", type=float, default=20.0,
                     help="CPU work (seconds summed over threads) for the oracle baseline; 0 = skip")
     ap.add_argument("--scan-wgs", type=int, default=0, help="lookup launch tuning (0 = auto)")
@@ -300,7 +300,9 @@ def main():
     lib = lcd.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload == "c3":
+    if args.workload == "c2":
+        w = wl.config2()
+    elif args.workload == "c3":
         w = wl.config3()
     elif args.workload == "c4":
         w = wl.config4()
@@ -504,7 +506,7 @@ def bench_index(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = {"c3": wl.config3, "c4": wl.config4, "c5": wl.config5}[args.workload]()
+    w = {"c2": wl.config2, "c3": wl.config3, "c4": wl.config4, "c5": wl.config5}[args.workload]()
     K, W = args.steps, args.warmup
     R = 8
     n_k = 200                                              # event-timed steps after the graph
