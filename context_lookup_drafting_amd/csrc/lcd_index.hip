@@ -137,20 +137,29 @@ __device__ u64 exact_scan(const int32_t *__restrict__ h, int n, const IndexArgs 
 // kStep: the wave also finishes its request's decode step (io).
 template <bool kStep>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
-index_propose_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
+index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
                      const int32_t *__restrict__ len, int32_t B, IndexArgs a,
                      const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_bits,
                      u64 *__restrict__ tables, int32_t *__restrict__ indexed_len,
                      int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
-                     int32_t *__restrict__ draft, StepIO io) {
+                     int32_t *__restrict__ draft) {
+    // The step's pointers and rules are read from the kernel-argument segment
+    // (io_arg is the first argument, at its start) where they are used, so
+    // they are not held in scalar registers through the lookup.
+    (void)io_arg;
+    const StepIO *iop = (const StepIO *)__builtin_amdgcn_kernarg_segment_ptr();
     const int lane = threadIdx.x & 63;
     const int r = uni(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
     if (r >= B) return;
     // the rest of the step's inputs, in flight during the lookup
-    const int sin = kStep ? load_step_input(r, lane, io) : 0;
+    int sin = 0;
     uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
-    if (kStep && io.tele != nullptr)
-        tin = io.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
+    if (kStep) {
+        const StepIO io0 = *iop;
+        sin = load_step_input(r, lane, io0);
+        if (io0.tele != nullptr)
+            tin = io0.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
+    }
     const int32_t n0 = len[r];
     const int n = n0 > 0 ? n0 : 0;
     const int64_t ro = row_off[r];
@@ -164,11 +173,19 @@ index_propose_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict
     bool overfull = false;
     u64 key = 0;
     if (!exact) {
-        // The suffix s_j = h[n-1-j], in every lane (the same addresses for all
-        // lanes), loaded together with the appended positions' tokens below.
+        // The suffix s_j = h[n-1-j]: lane j < 16 loads it (one vector load,
+        // in flight with the appended positions' tokens below) and every lane
+        // reads them all.  (As uniform loads they became one scalar load per
+        // token, each waited for before the next.)
+        int32_t sv = 0;
+        if (n > 0) {
+            const int sp = n - 1 - (lane < kMaxL ? lane : 0);
+            sv = h[sp > 0 ? sp : 0];
+        }
         int32_t s[kMaxL];
 #pragma unroll
-        for (int j = 0; j < kMaxL; ++j) s[j] = (j < a.l_max && n - 1 - j >= 0) ? h[n - 1 - j] : 0;
+        for (int j = 0; j < kMaxL; ++j)
+            s[j] = (j < a.l_max && n - 1 - j >= 0) ? __builtin_amdgcn_readlane(sv, j) : 0;
 
         // ---- the positions appended since the last call: p_lo..p_hi --------
         // Each is matched against the suffix directly (from its tokens in
@@ -305,7 +322,7 @@ index_propose_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict
         match_len[r] = m;
         match_end[r] = e;
     }
-    if (kStep) finish_step(r, m, d, sin, tin, lane, ro, n, io);
+    if (kStep) finish_step(r, m, d, sin, tin, lane, ro, n, *iop);
 }
 
 // Build: clear the tables, then insert every position p <= n-2 of every row.
@@ -443,13 +460,12 @@ int index_launch(const int32_t *hist, const int64_t *row_off, const int32_t *len
     if (ev0 != nullptr || ev1 != nullptr)
         hipExtLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(64 * kWavesPerBlock), 0u, st,
                               reinterpret_cast<hipEvent_t>(ev0), reinterpret_cast<hipEvent_t>(ev1),
-                              0u, hist, row_off, len, B, a, table_off, table_bits,
-                              static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft,
-                              io);
+                              0u, io, hist, row_off, len, B, a, table_off, table_bits,
+                              static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft);
     else
-        hipLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(64 * kWavesPerBlock), 0, st, hist,
-                           row_off, len, B, a, table_off, table_bits, static_cast<u64 *>(tables),
-                           indexed_len, match_len, match_end, draft, io);
+        hipLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(64 * kWavesPerBlock), 0, st, io,
+                           hist, row_off, len, B, a, table_off, table_bits,
+                           static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft);
     return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
 }
 
