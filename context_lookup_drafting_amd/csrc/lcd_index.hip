@@ -205,11 +205,16 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int6
         const bool qlane = lane < nL && L <= n - 1;   // the suffix and an earlier occurrence both fit
         u64 qk = 0;
         {
-            u64 hs = kHashSeed;
+            // the prefix hashes are the same in every lane; lane k keeps the
+            // one of length L (a select, not a branch per length: per-length
+            // lane masks kept for later uses were spilled)
+            u64 hs = kHashSeed, hl = kHashSeed;
 #pragma unroll
-            for (int j = 0; j < kMaxL; ++j)
-                if (j < L) hs = roll(hs, s[j]);
-            qk = finish_key(hs, L);
+            for (int j = 0; j < kMaxL; ++j) {
+                hs = roll(hs, s[j]);
+                hl = j < L ? hs : hl;
+            }
+            qk = finish_key(hl, L);
         }
         const uint32_t qfp = fingerprint(qk, a.fp_mask);
         u64 qi = qk & cmask;
@@ -277,11 +282,13 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int6
                     const int pe = (int)(uint32_t)v - 1;
                     bool same = pe >= L - 1 && pe <= n - 2;
                     if (same) {
+                        int Lv = L;                                  // opaque: see the hash above
+                        asm volatile("" : "+v"(Lv));
                         int32_t g[kMaxL];                            // all loads in flight at once
 #pragma unroll
-                        for (int j = 0; j < kMaxL; ++j) g[j] = j < L ? h[pe - j] : 0;
+                        for (int j = 0; j < kMaxL; ++j) g[j] = j < Lv ? h[pe - j] : 0;
 #pragma unroll
-                        for (int j = 0; j < kMaxL; ++j) same = same && (j >= L || g[j] == s[j]);
+                        for (int j = 0; j < kMaxL; ++j) same = same && (j >= Lv || g[j] == s[j]);
                     }
                     if (same) e = pe; else collide = true;
                     break;
