@@ -223,19 +223,23 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int6
         for (int p0 = p_lo, first = 1; p0 <= p_hi || first; p0 += 64, first = 0) {
             const int p = p0 + lane;
             const bool ins = p <= p_hi;
+            // opaque copies of the length bounds: tests against them hoisted
+            // out of this loop were held (and spilled) through the whole kernel
+            int lmin = a.l_min, lmax = a.l_max;
+            asm volatile("" : "+s"(lmin), "+s"(lmax));
             int32_t t[kMaxL];
 #pragma unroll
             for (int j = 0; j < kMaxL; ++j)
-                t[j] = (ins && j < a.l_max && p - j >= 0) ? h[p - j] : 0;
+                t[j] = (ins && j < lmax && p - j >= 0) ? h[p - j] : 0;
             // direct match length at end p (capped at l_max)
             int Lp = 0;
             bool run = ins;
 #pragma unroll
             for (int j = 0; j < kMaxL; ++j) {
-                run = run && j < a.l_max && p - j >= 0 && t[j] == s[j];
+                run = run && j < lmax && p - j >= 0 && t[j] == s[j];
                 Lp += run ? 1 : 0;
             }
-            if (Lp >= a.l_min) {
+            if (Lp >= lmin) {
                 const u64 k = ((u64)Lp << 31) | (uint32_t)p;
                 key_new = k > key_new ? k : key_new;
             }
@@ -249,7 +253,7 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int6
                 const u64 k = finish_key(hs, Lj);
                 ent[j] = entry_of(k, a.fp_mask, p);
                 slot[j] = k & cmask;
-                old[j] = (ins && Lj >= a.l_min && Lj <= a.l_max && p - j >= 0)
+                old[j] = (ins && Lj >= lmin && Lj <= lmax && p - j >= 0)
                              ? atomicCAS(T + slot[j], 0ull, ent[j]) : 0ull;
             }
             // ... and, on the first pass, the query's first probe with them
