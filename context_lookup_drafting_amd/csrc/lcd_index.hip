@@ -137,8 +137,9 @@ __device__ u64 exact_scan(const int32_t *__restrict__ h, int n, const IndexArgs 
 // kStep: the wave also finishes its request's decode step (io).
 template <bool kStep>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
-index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
-                     const int32_t *__restrict__ len, int32_t B, IndexArgs a,
+index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
+                     const int64_t *__restrict__ row_off, const int32_t *__restrict__ len,
+                     int32_t B, IndexArgs a,
                      const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_bits,
                      u64 *__restrict__ tables, int32_t *__restrict__ indexed_len,
                      int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,

@@ -347,8 +347,9 @@ struct ScanOut {
 
 template <int PF, int kMode, bool kBal, int kWaves>
 __global__ void __launch_bounds__(64 * kWaves)
-lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
-                   const int32_t *__restrict__ len, int32_t cpr, int32_t T, ScanArgs a,
+lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
+                   const int64_t *__restrict__ row_off, const int32_t *__restrict__ len,
+                   int32_t cpr, int32_t T, ScanArgs a,
                    u64 *__restrict__ ws)
 {
     // The lookup's output pointers and the rest of the step's pointers and
@@ -393,7 +394,8 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist, const int6
     const int nc = n - 1;             // candidate ends 0..n-2
     if (nc <= 0) {                    // no earlier position: chunk 0 finishes the request
         if (c0 == 0 && wave == 0)
-            finish_request<kMode>(r, 0, 0, sin, tin, lane, ro, n, a.k_max, op->match_len, op->match_end, op->draft, op->io);
+            finish_request<kMode>(r, 0, 0, sin, tin, lane, ro, n, a.k_max, op->match_len,
+                                  op->match_end, op->draft, op->io);
         return;
     }
     if ((int64_t)c0 * T >= nc) return;                  // past the row's last chunk
@@ -678,7 +680,8 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist, const int6
         if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, op->match_len, op->match_end, op->draft, op->io);
+    finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, op->match_len, op->match_end,
+                          op->draft, op->io);
 }
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
