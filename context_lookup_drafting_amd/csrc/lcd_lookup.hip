@@ -12,7 +12,11 @@
 //
 //  * The candidate ends of every request are cut into chunks of T tokens
 //    (whole 256-token tiles; the host derives T from the longest row), one
-//    workgroup of four waves per chunk, B x cpr workgroups per launch.
+//    workgroup per chunk, B x cpr workgroups per launch: four waves each, or
+//    sixteen (one workgroup per CU) for batches of 32-128 long rows.
+//  * Only the waves that need them read the lookup's output pointers and the
+//    rest of the step's arguments, from the kernel-argument segment where
+//    they are used, so they are not held (and spilled) through the scan.
 //  * A decode-step scan is short, so dependent memory round trips cost as much
 //    as the bytes: the row offset and length are loaded together, then the 16
 //    suffix tokens (one per lane) and the wave's first batch of tiles go into
@@ -62,8 +66,8 @@ namespace {
 constexpr int kWavesSmall = 4;
 constexpr int kWavesLarge = 16;
 constexpr int kNumCUs = 256;
-// 4-wave workgroups of the scan resident on one CU at once, as compiled (35
-// VGPRs and 106 SGPRs per wave: 7 waves per SIMD; lookup_scan_occupancy
+// 4-wave workgroups of the scan resident on one CU at once, as compiled (106
+// SGPRs and at most 52 VGPRs per wave: 7 waves per SIMD; lookup_scan_occupancy
 // reports the runtime's figure and the GPU tests hold it to this).  Automatic
 // grids stay within 7 x 256 workgroups: a workgroup beyond them is dispatched
 // only when an earlier one ends, and on ragged batches that put a long row's
