@@ -273,6 +273,12 @@ def test_launch_shape_query():
     rows' lengths (host) and cover every row's candidate ends within the grid."""
     p = lcd.default_params()
     assert lcd.launch_shape(64, 25_000, p) == (256, 6400)
+    # fewer than 32 rows of 16k+ tokens: one workgroup per ~12k tokens of the
+    # longest row, at most 256 in all
+    assert lcd.launch_shape(1, 25_000, p) == (2, 12544)
+    assert lcd.launch_shape(1, 150_000, p) == (12, 12544)
+    assert lcd.launch_shape(16, 150_000, p) == (192, 12544)
+    assert lcd.launch_shape(31, 262_144, p) == (248, 32768)
     pb = lcd.default_params(scan_balance=1)
     with pytest.raises(lcd.LCDError):
         lcd.launch_shape(256, 262_144, pb)

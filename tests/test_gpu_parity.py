@@ -262,6 +262,62 @@ def test_match_across_workgroup_boundaries(gpu):
         assert np.all(m == 12)
 
 
+@pytest.mark.parametrize("k", [4, 5])
+def test_small_batches_of_long_rows(gpu, k):
+    """Batches of 1-31 rows of 16k+ tokens (16-wave workgroups, one per ~12k
+    tokens of the longest row): lookup, and the fused step on the same rows,
+    equal the oracle's."""
+    import torch
+    lcd = _lcd()
+    w = wl.make_config(k)
+    order = np.argsort([-len(h) for h in w.hists], kind="stable")
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    op = _oparams(lcd.default_params())
+    for B in (1, 7, 16, 31):
+        hs = [w.hists[i] for i in order[:B]]
+        flat, ro, ln, cap = wl.pack_rows(hs, extra=16)
+        assert lcd.launch_shape(B, int(ln.max()))[0] >= B
+        m, e, d = assert_lookup_parity(flat, ro, ln)
+        q, tgt = w.step_inputs(np.zeros(w.B, np.int64), 0)
+        q, tgt = q[order[:B]], tgt[order[:B]]
+        h_d, ln_d = t(flat), t(ln.copy())
+        dr = lcd.LookupDrafter(B, int(ln.max()), dev)
+        out = dr.step(h_d, t(ro), ln_d, t(cap), t(q), t(tgt))
+        torch.cuda.synchronize()
+        oblk, obl = oracle.fuse_verify_block(d, m, q, np.zeros(B, np.int32), op)
+        o_flat, o_ln = flat.copy(), ln.copy()
+        oacc = oracle.greedy_accept(oblk, obl, tgt, o_flat, ro, o_ln, cap)
+        np.testing.assert_array_equal(out["match_len"].cpu().numpy(), m)
+        np.testing.assert_array_equal(out["match_end"].cpu().numpy(), e)
+        np.testing.assert_array_equal(out["block"].cpu().numpy(), oblk)
+        np.testing.assert_array_equal(out["accept"].cpu().numpy(), oacc)
+        np.testing.assert_array_equal(h_d.cpu().numpy(), o_flat)
+        np.testing.assert_array_equal(ln_d.cpu().numpy(), o_ln)
+
+
+def test_match_across_long_chunk_boundaries(gpu):
+    """One 40k-token row cut into 16-wave chunks, with the winning occurrence
+    ending at every offset around a chunk edge."""
+    lcd = _lcd()
+    rng = np.random.Generator(np.random.PCG64(23))
+    n = 40_000
+    wgs, T = lcd.launch_shape(1, n)
+    assert wgs >= 2
+    for edge in (T, 2 * T):
+        hs = []
+        for off in range(-13, 14):
+            h = rng.integers(0, 1 << 20, n).astype(np.int32)
+            L = 12
+            end = edge + off
+            h[n - L:] = h[end - L + 1:end + 1]
+            hs.append(h)
+        for h in hs:
+            flat, ro, ln = wl.pack_csr([h])
+            m, e, d = assert_lookup_parity(flat, ro, ln)
+            assert m[0] == 12
+
+
 def test_empty_and_tiny_rows(gpu):
     hs = [np.zeros(0, np.int32), np.array([1], np.int32), np.array([1, 1], np.int32),
           np.array([2, 2, 2, 2], np.int32), np.array([2, 2, 2, 2, 2], np.int32),
