@@ -296,6 +296,23 @@ def test_small_batches_of_long_rows(gpu, k):
         np.testing.assert_array_equal(ln_d.cpu().numpy(), o_ln)
 
 
+def test_small_batch_rows_longer_than_max_len(gpu):
+    """16-wave launches of 1-3 rows sized from a max_len below the rows' true
+    lengths (each workgroup then takes every cpr-th chunk), and rows on both
+    sides of the 16k-token threshold of that launch."""
+    lcd = _lcd()
+    w = wl.config4()
+    hs = [w.hists[i] for i in range(3)]
+    for B in (1, 3):
+        flat, ro, ln, cap = wl.pack_rows(hs[:B])
+        for ml in (16_384, 20_000, 30_000, 70_000):
+            assert lcd.launch_shape(B, ml)[1] < int(ln.max())
+            assert_lookup_parity(flat, ro, ln, max_len=ml)
+    for n in (16_383, 16_384, 16_385, 24_577):
+        flat, ro, ln = wl.pack_csr([h[-n:] for h in hs])
+        assert_lookup_parity(flat, ro, ln)
+
+
 def test_match_across_long_chunk_boundaries(gpu):
     """One 40k-token row cut into 16-wave chunks, with the winning occurrence
     ending at every offset around a chunk edge."""
