@@ -788,10 +788,12 @@ ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
         return ScanArgs{0, 0, p->l_min, p->l_max, p->k_max, B, balanced_wgs(B, max_len, p->scan_wgs),
                         kWavesSmall};
     // Batches of 32-128 rows of at least 16k tokens: one 16-wave workgroup per
-    // CU (256 workgroups, equal chunks per row).  Measured on 64 rows of 25k and
-    // 150k tokens: 4 % and 7 % faster than 4-wave workgroups at their best grid.
+    // CU (at most 256 workgroups, equal chunks per row; a CU holds only one, so
+    // a workgroup past 256 would wait for a whole one to finish).  Measured on
+    // 64 rows of 25k and 150k tokens: 4 % and 7 % faster than 4-wave
+    // workgroups at their best grid.
     if (p->scan_wgs == 0 && B >= 32 && B <= 128 && max_len >= 16384) {
-        int cpr = (kNumCUs + B / 2) / B;
+        int cpr = kNumCUs / B;
         const int most = (max_len + 2047) / 2048;
         if (cpr > most) cpr = most;
         if (cpr < 1) cpr = 1;

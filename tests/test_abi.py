@@ -279,6 +279,11 @@ def test_launch_shape_query():
     assert lcd.launch_shape(1, 150_000, p) == (12, 12544)
     assert lcd.launch_shape(16, 150_000, p) == (192, 12544)
     assert lcd.launch_shape(31, 262_144, p) == (248, 32768)
+    # 16-wave workgroups (one per CU) never exceed the 256 CUs
+    for B in range(1, 129):
+        for n in (16_384, 25_000, 150_000, 262_144):
+            assert lcd.launch_shape(B, n, p)[0] <= 256, (B, n)
+    assert lcd.launch_shape(100, 150_000, p)[0] == 200
     pb = lcd.default_params(scan_balance=1)
     with pytest.raises(lcd.LCDError):
         lcd.launch_shape(256, 262_144, pb)

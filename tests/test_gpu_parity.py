@@ -264,9 +264,9 @@ def test_match_across_workgroup_boundaries(gpu):
 
 @pytest.mark.parametrize("k", [4, 5])
 def test_small_batches_of_long_rows(gpu, k):
-    """Batches of 1-31 rows of 16k+ tokens (16-wave workgroups, one per ~12k
-    tokens of the longest row): lookup, and the fused step on the same rows,
-    equal the oracle's."""
+    """Batches of 1-100 rows of 16k+ tokens (16-wave workgroups: one per ~12k
+    tokens of the longest row below 32 rows, at most one per CU from 32):
+    lookup, and the fused step on the same rows, equal the oracle's."""
     import torch
     lcd = _lcd()
     w = wl.make_config(k)
@@ -274,13 +274,14 @@ def test_small_batches_of_long_rows(gpu, k):
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     op = _oparams(lcd.default_params())
-    for B in (1, 7, 16, 31):
-        hs = [w.hists[i] for i in order[:B]]
+    for B in (1, 7, 16, 31, 37, 100):
+        sel = order[np.arange(B) % len(order)]
+        hs = [w.hists[i] for i in sel]
         flat, ro, ln, cap = wl.pack_rows(hs, extra=16)
         assert lcd.launch_shape(B, int(ln.max()))[0] >= B
         m, e, d = assert_lookup_parity(flat, ro, ln)
         q, tgt = w.step_inputs(np.zeros(w.B, np.int64), 0)
-        q, tgt = q[order[:B]], tgt[order[:B]]
+        q, tgt = q[sel], tgt[sel]
         h_d, ln_d = t(flat), t(ln.copy())
         dr = lcd.LookupDrafter(B, int(ln.max()), dev)
         out = dr.step(h_d, t(ro), ln_d, t(cap), t(q), t(tgt))
