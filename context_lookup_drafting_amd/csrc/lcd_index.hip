@@ -50,7 +50,10 @@ namespace {
 
 using u64 = unsigned long long;
 
-constexpr int kWavesPerBlock = 4;
+// One wave per workgroup: a request's wave issues scattered probes and
+// atomics, and spreading the waves over more CUs measured 0.1-0.45 us faster
+// per step than four per workgroup (1 x 25k, 64 x 25k, 256 ragged rows).
+constexpr int kWavesPerBlock = 1;
 constexpr int kBuildThreads = 256;
 constexpr int kMaxL = LCD_MAX_SUFFIX;            // 16
 constexpr int kMaxProbe = 1 << 20;               // bound on a probe sequence
