@@ -14,7 +14,8 @@
 //    (whole 256-token tiles; the host derives T from the longest row), one
 //    workgroup per chunk, B x cpr workgroups per launch: four waves each, or
 //    sixteen for batches of at most 128 long rows (one workgroup per CU from
-//    32 rows, one per ~12k tokens of the longest row below).
+//    32 rows of 16k+ tokens, one per ~12k tokens of the longest row for
+//    fewer rows of 6k+ tokens).
 //  * Only the waves that need them read the lookup's output pointers and the
 //    rest of the step's arguments, from the kernel-argument segment where
 //    they are used, so they are not held (and spilled) through the scan.
@@ -62,8 +63,8 @@
 namespace lcd {
 namespace {
 
-// Waves per workgroup: 4 in general; 16 for batches of at most 128 rows of
-// 16k+ tokens, where it measured 4-42 % faster.
+// Waves per workgroup: 4 in general; 16 for batches of 32-128 rows of 16k+
+// tokens and of 1-31 rows of 6k+ tokens, where it measured 4-42 % faster.
 constexpr int kWavesSmall = 4;
 constexpr int kWavesLarge = 16;
 constexpr int kNumCUs = 256;
@@ -800,11 +801,12 @@ ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
         return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max, B, 0,
                         kWavesLarge};
     }
-    // Smaller batches of rows of at least 16k tokens: 16-wave workgroups too,
-    // one per ~12k tokens of the longest row, at most 256 in all.  Measured on
-    // 1-16 rows of 25k-260k tokens: 14-42 % faster than 4-wave workgroups, and
-    // within 10 % of the best fixed count per request on each.
-    if (p->scan_wgs == 0 && B >= 1 && B < 32 && max_len >= 16384) {
+    // Smaller batches whose longest row has at least 6k tokens: 16-wave
+    // workgroups too, one per ~12k tokens of the longest row, at most 256 in
+    // all.  Measured on 1-31 rows of 6k-260k tokens: 6-42 % faster than 4-wave
+    // workgroups, and within 10 % of the best fixed count per request on each
+    // (at 4k tokens both launches are even).
+    if (p->scan_wgs == 0 && B >= 1 && B < 32 && max_len >= 6000) {
         int cpr = (max_len + 6144) / 12288;
         if (cpr > kNumCUs / B) cpr = kNumCUs / B;
         if (cpr > kMaxCpr) cpr = kMaxCpr;

@@ -59,9 +59,10 @@ extern "C" {
  *   near_full_slack  a step is "nearly full" when accept >= blk - slack, >= 0 (1)
  *   scan_wgs      launch tuning of the scan (lookup_propose, lookup_decode_step):
  *                 workgroups of 4 waves per launch; 0 = automatic (16-wave
- *                 workgroups, at most 256, for batches of at most 128 rows
- *                 whose longest row has 16k+ tokens; 4-wave workgroups
- *                 otherwise).  Results never depend on it.
+ *                 workgroups, at most 256, for batches of 32-128 rows whose
+ *                 longest row has 16k+ tokens and of 1-31 rows whose longest
+ *                 row has 6k+ tokens; 4-wave workgroups otherwise).  Results
+ *                 never depend on it.
  *   scan_balance  launch tuning of the scan (lookup_propose, lookup_decode_step)
  *                 for ragged batches: 1 = chunks of equal token count, sized on
  *                 the device from the rows' lengths, so long rows get more

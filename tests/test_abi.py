@@ -273,8 +273,10 @@ def test_launch_shape_query():
     rows' lengths (host) and cover every row's candidate ends within the grid."""
     p = lcd.default_params()
     assert lcd.launch_shape(64, 25_000, p) == (256, 6400)
-    # fewer than 32 rows of 16k+ tokens: one workgroup per ~12k tokens of the
+    # fewer than 32 rows of 6k+ tokens: one workgroup per ~12k tokens of the
     # longest row, at most 256 in all
+    assert lcd.launch_shape(16, 8_192, p) == (16, 8192)
+    assert lcd.launch_shape(1, 5_999, p) == (3, 2048)          # 4-wave launch below 6k
     assert lcd.launch_shape(1, 25_000, p) == (2, 12544)
     assert lcd.launch_shape(1, 150_000, p) == (12, 12544)
     assert lcd.launch_shape(16, 150_000, p) == (192, 12544)

@@ -300,7 +300,7 @@ def test_small_batches_of_long_rows(gpu, k):
 def test_small_batch_rows_longer_than_max_len(gpu):
     """16-wave launches of 1-3 rows sized from a max_len below the rows' true
     lengths (each workgroup then takes every cpr-th chunk), and rows on both
-    sides of the 16k-token threshold of that launch."""
+    sides of the 6k- and 16k-token thresholds of the 16-wave launches."""
     lcd = _lcd()
     w = wl.config4()
     hs = [w.hists[i] for i in range(3)]
@@ -309,7 +309,7 @@ def test_small_batch_rows_longer_than_max_len(gpu):
         for ml in (16_384, 20_000, 30_000, 70_000):
             assert lcd.launch_shape(B, ml)[1] < int(ln.max())
             assert_lookup_parity(flat, ro, ln, max_len=ml)
-    for n in (16_383, 16_384, 16_385, 24_577):
+    for n in (5_999, 6_000, 8_192, 16_383, 16_384, 16_385, 24_577):
         flat, ro, ln = wl.pack_csr([h[-n:] for h in hs])
         assert_lookup_parity(flat, ro, ln)
 
