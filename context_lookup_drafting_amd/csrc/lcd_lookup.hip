@@ -14,8 +14,8 @@
 //    (whole 256-token tiles; the host derives T from the longest row), one
 //    workgroup per chunk, B x cpr workgroups per launch: four waves each, or
 //    sixteen for batches of at most 128 long rows (one workgroup per CU from
-//    32 rows of 16k+ tokens, one per ~12k tokens of the longest row for
-//    fewer rows of 6k+ tokens).
+//    32 rows of 16k+ tokens, or of 8k+ tokens and 1.2M+ in all; one per ~12k
+//    tokens of the longest row for fewer rows of 6k+ tokens).
 //  * Only the waves that need them read the lookup's output pointers and the
 //    rest of the step's arguments, from the kernel-argument segment where
 //    they are used, so they are not held (and spilled) through the scan.
@@ -64,7 +64,8 @@ namespace lcd {
 namespace {
 
 // Waves per workgroup: 4 in general; 16 for batches of 32-128 rows of 16k+
-// tokens and of 1-31 rows of 6k+ tokens, where it measured 4-42 % faster.
+// tokens (8k+ when the batch holds 1.2M+ tokens) and of 1-31 rows of 6k+
+// tokens, where it measured 3-42 % faster.
 constexpr int kWavesSmall = 4;
 constexpr int kWavesLarge = 16;
 constexpr int kNumCUs = 256;
@@ -788,12 +789,15 @@ ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
     if (p->scan_balance == 1 && B <= LCD_BALANCE_MAX_B)
         return ScanArgs{0, 0, p->l_min, p->l_max, p->k_max, B, balanced_wgs(B, max_len, p->scan_wgs),
                         kWavesSmall};
-    // Batches of 32-128 rows of at least 16k tokens: one 16-wave workgroup per
-    // CU (at most 256 workgroups, equal chunks per row; a CU holds only one, so
-    // a workgroup past 256 would wait for a whole one to finish).  Measured on
-    // 64 rows of 25k and 150k tokens: 4 % and 7 % faster than 4-wave
-    // workgroups at their best grid.
-    if (p->scan_wgs == 0 && B >= 32 && B <= 128 && max_len >= 16384) {
+    // Batches of 32-128 rows of at least 16k tokens, or of 8k+ tokens when the
+    // batch holds 1.2M+ tokens: one 16-wave workgroup per CU (at most 256
+    // workgroups, equal chunks per row; a CU holds only one, so a workgroup
+    // past 256 would wait for a whole one to finish).  Measured on 64 rows of
+    // 25k and 150k tokens: 4 % and 7 % faster than 4-wave workgroups at their
+    // best grid; on 100 x 14k and 128 x 12k, 6 % and 3 %; slower on 64 x 14k
+    // and 128 x 8k.
+    if (p->scan_wgs == 0 && B >= 32 && B <= 128 &&
+        (max_len >= 16384 || (max_len >= 8192 && (int64_t)B * max_len >= 1200000))) {
         int cpr = kNumCUs / B;
         const int most = (max_len + 2047) / 2048;
         if (cpr > most) cpr = most;

@@ -60,9 +60,9 @@ extern "C" {
  *   scan_wgs      launch tuning of the scan (lookup_propose, lookup_decode_step):
  *                 workgroups of 4 waves per launch; 0 = automatic (16-wave
  *                 workgroups, at most 256, for batches of 32-128 rows whose
- *                 longest row has 16k+ tokens and of 1-31 rows whose longest
- *                 row has 6k+ tokens; 4-wave workgroups otherwise).  Results
- *                 never depend on it.
+ *                 longest row has 16k+ tokens, or 8k+ with B x max_len of
+ *                 1.2M+, and of 1-31 rows whose longest row has 6k+ tokens;
+ *                 4-wave workgroups otherwise).  Results never depend on it.
  *   scan_balance  launch tuning of the scan (lookup_propose, lookup_decode_step)
  *                 for ragged batches: 1 = chunks of equal token count, sized on
  *                 the device from the rows' lengths, so long rows get more

@@ -286,6 +286,10 @@ def test_launch_shape_query():
         for n in (16_384, 25_000, 150_000, 262_144):
             assert lcd.launch_shape(B, n, p)[0] <= 256, (B, n)
     assert lcd.launch_shape(100, 150_000, p)[0] == 200
+    # 32-128 rows of 8k-16k tokens: 16-wave from 1.2M tokens in all
+    assert lcd.launch_shape(100, 14_000, p) == (200, 7168)
+    assert lcd.launch_shape(100, 12_000, p) == (200, 6144)    # 1.2M exactly
+    assert lcd.launch_shape(100, 11_999, p)[0] == 300         # 4-wave below 1.2M
     pb = lcd.default_params(scan_balance=1)
     with pytest.raises(lcd.LCDError):
         lcd.launch_shape(256, 262_144, pb)

@@ -312,6 +312,10 @@ def test_small_batch_rows_longer_than_max_len(gpu):
     for n in (5_999, 6_000, 8_192, 16_383, 16_384, 16_385, 24_577):
         flat, ro, ln = wl.pack_csr([h[-n:] for h in hs])
         assert_lookup_parity(flat, ro, ln)
+    # 32-128 rows of 8k-16k tokens, on both sides of 1.2M tokens in all
+    for B, n in ((64, 14_000), (100, 14_000), (128, 9_500)):
+        flat, ro, ln = wl.pack_csr([w.hists[i % w.B][-n:] for i in range(B)])
+        assert_lookup_parity(flat, ro, ln)
 
 
 def test_match_across_long_chunk_boundaries(gpu):
