@@ -9,7 +9,8 @@ library raises.
 Entry points (same names as the C ABI):
   lookup_propose(hist, row_off, lens, max_len, workspace, match_len, match_end, draft, params)
   lookup_decode_step(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
-                     match_len, match_end, draft, block, block_len, accept, long_next, append, params)
+                     match_len, match_end, draft, block, block_len, accept, long_next, append, params,
+                     lens_out=...)
   fuse_verify_block(draft, match_len, model_draft, long_mode, block, block_len, params,
                     model_mask=None)
   greedy_accept(block, block_len, target, accept, hist=None, row_off=None, lens=None, cap=None)
@@ -54,7 +55,7 @@ class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "l_min", "l_max", "k_max", "n_head", "n_block", "head_full", "head_agree",
         "agree_n", "tail_min", "entry_steps", "sticky", "near_full_slack", "scan_wgs",
-        "scan_balance")]
+        "scan_balance", "merge_polls")]
 
     def __repr__(self):
         return "Params(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -85,7 +86,8 @@ def load():
         L.fuse_verify_block.argtypes = [P, P, P, P, i32, pp, P, P, P, P]
         L.lcd_decode_step_workspace_bytes.argtypes = [i32, i32, pp]
         L.lcd_decode_step_workspace_bytes.restype = ctypes.c_size_t
-        dec = [P, P, P, P, i32, i32, P, P, P, pp, P, ctypes.c_size_t, P, P, P, P, P, P, P, P, i32, P]
+        dec = [P, P, P, P, P, i32, i32, P, P, P, pp, P, ctypes.c_size_t, P, P, P, P, P, P, P, P, i32,
+               P]
         L.lookup_decode_step.argtypes = dec
         L.lookup_decode_step_timed.argtypes = dec + [P, P]
         L.greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P, P]
@@ -107,7 +109,7 @@ def load():
         idec = [P, P, P, P, i32, pp, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, i32, P]
         L.lookup_index_decode_step.argtypes = idec
         L.lookup_index_decode_step_timed.argtypes = idec + [P, P]
-        rej = [P, P, P, P, P, i32, P, P, i32, i32, P, ctypes.c_size_t, P, P, P, P, P, P, P]
+        rej = [P, P, P, P, P, i32, P, P, i32, i32, i32, P, ctypes.c_size_t, P, P, P, P, P, P, P]
         L.rejection_accept.argtypes = rej
         L.rejection_accept_timed.argtypes = rej + [P, P]
         for f in (L.lookup_propose, L.lookup_propose_timed, L.fuse_verify_block,
@@ -140,7 +142,8 @@ def workspace_bytes(B: int) -> int:
 
 
 def alloc_workspace(B: int, device):
-    """Zero-filled lookup workspace for B requests (kept zero by every call)."""
+    """Zero-filled lookup workspace for B requests (then kept valid by every
+    call: counts and gathered slots back at zero, a per-request call epoch)."""
     import torch
     n = max(workspace_bytes(B), 16)
     return torch.zeros(n // 8, dtype=torch.int64, device=device)
@@ -279,7 +282,8 @@ def decode_step_workspace_bytes(B: int, max_len: int, params: Params | None = No
 
 
 def alloc_decode_workspace(B: int, max_len: int, device, params: Params | None = None):
-    """Zero-filled workspace for lookup_decode_step (kept zero by every call)."""
+    """Zero-filled workspace for lookup_decode_step (then kept valid by every
+    call, as lookup_propose's)."""
     import torch
     n = max(decode_step_workspace_bytes(B, max_len, params), 16)
     return torch.zeros((n + 7) // 8, dtype=torch.int64, device=device)
@@ -287,15 +291,19 @@ def alloc_decode_workspace(B: int, max_len: int, device, params: Params | None =
 
 def _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
                  match_len, match_end, draft, block, block_len, accept, long_next, append, p,
-                 telemetry=None):
+                 telemetry=None, lens_out=None):
     import torch
     B = lens.numel()
     dev = lens.device
     nul = ctypes.c_void_p(None)
+    if append and lens_out is None:
+        raise ValueError("lookup_decode_step: append needs lens_out, a second length array "
+                         "(the launch reads lens and writes the new lengths to lens_out)")
     return (
         _dev(hist, "hist", torch.int32, device=dev),
         _dev(row_off, "row_off", torch.int64, B, dev),
         _dev(lens, "lens", torch.int32, B, dev),
+        _dev(lens_out, "lens_out", torch.int32, B, dev) if lens_out is not None else nul,
         _dev(cap, "cap", torch.int32, B, dev) if cap is not None else nul,
         ctypes.c_int32(B), ctypes.c_int32(int(max_len)),
         _dev(model_draft, "model_draft", torch.int32, B * Q_STRIDE, dev),
@@ -320,25 +328,28 @@ def _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, 
 
 def lookup_decode_step(hist, row_off, lens, cap, max_len, model_draft, target, state, workspace,
                        match_len, match_end, draft, block, block_len, accept, long_next=None,
-                       append=True, params: Params | None = None, telemetry=None):
+                       append=True, params: Params | None = None, telemetry=None, lens_out=None):
     """One whole decode step (lookup, fusion under state's current mode, greedy
     accept with optional append, scheduler update, optional telemetry) in one
-    kernel.  ``telemetry``: int32 [B,32] counter rows (from alloc_telemetry)."""
+    kernel.  ``lens`` is only read; with ``append`` the lengths after the step
+    go to ``lens_out`` (int32 [B], not overlapping ``lens``; a decode loop
+    alternates the two).  ``telemetry``: int32 [B,32] counter rows (from
+    alloc_telemetry)."""
     p = params or default_params()
     _check("lookup_decode_step", load().lookup_decode_step(*_decode_args(
         hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,
-        match_end, draft, block, block_len, accept, long_next, append, p, telemetry)))
+        match_end, draft, block, block_len, accept, long_next, append, p, telemetry, lens_out)))
 
 
 def lookup_decode_step_timed(hist, row_off, lens, cap, max_len, model_draft, target, state,
                              workspace, match_len, match_end, draft, block, block_len, accept,
                              ev_start, ev_stop, long_next=None, append=True,
-                             params: Params | None = None, telemetry=None):
+                             params: Params | None = None, telemetry=None, lens_out=None):
     """lookup_decode_step with GPU-stamped events around its scan kernel."""
     p = params or default_params()
     _check("lookup_decode_step_timed", load().lookup_decode_step_timed(*_decode_args(
         hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,
-        match_end, draft, block, block_len, accept, long_next, append, p, telemetry),
+        match_end, draft, block, block_len, accept, long_next, append, p, telemetry, lens_out),
         ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
 
 
@@ -394,14 +405,15 @@ def rejection_accept_workspace_bytes(B: int, V: int) -> int:
 
 
 def alloc_rejection_workspace(B: int, V: int, device):
-    """Zero-filled rejection_accept workspace (kept zero by every call)."""
+    """Zero-filled rejection_accept workspace (then kept valid by every call)."""
     import torch
     n = max(rejection_accept_workspace_bytes(B, V), 16)
     return torch.zeros((n + 7) // 8, dtype=torch.int64, device=device)
 
 
 def _rejection_args(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
-                    emitted, model_mask, model_probs, hist, row_off, lens, cap, wg_units):
+                    emitted, model_mask, model_probs, hist, row_off, lens, cap, wg_units,
+                    merge_polls=0):
     import torch
     B = block_len.numel()
     dev = block_len.device
@@ -430,7 +442,7 @@ def _rejection_args(block, block_len, target_probs, u_accept, u_sample, workspac
         ctypes.c_int32(V),
         _dev(u_accept, "u_accept", torch.float64, B * DRAFT_STRIDE, dev),
         _dev(u_sample, "u_sample", torch.int64, B, dev),
-        ctypes.c_int32(B), ctypes.c_int32(int(wg_units)),
+        ctypes.c_int32(B), ctypes.c_int32(int(wg_units)), ctypes.c_int32(int(merge_polls)),
         _dev(workspace, "workspace", workspace.dtype, device=dev),
         ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _dev(accept, "accept", torch.int32, B, dev),
@@ -441,14 +453,16 @@ def _rejection_args(block, block_len, target_probs, u_accept, u_sample, workspac
 
 def rejection_accept(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
                      emitted, model_mask=None, model_probs=None, hist=None, row_off=None,
-                     lens=None, cap=None, wg_units: int = 0):
+                     lens=None, cap=None, wg_units: int = 0, merge_polls: int = 0):
     """Sampled verification with point-mass lookup proposals (include/lcd.h,
     rejection_accept).  target_probs float32 [B,16,V], model_probs float32
     [B,7,V] or None, u_accept float64 [B,15], u_sample int64 [B] (the bits of
     uniform 64-bit words), model_mask int32 [B] or None; writes accept int32
-    [B] and emitted int32 [B,16]; appends when ``hist`` is given."""
+    [B] and emitted int32 [B,16]; appends when ``hist`` is given.
+    ``merge_polls`` is a diagnostic bound of the gathering's wait."""
     args = _rejection_args(block, block_len, target_probs, u_accept, u_sample, workspace, accept,
-                           emitted, model_mask, model_probs, hist, row_off, lens, cap, wg_units)
+                           emitted, model_mask, model_probs, hist, row_off, lens, cap, wg_units,
+                           merge_polls)
     _check("rejection_accept", load().rejection_accept(*args))
 
 

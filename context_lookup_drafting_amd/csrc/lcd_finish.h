@@ -20,13 +20,15 @@
 
 namespace lcd {
 
-// Inputs and outputs of the rest of the decode step.  hist_w and len_w alias
-// the history and its lengths: a request's row is appended to only after
-// every reader of that row in the launch is done with it, and the append lies
-// past every position a lookup of the row reads.
+// Inputs and outputs of the rest of the decode step.  hist_w aliases the
+// history: the append lies past every position a lookup of the row reads.
+// len_out receives the lengths after the step; the scan's decode step takes it
+// apart from the lengths its launch reads (a workgroup may read a row's length
+// after another has finished that row), the index step, whose one wave per
+// request reads and writes only its own row, may pass the same array.
 struct StepIO {
     int32_t *hist_w;
-    int32_t *len_w;
+    int32_t *len_out;
     const int32_t *cap;
     const int32_t *q;
     const int32_t *target;
@@ -56,13 +58,14 @@ __device__ __forceinline__ int load_step_input(int r, int lane, const StepIO &io
     return *src;
 }
 
-// The step after request r's lookup (match length m, row of n >= 0 tokens at
-// ro), run by one whole wave: lane k < 15 holds dk, the draft token of verify
-// slot k (PAD past k_max or without a match); sin holds the step inputs as
-// load_step_input left them and tin the request's telemetry counter of the
-// lane (unused without telemetry).
+// The step after request r's lookup (match length m, -1 when the lookup gave
+// no answer; row of lr tokens as stored, n = max(lr, 0), at ro), run by one
+// whole wave: lane k < 15 holds dk, the draft token of verify slot k (PAD past
+// k_max or without a match); sin holds the step inputs as load_step_input left
+// them and tin the request's telemetry counter of the lane (unused without
+// telemetry).
 __device__ __forceinline__ void finish_step(int r, int m, int dk, int sin, uint32_t tin, int lane,
-                                            int64_t ro, int n, const StepIO &io) {
+                                            int64_t ro, int32_t lr, int n, const StepIO &io) {
     constexpr int kSt = LCD_Q_STRIDE + LCD_TARGET_STRIDE;      // sin lane of the state
     const int qk = sin;                                       // lanes 0..6: proposal
     const int tk = __shfl(sin, LCD_Q_STRIDE + (lane < LCD_TARGET_STRIDE ? lane : 0));
@@ -80,12 +83,10 @@ __device__ __forceinline__ void finish_step(int r, int m, int dk, int sin, uint3
     const unsigned long long miss = __ballot(lane < blk && bk != tk);
     int acc = miss ? (int)__builtin_ctzll(miss) : blk;
     if (io.append) {
-        if ((int64_t)n + acc + 1 > (int64_t)capr) {
-            acc = -1;
-        } else {
-            if (lane <= acc) io.hist_w[ro + n + lane] = tk;
-            if (lane == 0) io.len_w[r] = n + acc + 1;
-        }
+        // a failed append writes nothing and leaves the length as it was
+        if ((int64_t)n + acc + 1 > (int64_t)capr) acc = -1;
+        else if (lane <= acc) io.hist_w[ro + n + lane] = tk;
+        if (lane == 0) io.len_out[r] = acc >= 0 ? n + acc + 1 : lr;
     }
     const bool was_long = st.long_mode != 0;
     const int ln = schedule_row(st, m, acc, blk, io.s);

@@ -61,7 +61,9 @@ constexpr int kMaxProbe = 1 << 20;               // bound on a probe sequence
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Rolling hash of the tokens t_p, t_{p-1}, ... (read backwards from the end
-// position), then a SplitMix64-style finaliser keyed by the length.
+// position), then the SplitMix64 finaliser (Steele, Lea & Flood, "Fast
+// Splittable Pseudorandom Number Generators", OOPSLA 2014: its two
+// xor-shift-multiply rounds and constants), keyed by the length.
 __device__ __forceinline__ u64 roll(u64 h, int32_t t) {
     h = (h ^ (uint32_t)t) * 0x9E3779B97F4A7C15ull;
     return h ^ (h >> 32);
@@ -337,7 +339,7 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
         match_len[r] = m;
         match_end[r] = e;
     }
-    if (kStep) finish_step(r, m, d, sin, tin, lane, ro, n, *iop);
+    if (kStep) finish_step(r, m, d, sin, tin, lane, ro, n0, n, *iop);
 }
 
 // Build: clear the tables, then insert every position p <= n-2 of every row.

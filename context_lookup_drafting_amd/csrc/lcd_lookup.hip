@@ -48,6 +48,12 @@
 //    dependent load.  It finishes the
 //    request with one wave (draft copy and, in the decode step, fusion,
 //    acceptance, append and scheduler update) and re-zeroes the workspace.
+//  * The words carry the call's tag, which the ticket returns with the arrival
+//    count: the gatherer takes only words of its own call, and starts the
+//    next call's tag when it resets the count.  Its wait is bounded all the
+//    same; when the bound runs out the request reports match_len = -1 (no
+//    answer, an error) and a slot published later carries a tag no later call
+//    accepts.
 //
 // No MFMA: the work is integer compares on a stream; HBM bandwidth and memory
 // latency bound it.
@@ -91,15 +97,16 @@ typedef unsigned long long u64;
 constexpr int kLenShift = 31;
 constexpr u64 kEndMask = (1ull << kLenShift) - 1;
 
-// Workspace of one request: the arrival-ticket counter, a pad word, then one
-// slot per workgroup of 16 words: units 0..14 hold the staged draft tokens as
-// kTokValid | token, unit 15 holds kKeyValid | key.  Zero means "not written".
+// Workspace of one request: the header word (arrival count in bits 0..31,
+// the call's epoch above), a pad word, then one slot per workgroup of 16
+// words: units 0..14 hold the staged draft tokens as tag << 32 | token, unit
+// 15 holds tag << 36 | key, where tag = epoch + 1 (1 .. 2^28 - 1).  A zero
+// word is "not written" for every tag.
 constexpr int kMaxCpr = 64;                               // workgroups per request, at most
 constexpr int kSlotWords = 16;
 constexpr int kReqWords = 2 + kMaxCpr * kSlotWords;
-constexpr u64 kKeyValid = 1ull << 63;
-constexpr u64 kTokValid = 1ull << 32;
-constexpr int kPollMax = 1 << 20;                         // gathering polls, at most
+constexpr u64 kTagLimit = (1ull << 28) - 1;               // epochs 0 .. kTagLimit - 1
+constexpr int kPollMax = 1 << 20;                         // gathering polls, at most (default)
 constexpr int kBufferWord3 = 0x00020000;                  // gfx9 buffer descriptor, dword 3
 constexpr int kNoTile = 1 << 19;                          // a tile index past every descriptor
 constexpr int kFullAfter = 4;                             // flagged tiles before a wave drops the quick test
@@ -111,7 +118,16 @@ struct ScanArgs {
     int32_t B;                 // requests
     int32_t wgs;               // workgroups per launch (token-balanced chunks)
     int32_t waves;             // waves per workgroup (kWavesSmall or kWavesLarge)
+    int32_t polls;             // gathering polls before giving up
 };
+
+// Tag of the call whose ticket returned header word h, and the header that
+// starts the next call (count 0, next epoch).
+__device__ __forceinline__ u64 call_tag(u64 h) { return (h >> 32) + 1; }
+__device__ __forceinline__ u64 next_header(u64 h) {
+    const u64 e = (h >> 32) + 1;
+    return (e < kTagLimit ? e : 0) << 32;
+}
 
 // Token-balanced chunks (ragged batches): one chunk length for the whole
 // batch, from the total and the longest row's candidate ends and the grid of
@@ -264,17 +280,20 @@ __device__ __forceinline__ u64 wave_max(u64 v) {
     return v;
 }
 
-// Result of request r (row of n >= 0 tokens at ro) given its best key, run by
-// one whole wave: lane k < 15 holds tok = h[e+1+min(k, D-1)], D = n-1-e, the
-// tokens following the match.  Writes the match and draft and, in kStep mode,
-// the rest of the step (sin: the per-lane step inputs).
+// Result of request r (row of lr tokens as stored, n = max(lr, 0), at ro)
+// given its best key, run by one whole wave: lane k < 15 holds tok =
+// h[e+1+min(k, D-1)], D = n-1-e, the tokens following the match.  Writes the
+// match and draft and, in kStep mode, the rest of the step (sin: the per-lane
+// step inputs).  `failed`: the merge gave up, reported as m = -1, e = -1 and
+// an empty draft (the step then goes on as without a match).
 template <int kMode>
-__device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin, uint32_t tin, int lane,
-                                               int64_t ro, int n, int k_max,
-                                               int32_t *__restrict__ match_len,
+__device__ __forceinline__ void finish_request(int r, u64 key, bool failed, int tok, int sin,
+                                               uint32_t tin, int lane, int64_t ro, int32_t lr, int n,
+                                               int k_max, int32_t *__restrict__ match_len,
                                                int32_t *__restrict__ match_end,
                                                int32_t *__restrict__ draft, const StepIO &io) {
-    const int m = key ? (int)(key >> kLenShift) : 0;
+    if (failed) key = 0;
+    const int m = failed ? -1 : (key ? (int)(key >> kLenShift) : 0);
     const int e = key ? (int)(key & kEndMask) : -1;
     const int D = key ? n - 1 - e : 1;
     // LZ-style copy: d[k] = h[n - D + (k mod D)], the tok of lane (k mod D)
@@ -286,7 +305,7 @@ __device__ __forceinline__ void finish_request(int r, u64 key, int tok, int sin,
         match_len[r] = m;
         match_end[r] = e;
     }
-    if (kMode == kStep) finish_step(r, m, dk, sin, tin, lane, ro, n, io);
+    if (kMode == kStep) finish_step(r, m, dk, sin, tin, lane, ro, lr, n, io);
 }
 
 constexpr int kBalPer = LCD_BALANCE_MAX_B / 64;           // lengths held per lane
@@ -401,7 +420,7 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
     const int nc = n - 1;             // candidate ends 0..n-2
     if (nc <= 0) {                    // no earlier position: chunk 0 finishes the request
         if (c0 == 0 && wave == 0)
-            finish_request<kMode>(r, 0, 0, sin, tin, lane, ro, n, a.k_max, op->match_len,
+            finish_request<kMode>(r, 0, false, 0, sin, tin, lane, ro, lr, n, a.k_max, op->match_len,
                                   op->match_end, op->draft, op->io);
         return;
     }
@@ -410,10 +429,11 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
     const int P = contrib < cpr ? contrib : cpr;      // workgroups taking part
     const int J = a.l_max;
     u64 *__restrict__ req = ws + (int64_t)r * kReqWords;
-    // Arrival ticket of this workgroup, taken by lane 0 and read back only at
-    // the end (from lane 0): the other lanes' value is left unspecified so
-    // that no register copy of the result -- which would wait for it -- is
-    // needed here.
+    // Arrival ticket of this workgroup (the header word before its add: the
+    // count of earlier arrivals and the call's epoch), taken by lane 0 and
+    // read back only at the end (from lane 0): the other lanes' value is left
+    // unspecified so that no register copy of the result -- which would wait
+    // for it -- is needed here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wsometimes-uninitialized"
 #pragma clang diagnostic ignored "-Wuninitialized"
@@ -636,10 +656,13 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
     int tok = s_wtok[wbest * kSlotWords + (lane < kSlotWords ? lane : 0)];
     if (P > 1) {
         u64 *__restrict__ slots = req + 2;
-        const int my_ticket = uni((int)ticket);    // lane 0 took it (P > 1)
+        // lane 0 took the ticket (P > 1): the arrival count and the call's tag
+        const u64 hdr = ((u64)(uint32_t)__builtin_amdgcn_readfirstlane((int)(ticket >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ticket);
 #pragma clang diagnostic pop
-        if (my_ticket != P - 1) {                  // not the last to start: publish, leave
-            const u64 unit = lane < kSlotWords - 1 ? (kTokValid | (u64)(uint32_t)tok) : (kKeyValid | key);
+        const u64 tag = call_tag(hdr);
+        if ((int)(uint32_t)hdr != P - 1) {          // not the last to start: publish, leave
+            const u64 unit = lane < kSlotWords - 1 ? ((tag << 32) | (u64)(uint32_t)tok) : ((tag << 36) | key);
             if (lane < kSlotWords)
                 __hip_atomic_store(slots + c0 * kSlotWords + lane, unit, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -650,13 +673,14 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         // own key and tokens stay in registers.
         const int nu = P * kSlotWords;
         bool all = false;
-        for (int tries = 0; tries < kPollMax && !all; ++tries) {
+        for (int tries = 0; tries < a.polls && !all; ++tries) {
             bool ok = true;
             for (int u = lane; u < nu; u += 64) {
                 if (u / kSlotWords != c0) {
                     const u64 v = __hip_atomic_load(slots + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     s_units[u] = v;
-                    ok = ok && (v != 0);
+                    const bool is_key = (u & (kSlotWords - 1)) == kSlotWords - 1;
+                    ok = ok && ((v >> (is_key ? 36 : 32)) == tag);
                 }
             }
             all = ballot(!ok) == 0;
@@ -664,9 +688,10 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         // best key over the slots (keys of different slots differ unless zero):
         // a scalar pass over the P slot keys, which are few (a 64-bit wave-wide
         // shuffle reduction is six dependent LDS round trips)
+        const u64 kKeyMask = (1ull << 36) - 1;
         const u64 ks = lane >= P ? 0
                        : lane == c0 ? key
-                                    : (s_units[lane * kSlotWords + kSlotWords - 1] & ~kKeyValid);
+                                    : (s_units[lane * kSlotWords + kSlotWords - 1] & kKeyMask);
         u64 kbest = 0;
         int w = c0;
         for (int j = 0; j < P; ++j) {
@@ -676,19 +701,20 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         }
         if (kbest == 0) w = c0;
         if (w != c0) tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
-        key = all ? kbest : 0;                      // gathering gave up: report no match
-        finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, op->match_len,
+        finish_request<kMode>(r, kbest, !all, tok, sin, tin, lane, ro, lr, n, a.k_max, op->match_len,
                               op->match_end, op->draft, op->io);
-        // Re-zero the request's workspace for the next call, after the
-        // outputs: a wait for these stores' acknowledgement must not sit in
-        // front of the finish.
-        for (int u = lane; u < nu; u += 64)
-            __hip_atomic_store(slots + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Re-zero the slots for the next call (after the outputs: a wait for
+        // these stores' acknowledgement must not sit in front of the finish),
+        // unless the gathering gave up: a late publisher may still write into
+        // them, and its words keep this call's tag, which no later call takes.
+        if (all)
+            for (int u = lane; u < nu; u += 64)
+                __hip_atomic_store(slots + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(req, next_header(hdr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    finish_request<kMode>(r, key, tok, sin, tin, lane, ro, n, a.k_max, op->match_len, op->match_end,
-                          op->draft, op->io);
+    finish_request<kMode>(r, key, false, tok, sin, tin, lane, ro, lr, n, a.k_max, op->match_len,
+                          op->match_end, op->draft, op->io);
 }
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
@@ -785,7 +811,7 @@ int balanced_wgs(int32_t B, int32_t max_len, int32_t scan_wgs) {
     return (int)g;
 }
 
-ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
+ScanArgs scan_shape(int32_t B, int32_t max_len, const lcd_params *p) {
     if (p->scan_balance == 1 && B <= LCD_BALANCE_MAX_B)
         return ScanArgs{0, 0, p->l_min, p->l_max, p->k_max, B, balanced_wgs(B, max_len, p->scan_wgs),
                         kWavesSmall};
@@ -822,6 +848,14 @@ ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
     return ScanArgs{cpr, chunk_len(max_len, cpr), p->l_min, p->l_max, p->k_max, B, 0, kWavesSmall};
 }
 
+// The launch shape and the bound on the merge's wait (merge_polls: 0 = the
+// default, -1 = no poll at all, a diagnostic that makes every merge give up).
+ScanArgs scan_args(int32_t B, int32_t max_len, const lcd_params *p) {
+    ScanArgs sa = scan_shape(B, max_len, p);
+    sa.polls = p->merge_polls == 0 ? kPollMax : (p->merge_polls < 0 ? 0 : p->merge_polls);
+    return sa;
+}
+
 int propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
             int32_t max_len, const lcd_params *p, void *workspace, int32_t *match_len,
             int32_t *match_end, int32_t *draft, void *stream, hipEvent_t ev0, hipEvent_t ev1) {
@@ -845,24 +879,34 @@ size_t workspace_bytes(int32_t B) {
     return B > 0 ? (size_t)B * kReqWords * sizeof(u64) : 0;
 }
 
-int decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap, int32_t B,
-                int32_t max_len, const int32_t *model_draft, const int32_t *target,
-                lcd_sched_state *state, const lcd_params *p, void *workspace, size_t ws_bytes,
-                int32_t *match_len, int32_t *match_end, int32_t *draft, int32_t *block,
-                int32_t *block_len, int32_t *accept, int32_t *long_next, uint32_t *tele,
-                int32_t append, void *stream, hipEvent_t ev0, hipEvent_t ev1) {
+// True when the int32 arrays [a, a+B) and [b, b+B) share an element.
+bool overlaps(const int32_t *a, const int32_t *b, int32_t B) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    const uintptr_t bytes = (uintptr_t)B * sizeof(int32_t);
+    return x < y + bytes && y < x + bytes;
+}
+
+int decode_step(int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t *len_out,
+                const int32_t *cap, int32_t B, int32_t max_len, const int32_t *model_draft,
+                const int32_t *target, lcd_sched_state *state, const lcd_params *p, void *workspace,
+                size_t ws_bytes, int32_t *match_len, int32_t *match_end, int32_t *draft,
+                int32_t *block, int32_t *block_len, int32_t *accept, int32_t *long_next,
+                uint32_t *tele, int32_t append, void *stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (B < 0 || p == nullptr || max_len < 0) return LCD_EINVAL;
     if (lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
     if (!hist || !row_off || !len || !model_draft || !target || !state || !workspace ||
         !match_len || !match_end || !draft || !block || !block_len || !accept)
         return LCD_EINVAL;
-    if (append && !cap) return LCD_EINVAL;
+    // Appending needs the capacities and a length array apart from the one
+    // the launch reads: a workgroup may read a row's length after another
+    // workgroup has finished that row.
+    if (append && (!cap || !len_out || overlaps(len, len_out, B))) return LCD_EINVAL;
     if (((uintptr_t)hist & 15u) != 0 || ((uintptr_t)workspace & 15u) != 0) return LCD_EINVAL;
     if (ws_bytes < workspace_bytes(B)) return LCD_EINVAL;
 
     const int pf = p->l_min < 4 ? p->l_min : 4;
-    StepIO io{hist, len, cap, model_draft, target, state, block, block_len, accept, long_next,
+    StepIO io{hist, len_out, cap, model_draft, target, state, block, block_len, accept, long_next,
               tele, fuse_args(p), sched_args(p), append ? 1 : 0};
     const hipError_t err = launch_scan<kStep>(pf, hist, row_off, len, B, scan_args(B, max_len, p),
                                               reinterpret_cast<u64 *>(workspace), match_len,
@@ -959,22 +1003,23 @@ extern "C" size_t lcd_decode_step_workspace_bytes(int32_t B, int32_t max_len, co
     return p != nullptr ? lcd::workspace_bytes(B) : 0;
 }
 
-extern "C" int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len,
-                                  const int32_t *cap, int32_t B, int32_t max_len,
+extern "C" int lookup_decode_step(int32_t *hist, const int64_t *row_off, const int32_t *len,
+                                  int32_t *len_out, const int32_t *cap, int32_t B, int32_t max_len,
                                   const int32_t *model_draft, const int32_t *target,
                                   lcd_sched_state *state, const lcd_params *p, void *workspace,
                                   size_t workspace_bytes, int32_t *match_len, int32_t *match_end,
                                   int32_t *draft, int32_t *block, int32_t *block_len,
                                   int32_t *accept, int32_t *long_next, uint32_t *telemetry,
                                   int32_t append, void *stream) {
-    return lcd::decode_step(hist, row_off, len, cap, B, max_len, model_draft, target, state, p,
+    return lcd::decode_step(hist, row_off, len, len_out, cap, B, max_len, model_draft, target, state, p,
                             workspace, workspace_bytes, match_len, match_end, draft, block,
                             block_len, accept, long_next, telemetry, append, stream, nullptr,
                             nullptr);
 }
 
-extern "C" int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len,
-                                        const int32_t *cap, int32_t B, int32_t max_len,
+extern "C" int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, const int32_t *len,
+                                        int32_t *len_out, const int32_t *cap, int32_t B,
+                                        int32_t max_len,
                                         const int32_t *model_draft, const int32_t *target,
                                         lcd_sched_state *state, const lcd_params *p,
                                         void *workspace, size_t workspace_bytes,
@@ -982,7 +1027,7 @@ extern "C" int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, i
                                         int32_t *block, int32_t *block_len, int32_t *accept,
                                         int32_t *long_next, uint32_t *telemetry, int32_t append,
                                         void *stream, void *ev_start, void *ev_stop) {
-    return lcd::decode_step(hist, row_off, len, cap, B, max_len, model_draft, target, state, p,
+    return lcd::decode_step(hist, row_off, len, len_out, cap, B, max_len, model_draft, target, state, p,
                             workspace, workspace_bytes, match_len, match_end, draft, block,
                             block_len, accept, long_next, telemetry, append, stream,
                             reinterpret_cast<hipEvent_t>(ev_start),

@@ -26,7 +26,9 @@
 // token in three wave-wide steps (lane ranges, then units, then the 16 floats
 // of one lane) -- integer sums are exact, so the order of summation never
 // changes the token.  It then writes the accepted count, the emitted tokens and
-// the append, and re-zeroes the workspace.
+// the append, and re-zeroes the workspace.  Published sums carry the call's
+// tag (from the ticket, as in the lookup merge), so a sum published after a
+// gathering gave up (accept = -1) is never taken by a later call.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -42,8 +44,13 @@ using u64 = unsigned long long;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnit = 1024;                 // floats per unit: 4 x (64 lanes x 4 floats)
-constexpr u64 kSumValid = 1ull << 63;       // tag of a published unit sum (sums < 2^51)
-constexpr int kPollMax = 1 << 20;           // bound on the gathering's polls
+// A published unit sum (at most 1024 * 2^40 = 2^50) is tag << 51 | sum, tag =
+// epoch + 1 in 1 .. 8191; the request's header word holds the arrival count in
+// bits 0..31 and the epoch above.  Zero is "not published" for every tag.
+constexpr int kTagShift = 51;
+constexpr u64 kSumMask = (1ull << kTagShift) - 1;
+constexpr u64 kTagLimit = (1ull << (64 - kTagShift)) - 1;   // epochs 0 .. kTagLimit - 1
+constexpr int kPollMax = 1 << 20;           // bound on the gathering's polls (default)
 constexpr int kBufferWord3 = 0x00020000;    // gfx9 buffer descriptor, dword 3
 
 // Kinds of the distribution a request draws from.
@@ -51,6 +58,7 @@ constexpr int kPlain = 0;                   // the target row p_a itself
 constexpr int kPointResidual = 1;           // p_a without the rejected token x
 constexpr int kModelResidual = 2;           // max(p_a - q_a, 0)
 constexpr int kKeep = 4;                    // unit sums a lane keeps in registers (U <= 256)
+constexpr int kMaxUpw = 256;                // units per workgroup, at most
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -119,6 +127,7 @@ struct SampleArgs {
     int32_t U;                   // units per row, ceil(V / 1024)
     int32_t upw;                 // units per workgroup
     int32_t G;                   // workgroups per request
+    int32_t polls;               // gathering polls before giving up
 };
 
 struct SampleIO {
@@ -241,18 +250,26 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     // ---- stream this workgroup's units -----------------------------------
     const int u0 = c * sa.upw;
     const int u1 = min(u0 + sa.upw, sa.U);
+    // The unit sums wait in LDS until the workgroup's ticket -- and with it the
+    // call's tag -- is in: wave 0 publishes them all after the barrier.
+    __shared__ u64 s_sums[kMaxUpw];
     for (int u = u0 + wave; u < u1; u += kWaves) {
         u64 s = unit_sum(prs, qrs, u, lane, model);
         if (u == u_rej) s -= w_rej;
-        if (lane == 0)
-            __hip_atomic_store(sums + u, kSumValid | s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) s_sums[u - u0] = s;
     }
+    __syncthreads();
+    if (wave != 0) return;
+    // lane 0 took the ticket: the arrival count and the call's epoch
+    const u64 hdr = ((u64)(uint32_t)__builtin_amdgcn_readfirstlane((int)(ticket >> 32)) << 32) |
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ticket);
+    const u64 tagged = ((hdr >> 32) + 1) << kTagShift;   // this call's tag, in place
+    for (int k = lane; k < u1 - u0; k += 64)
+        __hip_atomic_store(sums + u0 + k, tagged | s_sums[k], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- only the last workgroup of the request to start goes on ------------
-    __shared__ int s_last;
-    if (tid == 0) s_last = (int)ticket == sa.G - 1;
-    __syncthreads();
-    if (!s_last || wave != 0) return;
+    if ((int)(uint32_t)hdr != sa.G - 1) return;
 
     // Every other workgroup of the request has started and publishes without
     // waiting for anything, so this gathering ends (bounded all the same).
@@ -262,7 +279,9 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     u64 kept[kKeep];
     u64 lsum = 0;
     bool all = false;
-    for (int tries = 0; tries < kPollMax && !all; ++tries) {
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k) kept[k] = 0;
+    for (int tries = 0; tries < sa.polls && !all; ++tries) {
         bool ok = true;
         lsum = 0;
         if (n <= kKeep) {
@@ -271,18 +290,18 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
             for (int k = 0; k < kKeep; ++k)
                 kept[k] = ua + k < ub ? __hip_atomic_load(sums + ua + k, __ATOMIC_RELAXED,
                                                           __HIP_MEMORY_SCOPE_AGENT)
-                                      : kSumValid;
+                                      : tagged;
 #pragma unroll
             for (int k = 0; k < kKeep; ++k) {
-                ok = ok && (kept[k] != 0);
-                kept[k] &= ~kSumValid;
+                ok = ok && ((kept[k] & ~kSumMask) == tagged);
+                kept[k] &= kSumMask;
                 lsum += kept[k];
             }
         } else {
             for (int u = ua; u < ub; ++u) {
                 const u64 v = __hip_atomic_load(sums + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = ok && (v != 0);
-                lsum += v & ~kSumValid;
+                ok = ok && ((v & ~kSumMask) == tagged);
+                lsum += v & kSumMask;
             }
         }
         all = __ballot(!ok) == 0;
@@ -306,7 +325,7 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
         for (int u = 0; u < sa.U; ++u) {
             const u64 s = unit_sum(prs, qrs, u, lane, false);
             if (lane == 0)
-                __hip_atomic_store(sums + u, kSumValid | s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sums + u, tagged | s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (u >= ua && u < ub) {
                 lsum += s;
 #pragma unroll
@@ -338,7 +357,7 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
             }
         } else if (lane < n && ub0 + lane < sa.U) {
             us = __hip_atomic_load(sums + ub0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
-                 ~kSumValid;
+                 kSumMask;
         }
         if (lane >= n || ub0 + lane >= sa.U) us = 0;
         const u64 uincl = wave_scan(us) + before_l;
@@ -379,10 +398,17 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     }
     if (!all) z = -1;                       // gathering gave up: the request emits nothing
 
-    // re-zero the request's workspace for the next call
-    for (int u = lane; u < sa.U; u += 64)
-        __hip_atomic_store(sums + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) __hip_atomic_store(req, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Re-zero the unit sums for the next call, unless the gathering gave up (a
+    // late publisher may still write, with this call's tag, which no later
+    // call takes); reset the count and start the next epoch.
+    if (all)
+        for (int u = lane; u < sa.U; u += 64)
+            __hip_atomic_store(sums + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+        const u64 e = (hdr >> 32) + 1;
+        __hip_atomic_store(req, (e < kTagLimit ? e : 0) << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // emitted tokens: block[0..a-1], then z; the append as greedy acceptance does it
     const bool drew = z >= 0;
@@ -403,18 +429,20 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
 }
 
 // Units per workgroup: about 2048 workgroups per launch, at least one unit per
-// wave, a multiple of the wave count.
+// wave, a multiple of the wave count, at most kMaxUpw.
 int pick_units_per_wg(int B, int U, int wg_units) {
     if (wg_units > 0) return wg_units;
     const int64_t total = (int64_t)B * U;
-    int upw = (int)((total + 2047) / 2048);
+    int64_t upw = (total + 2047) / 2048;
     upw = (upw + kWaves - 1) / kWaves * kWaves;
-    return upw < kWaves ? kWaves : upw;
+    if (upw > kMaxUpw) upw = kMaxUpw;
+    return upw < kWaves ? kWaves : (int)upw;
 }
 
-int launch(const SampleIO &io, int32_t B, int32_t V, int32_t wg_units, void *workspace,
-           size_t workspace_bytes, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+int launch(const SampleIO &io, int32_t B, int32_t V, int32_t wg_units, int32_t merge_polls,
+           void *workspace, size_t workspace_bytes, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     SampleArgs sa;
+    sa.polls = merge_polls == 0 ? kPollMax : (merge_polls < 0 ? 0 : merge_polls);
     sa.V = V;
     sa.U = (V + kUnit - 1) / kUnit;
     sa.upw = pick_units_per_wg(B, sa.U, wg_units);
@@ -433,11 +461,11 @@ int launch(const SampleIO &io, int32_t B, int32_t V, int32_t wg_units, void *wor
 int sample_entry(const int32_t *block, const int32_t *block_len, const uint32_t *model_mask,
                  const float *target_probs, const float *model_probs, int32_t V,
                  const double *u_accept, const uint64_t *u_sample, int32_t B, int32_t wg_units,
-                 void *workspace, size_t workspace_bytes, int32_t *accept, int32_t *emitted,
-                 int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap,
-                 void *stream, void *ev0, void *ev1) {
+                 int32_t merge_polls, void *workspace, size_t workspace_bytes, int32_t *accept,
+                 int32_t *emitted, int32_t *hist, const int64_t *row_off, int32_t *len,
+                 const int32_t *cap, void *stream, void *ev0, void *ev1) {
     if (B < 0 || V < 4 || V > LCD_SAMPLE_MAX_VOCAB || (V & 3) != 0 || wg_units < 0 ||
-        wg_units > (1 << 20))
+        wg_units > kMaxUpw || merge_polls < -1)
         return LCD_EINVAL;
     if (B == 0) return LCD_OK;
     if (!block || !block_len || !target_probs || !u_accept || !u_sample || !accept || !emitted ||
@@ -451,7 +479,7 @@ int sample_entry(const int32_t *block, const int32_t *block_len, const uint32_t 
     if ((int64_t)B * ((V + kUnit - 1) / kUnit) > (int64_t)1 << 31) return LCD_EINVAL;
     SampleIO io{block, block_len, model_mask, target_probs, model_probs, u_accept, u_sample,
                 accept, emitted, hist, row_off, len, cap};
-    return launch(io, B, V, wg_units, workspace, workspace_bytes,
+    return launch(io, B, V, wg_units, merge_polls, workspace, workspace_bytes,
                   reinterpret_cast<hipStream_t>(stream), reinterpret_cast<hipEvent_t>(ev0),
                   reinterpret_cast<hipEvent_t>(ev1));
 }
@@ -469,23 +497,24 @@ extern "C" int rejection_accept(const int32_t *block, const int32_t *block_len,
                                 const uint32_t *model_mask, const float *target_probs,
                                 const float *model_probs, int32_t V, const double *u_accept,
                                 const uint64_t *u_sample, int32_t B, int32_t wg_units,
-                                void *workspace, size_t workspace_bytes, int32_t *accept,
-                                int32_t *emitted, int32_t *hist, const int64_t *row_off,
-                                int32_t *len, const int32_t *cap, void *stream) {
+                                int32_t merge_polls, void *workspace, size_t workspace_bytes,
+                                int32_t *accept, int32_t *emitted, int32_t *hist,
+                                const int64_t *row_off, int32_t *len, const int32_t *cap,
+                                void *stream) {
     return lcd::sample_entry(block, block_len, model_mask, target_probs, model_probs, V, u_accept,
-                             u_sample, B, wg_units, workspace, workspace_bytes, accept, emitted,
-                             hist, row_off, len, cap, stream, nullptr, nullptr);
+                             u_sample, B, wg_units, merge_polls, workspace, workspace_bytes, accept,
+                             emitted, hist, row_off, len, cap, stream, nullptr, nullptr);
 }
 
 extern "C" int rejection_accept_timed(const int32_t *block, const int32_t *block_len,
                                       const uint32_t *model_mask, const float *target_probs,
                                       const float *model_probs, int32_t V, const double *u_accept,
                                       const uint64_t *u_sample, int32_t B, int32_t wg_units,
-                                      void *workspace, size_t workspace_bytes, int32_t *accept,
-                                      int32_t *emitted, int32_t *hist, const int64_t *row_off,
-                                      int32_t *len, const int32_t *cap, void *stream,
-                                      void *ev_start, void *ev_stop) {
+                                      int32_t merge_polls, void *workspace, size_t workspace_bytes,
+                                      int32_t *accept, int32_t *emitted, int32_t *hist,
+                                      const int64_t *row_off, int32_t *len, const int32_t *cap,
+                                      void *stream, void *ev_start, void *ev_stop) {
     return lcd::sample_entry(block, block_len, model_mask, target_probs, model_probs, V, u_accept,
-                             u_sample, B, wg_units, workspace, workspace_bytes, accept, emitted,
-                             hist, row_off, len, cap, stream, ev_start, ev_stop);
+                             u_sample, B, wg_units, merge_polls, workspace, workspace_bytes, accept,
+                             emitted, hist, row_off, len, cap, stream, ev_start, ev_stop);
 }

@@ -48,6 +48,7 @@ class LookupDrafter:
         self.block_len = torch.empty(self.B, **i32)
         self.accept = torch.empty(self.B, **i32)
         self.long_next = torch.empty(self.B, **i32)
+        self.lens_next = torch.empty(self.B, **i32)
         self.telemetry = alloc_telemetry(self.B, dev) if telemetry else None
         self.index = LookupIndex(index_cap, dev, self.params) if index_cap is not None else None
         self._rej_ws = None
@@ -82,7 +83,11 @@ class LookupDrafter:
         """One greedy decode step in one kernel (lookup, fusion, acceptance,
         append, scheduler update; telemetry when enabled): lookup_decode_step,
         or lookup_index_decode_step with the index.  ``separate`` runs the
-        index path as its four entry points instead (same outputs)."""
+        index path as its four entry points instead (same outputs).  ``lens``
+        is updated in place: lookup_decode_step writes the new lengths to the
+        drafter's second length array, which is then copied into ``lens`` on
+        the same stream (callers that alternate two arrays themselves call
+        lookup_decode_step directly)."""
         if self.index is not None and not separate:
             self.index.decode_step(hist, row_off, lens, cap, model_draft, target, self.state,
                                    self.match_len, self.match_end, self.draft, self.block,
@@ -108,7 +113,10 @@ class LookupDrafter:
             lookup_decode_step(hist, row_off, lens, cap, self.max_len, model_draft, target,
                                self.state, self.decode_ws, self.match_len, self.match_end,
                                self.draft, self.block, self.block_len, self.accept,
-                               self.long_next, append, self.params, telemetry=self.telemetry)
+                               self.long_next, append, self.params, telemetry=self.telemetry,
+                               lens_out=self.lens_next if append else None)
+            if append:
+                lens.copy_(self.lens_next)
         return dict(match_len=self.match_len, match_end=self.match_end, draft=self.draft,
                     block=self.block, block_len=self.block_len, accept=self.accept,
                     long_next=self.long_next)

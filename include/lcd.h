@@ -20,8 +20,9 @@
  * required, parameters out of range) -- nothing is launched; LCD_EHIP when the
  * HIP runtime reports a launch error.  B == 0 is a no-op returning LCD_OK.
  * Errors in device data cannot be seen by the host: lengths are clamped at 0,
- * and an append that would overflow a row's capacity is reported per request
- * (accept = -1) without writing.
+ * an append that would overflow a row's capacity is reported per request
+ * (accept = -1) without writing, and a lookup whose cross-workgroup merge gave
+ * up waiting (see merge_polls) is reported per request as match_len = -1.
  */
 #ifndef LCD_H
 #define LCD_H
@@ -70,6 +71,14 @@ extern "C" {
  *                 batches use equal chunks per row); 0 = every row is cut into
  *                 the same number of chunks, sized from max_len.  Results never
  *                 depend on it.
+ *   merge_polls   diagnostics: how often the workgroup that completes a
+ *                 request's lookup polls the other workgroups' results before
+ *                 it gives up (0 = the default, 2^20; -1 = not at all, which
+ *                 makes every request scanned by several workgroups give up).
+ *                 The wait always ends in practice -- every workgroup polled
+ *                 for has started and publishes without waiting -- so the
+ *                 bound is a safety net; a request whose merge gave up
+ *                 reports match_len = -1 (an error, not a lookup result).
  */
 typedef struct lcd_params {
     int32_t l_min, l_max, k_max;
@@ -78,6 +87,7 @@ typedef struct lcd_params {
     int32_t entry_steps, sticky, near_full_slack;
     int32_t scan_wgs;
     int32_t scan_balance;
+    int32_t merge_polls;
 } lcd_params;
 
 /* Largest batch the token-balanced scan (scan_balance = 1) handles. */
@@ -94,14 +104,20 @@ void lcd_default_params(lcd_params *p);
 /* Returns LCD_OK when *p is in range, LCD_EINVAL otherwise (host only). */
 int lcd_check_params(const lcd_params *p);
 
-/* Device workspace per request: an arrival counter and one 128-byte slot for
- * each of up to 64 workgroups scanning the request. */
+/* Device workspace per request: a header word (arrival count and call epoch),
+ * a pad word and one 128-byte slot for each of up to 64 workgroups scanning
+ * the request. */
 #define LCD_WORKSPACE_PER_REQUEST 8208
 
 /* Bytes of device workspace lookup_propose needs for B requests
  * (B * LCD_WORKSPACE_PER_REQUEST).  The workspace must be zero-filled once
- * before its first use; every completed call leaves it zero-filled again.
- * Concurrent calls must not share a workspace. */
+ * before its first use and is then kept valid by the calls themselves: each
+ * call leaves every arrival count (bits 0..31 of a request's header word) and
+ * every slot it gathered at zero, and advances the request's epoch (the
+ * header's upper bits), which tags the slots' words so that a call only takes
+ * words of its own.  A merge that gave up (match_len = -1) may see its slots
+ * written after it returned; their tag is never taken again.  Concurrent calls
+ * must not share a workspace. */
 size_t lcd_workspace_bytes(int32_t B);
 
 /*
@@ -114,7 +130,9 @@ size_t lcd_workspace_bytes(int32_t B);
  * the latest such e on ties (the longest current suffix of l_min..l_max
  * tokens and its most recent earlier occurrence; the occurrence may overlap
  * the suffix).  Outputs:
- *   match_len[r] = that length m, or 0 when there is none;
+ *   match_len[r] = that length m, or 0 when there is none, or -1 when the
+ *     merge of the workgroups scanning the row gave up (see merge_polls; the
+ *     draft is then all LCD_PAD);
  *   match_end[r] = e (an index into the row), or -1;
  *   draft[r*15 + k] = h[n - D + (k mod D)] for k < k_max with D = n-1-e
  *     (the tokens following the occurrence, copied LZ77-style, so an
@@ -217,10 +235,20 @@ int lookup_schedule_step(lcd_sched_state *state, const int32_t *match_len,
  * losslessness, as for the four calls.)  One kernel: the workgroups covering a
  * request merge their match keys in `workspace`, and the one whose merge
  * completes the request copies the draft, fuses, accepts, appends and
- * schedules it.
+ * schedules it.  A request whose merge gave up (match_len = -1) is fused,
+ * accepted and scheduled as one without a match.
  *
- * hist, row_off, len, cap   as for lookup_propose / greedy_accept; cap may be
- *                           NULL when append == 0 (then hist and len are only read)
+ * hist, row_off, cap        as for lookup_propose / greedy_accept; cap may be
+ *                           NULL when append == 0 (then hist is only read)
+ * len                       int32[B], the lengths the step reads; never written
+ * len_out                   int32[B]; when append != 0 it receives every
+ *                           request's length after the step (len[r] + a + 1,
+ *                           with len[r] read as max(len[r], 0), or len[r]
+ *                           unchanged when the append failed); it must not
+ *                           overlap len, because a workgroup may read a row's
+ *                           length after another has finished that row -- a
+ *                           decode loop alternates two length arrays.  Not
+ *                           touched (may be NULL) when append == 0.
  * model_draft int32[B*7], target int32[B*16]
  * state       lcd_sched_state[B], in/out; its long_mode selects this step's block
  * workspace   lcd_decode_step_workspace_bytes(B, max_len, p) bytes (as for
@@ -230,11 +258,15 @@ int lookup_schedule_step(lcd_sched_state *state, const int32_t *match_len,
  * outputs     match_len, match_end int32[B]; draft, block int32[B*15];
  *             block_len, accept int32[B]; long_next int32[B] (nullable)
  * telemetry   uint32[B * LCD_TELE_WORDS] (nullable), see lookup_telemetry_update
+ * Errors: LCD_EINVAL for the misuse lookup_propose rejects, a NULL
+ * model_draft, target, state, block, block_len or accept, a workspace smaller
+ * than lcd_decode_step_workspace_bytes, or append != 0 with a NULL cap or
+ * len_out or a len_out that overlaps len; LCD_EHIP on a launch failure.
  */
 size_t lcd_decode_step_workspace_bytes(int32_t B, int32_t max_len, const lcd_params *p);
 
-int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap,
-                       int32_t B, int32_t max_len, const int32_t *model_draft,
+int lookup_decode_step(int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t *len_out,
+                       const int32_t *cap, int32_t B, int32_t max_len, const int32_t *model_draft,
                        const int32_t *target, lcd_sched_state *state, const lcd_params *p,
                        void *workspace, size_t workspace_bytes, int32_t *match_len,
                        int32_t *match_end, int32_t *draft, int32_t *block, int32_t *block_len,
@@ -243,8 +275,8 @@ int lookup_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len, cons
 
 /* lookup_decode_step with GPU-stamped events around its scan kernel (see
  * lookup_propose_timed); for profiling only. */
-int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len,
-                             const int32_t *cap, int32_t B, int32_t max_len,
+int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, const int32_t *len,
+                             int32_t *len_out, const int32_t *cap, int32_t B, int32_t max_len,
                              const int32_t *model_draft, const int32_t *target,
                              lcd_sched_state *state, const lcd_params *p, void *workspace,
                              size_t workspace_bytes, int32_t *match_len, int32_t *match_end,
@@ -496,17 +528,21 @@ size_t rejection_accept_workspace_bytes(int32_t B, int32_t V);
  * (pad a vocabulary with zero-probability entries).  wg_units: vocabulary
  * units of 1024 per workgroup, 0 = automatic (launch tuning only).
  * workspace: device memory of at least rejection_accept_workspace_bytes(B, V),
- * 8-byte aligned, zero before the first call and left zero by every call;
- * calls that share a workspace must not overlap.  Returns LCD_EINVAL for a
- * bad size, alignment, pointer or too small a workspace, before launching.
- * One launch, no allocation.
+ * 8-byte aligned, zero before the first call and then kept valid by the calls
+ * (as lookup_propose's: arrival counts and gathered sums back at zero, a call
+ * epoch per request that tags the published sums); calls that share a
+ * workspace must not overlap.  merge_polls: diagnostics, as lcd_params'
+ * merge_polls for the lookup (0 = default 2^20 polls, -1 = none); a request
+ * whose gathering gave up reports accept = -1 and emits nothing.  wg_units is
+ * at most 256.  Returns LCD_EINVAL for a bad size, alignment, pointer or too
+ * small a workspace, before launching.  One launch, no allocation.
  */
 int rejection_accept(const int32_t *block, const int32_t *block_len, const uint32_t *model_mask,
                      const float *target_probs, const float *model_probs, int32_t V,
                      const double *u_accept, const uint64_t *u_sample, int32_t B,
-                     int32_t wg_units, void *workspace, size_t workspace_bytes,
-                     int32_t *accept, int32_t *emitted, int32_t *hist, const int64_t *row_off,
-                     int32_t *len, const int32_t *cap, void *stream);
+                     int32_t wg_units, int32_t merge_polls, void *workspace,
+                     size_t workspace_bytes, int32_t *accept, int32_t *emitted, int32_t *hist,
+                     const int64_t *row_off, int32_t *len, const int32_t *cap, void *stream);
 
 /*
  * rejection_accept_timed -- for profiling only: rejection_accept launched so
@@ -517,10 +553,10 @@ int rejection_accept_timed(const int32_t *block, const int32_t *block_len,
                            const uint32_t *model_mask, const float *target_probs,
                            const float *model_probs, int32_t V, const double *u_accept,
                            const uint64_t *u_sample, int32_t B, int32_t wg_units,
-                           void *workspace, size_t workspace_bytes, int32_t *accept,
-                           int32_t *emitted, int32_t *hist, const int64_t *row_off,
-                           int32_t *len, const int32_t *cap, void *stream, void *ev_start,
-                           void *ev_stop);
+                           int32_t merge_polls, void *workspace, size_t workspace_bytes,
+                           int32_t *accept, int32_t *emitted, int32_t *hist,
+                           const int64_t *row_off, int32_t *len, const int32_t *cap, void *stream,
+                           void *ev_start, void *ev_stop);
 
 #ifdef __cplusplus
 }

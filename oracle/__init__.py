@@ -16,6 +16,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lcd_oracle.c")
+_BENCH_SRC = os.path.join(_HERE, "lcd_oracle_bench.c")   # the CPU-baseline timing harness
 _LIB = os.path.join(_HERE, "liblcd_oracle.so")
 
 PAD = -1
@@ -42,8 +43,8 @@ def default_params(**kw) -> OracleParams:
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-           _SRC, "-o", _LIB + ".tmp"]
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
+           _SRC, _BENCH_SRC, "-o", _LIB + ".tmp"]
     subprocess.run(cmd, check=True, capture_output=not verbose)
     os.replace(_LIB + ".tmp", _LIB)
     return _LIB
@@ -68,10 +69,12 @@ def lib():
         L.oracle_telemetry_update.argtypes = [P, P, P, P, P, P, P, P, i32, pp]
         L.oracle_telemetry_reduce.argtypes = [P, P, i32, i32, P]
         L.oracle_rejection_accept.argtypes = [P, P, P, P, P, i32, P, P, i32, P, P, P, P, P, P]
+        L.oracle_bench_steps.argtypes = [P, P, P, i32, P, P, pp, i32, ctypes.c_double, i32, P, P,
+                                         P, P]
         for f in (L.oracle_lookup_propose, L.oracle_fuse_verify_block,
                   L.oracle_greedy_accept, L.oracle_lookup_schedule_step,
                   L.oracle_telemetry_update, L.oracle_telemetry_reduce,
-                  L.oracle_rejection_accept):
+                  L.oracle_rejection_accept, L.oracle_bench_steps):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -223,3 +226,28 @@ def rejection_accept(block, block_len, target_probs, u_accept, u_sample, model_m
                                       V, _ptr(ua), _ptr(us), B, _ptr(acc), _ptr(em), _ptr(hist),
                                       _ptr(row_off), _ptr(lens), _ptr(cap))
     return acc, em
+
+
+def bench_steps(hist, row_off, lens, q, target, params=None, nthreads=1, min_seconds=1.0,
+                max_steps=1 << 30):
+    """Times whole decode steps of the batch (lookup, fusion, greedy accept,
+    scheduler per request; no append) with the oracle's own functions on
+    `nthreads` native threads (lcd_oracle_bench.c).  Returns (steps, wall
+    seconds, process CPU seconds, checksum)."""
+    params = params or default_params()
+    hist = _c(hist, np.int32)
+    row_off = _c(row_off, np.int64)
+    lens = _c(lens, np.int32)
+    q = _c(q, np.int32)
+    target = _c(target, np.int32)
+    steps = ctypes.c_int64()
+    wall = ctypes.c_double()
+    cpu = ctypes.c_double()
+    chk = ctypes.c_int64()
+    rc = lib().oracle_bench_steps(_ptr(hist), _ptr(row_off), _ptr(lens), len(lens), _ptr(q),
+                                  _ptr(target), ctypes.byref(params), int(nthreads),
+                                  float(min_seconds), int(max_steps), ctypes.byref(steps),
+                                  ctypes.byref(wall), ctypes.byref(cpu), ctypes.byref(chk))
+    if rc != 0:
+        raise RuntimeError("oracle_bench_steps failed")
+    return steps.value, wall.value, cpu.value, chk.value

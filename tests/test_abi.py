@@ -34,7 +34,7 @@ def test_default_params_are_the_articles_values():
     assert (p.n_head, p.n_block) == (7, 15)
     assert (p.head_full, p.head_agree, p.agree_n, p.tail_min) == (8, 6, 2, 4)
     assert (p.entry_steps, p.sticky, p.near_full_slack, p.scan_wgs) == (2, 3, 1, 0)
-    assert p.scan_balance == 0
+    assert p.scan_balance == 0 and p.merge_polls == 0
     assert lcd.check_params(p)
 
 
@@ -43,7 +43,7 @@ def test_default_params_are_the_articles_values():
     dict(n_head=0), dict(n_head=8, n_block=15), dict(n_block=6), dict(n_block=16),
     dict(head_full=0), dict(head_agree=0), dict(agree_n=-1), dict(agree_n=8),
     dict(tail_min=0), dict(entry_steps=0), dict(sticky=-1), dict(near_full_slack=-1),
-    dict(scan_wgs=-1), dict(scan_balance=2), dict(scan_balance=-1),
+    dict(scan_wgs=-1), dict(scan_balance=2), dict(scan_balance=-1), dict(merge_polls=-2),
 ])
 def test_param_ranges_rejected(bad):
     assert not lcd.check_params(lcd.default_params(**bad))
@@ -102,7 +102,7 @@ def test_empty_batch_is_a_noop():
     pp = ctypes.byref(p)
     assert L.lookup_propose(None, None, None, 0, 0, pp, None, None, None, None, None) == lcd.LCD_OK
     assert L.fuse_verify_block(None, None, None, None, 0, pp, None, None, None, None) == lcd.LCD_OK
-    assert L.rejection_accept(None, None, None, None, None, 64, None, None, 0, 0, None, 0, None,
+    assert L.rejection_accept(None, None, None, None, None, 64, None, None, 0, 0, 0, None, 0, None,
                               None, None, None, None, None, None) == lcd.LCD_OK
     assert L.greedy_accept(None, None, None, 0, None, None, None, None, None, None) == lcd.LCD_OK
     assert L.lookup_schedule_step(None, None, None, None, 0, pp, None, None) == lcd.LCD_OK
@@ -132,20 +132,73 @@ def test_decode_step_rejects_misuse_without_launching():
     need = lcd.decode_step_workspace_bytes(8, 1000)
     assert need == 8 * 8208           # LCD_WORKSPACE_PER_REQUEST
 
-    def call(B=8, max_len=1000, cap=f, ws=f, ws_bytes=need, append=1, hist=f, prm=pp, ln=f):
+    lo = 0x20000
+
+    def call(B=8, max_len=1000, cap=f, ws=f, ws_bytes=need, append=1, hist=f, prm=pp, ln=f,
+             ln_out=lo):
         P = _P
-        return L.lookup_decode_step(P(hist), P(f), P(ln), P(cap), B, max_len, P(f), P(f), P(f), prm,
-                                    P(ws), ws_bytes, P(f), P(f), P(f), P(f), P(f), P(f), None,
-                                    None, append, None)
+        return L.lookup_decode_step(P(hist), P(f), P(ln), P(ln_out), P(cap), B, max_len, P(f),
+                                    P(f), P(f), prm, P(ws), ws_bytes, P(f), P(f), P(f), P(f), P(f),
+                                    P(f), None, None, append, None)
     assert call(B=0, hist=None, ln=None, cap=None, ws=None, ws_bytes=0) == lcd.LCD_OK
     assert call(B=-1) == lcd.LCD_EINVAL
     assert call(ws_bytes=need - 8) == lcd.LCD_EINVAL          # workspace too small
     assert call(cap=None) == lcd.LCD_EINVAL                   # append needs capacities
+    assert call(ln_out=None) == lcd.LCD_EINVAL                # ... and a second length array
+    assert call(ln_out=f) == lcd.LCD_EINVAL                   # that is not the one read
+    assert call(ln_out=f + 4 * 7) == lcd.LCD_EINVAL           # nor overlaps it
+    assert call(ln_out=f - 4 * 7) == lcd.LCD_EINVAL
     assert call(hist=f + 4) == lcd.LCD_EINVAL                 # misaligned history
     assert call(ws=None) == lcd.LCD_EINVAL
     assert call(max_len=-5) == lcd.LCD_EINVAL
     bad = lcd.default_params(k_max=16)
     assert call(prm=ctypes.byref(bad)) == lcd.LCD_EINVAL
+    bad = lcd.default_params(merge_polls=-2)
+    assert call(prm=ctypes.byref(bad)) == lcd.LCD_EINVAL
+
+
+def test_binding_needs_a_second_length_array_to_append():
+    import torch
+    x = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="lens_out"):
+        lcd.lookup_decode_step(x, x, x, x, 4, x, x, x, x, x, x, x, x, x, x, append=True)
+
+
+def test_same_launch_append_would_move_the_chunk_plan():
+    """Why the fused step reads its lengths from an array it never writes: the
+    launch derives every workgroup's (row, chunk) and whether it takes part
+    from the rows' lengths, so a workgroup that started after another had
+    appended a row's emitted tokens would work from another plan.  Shown with
+    the host-compiled launch rule over a 256-step decode of 256 rows of
+    1k-262k tokens (log-uniform), each step appending 1-16 tokens per row:
+    token-balanced chunks (3000 workgroups), where one row's append can change
+    the batch's chunk length or that row's chunk count (which moves every later
+    row's workgroups), and equal chunks (4096 workgroups), where it can make
+    one more chunk of the row take part (c * T < n - 1)."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    lens = np.floor(np.exp(rng.uniform(np.log(1024), np.log(262144), 256))).astype(np.int64)
+    B = len(lens)
+    bal = lcd.default_params(scan_balance=1, scan_wgs=3000)
+    eq = lcd.default_params(scan_wgs=4096)
+    chunks = lambda n, T: np.maximum((n - 1 + T - 1) // T, 1)
+    moved_bal = moved_eq = 0
+    for _ in range(256):
+        grow = rng.integers(1, 17, B)
+        _, T0 = lcd.launch_shape(B, int(lens.max()), bal, lens)
+        _, Te = lcd.launch_shape(B, int(lens.max()), eq, None)
+        step_bal = step_eq = False
+        for r in range(B):
+            grown = lens.copy()
+            grown[r] += grow[r]
+            _, T1 = lcd.launch_shape(B, int(grown.max()), bal, grown)
+            step_bal |= T1 != T0 or chunks(grown[r], T1) != chunks(lens[r], T0)
+            # equal chunks are sized from the launch's max_len, so only the
+            # participation test sees the append
+            step_eq |= chunks(grown[r], Te) != chunks(lens[r], Te)
+        moved_bal += step_bal
+        moved_eq += step_eq
+        lens += grow
+    assert moved_bal > 0 and moved_eq > 0
 
 
 def test_telemetry_entry_points_reject_misuse_without_launching():
@@ -176,10 +229,10 @@ def test_rejection_accept_rejects_misuse_without_launching():
     assert lcd.rejection_accept_workspace_bytes(0, 64) == 0
 
     def call(B=3, V=64, wg=0, ws_bytes=need, tp=fake, mp=None, ua=fake, hist=None, ro=None,
-             ln=None, cp=None, ws=fake, block=fake):
+             ln=None, cp=None, ws=fake, block=fake, polls=0):
         return L.rejection_accept(_P(block), _P(fake), None, _P(tp), _P(mp) if mp else None, V,
-                                  _P(ua), _P(fake), B, wg, _P(ws), ws_bytes, _P(fake), _P(fake),
-                                  _P(hist) if hist else None, _P(ro) if ro else None,
+                                  _P(ua), _P(fake), B, wg, polls, _P(ws), ws_bytes, _P(fake),
+                                  _P(fake), _P(hist) if hist else None, _P(ro) if ro else None,
                                   _P(ln) if ln else None, _P(cp) if cp else None, s)
 
     assert call(V=62) == lcd.LCD_EINVAL                    # not a multiple of 4
@@ -187,6 +240,8 @@ def test_rejection_accept_rejects_misuse_without_launching():
     assert call(V=lcd.SAMPLE_MAX_VOCAB + 4) == lcd.LCD_EINVAL
     assert call(B=-1) == lcd.LCD_EINVAL
     assert call(wg=-1) == lcd.LCD_EINVAL
+    assert call(wg=257) == lcd.LCD_EINVAL                   # at most 256 units per workgroup
+    assert call(polls=-2) == lcd.LCD_EINVAL
     assert call(ws_bytes=need - 8) == lcd.LCD_EINVAL        # workspace too small
     assert call(tp=fake + 4) == lcd.LCD_EINVAL              # target rows not 16-byte aligned
     assert call(mp=fake + 8) == lcd.LCD_EINVAL

@@ -26,6 +26,7 @@ def _fused_single_step(w_hists, q, tgt, long0, params=None, append=False, packed
     dev = torch.device("cuda:0")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     h_d, ro_d, ln_d, cap_d = t(flat), t(ro), t(ln.copy()), t(cap)
+    ln_out = torch.full((B,), -77, dtype=torch.int32, device=dev)
     ml = int(ln.max()) if max_len is None else max_len
     ws = lcd.alloc_decode_workspace(B, ml, dev, p)
     state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
@@ -34,11 +35,14 @@ def _fused_single_step(w_hists, q, tgt, long0, params=None, append=False, packed
     d = torch.full((B, 15), 77, dtype=torch.int32, device=dev)
     blk = torch.full((B, 15), 77, dtype=torch.int32, device=dev)
     lcd.lookup_decode_step(h_d, ro_d, ln_d, cap_d, ml, t(q), t(tgt), state, ws, outs[0], outs[1], d,
-                           blk, outs[2], outs[3], outs[4], append, p)
+                           blk, outs[2], outs[3], outs[4], append, p, lens_out=ln_out)
     torch.cuda.synchronize()
     got = dict(m=outs[0], e=outs[1], d=d, block=blk, blk=outs[2], acc=outs[3], ln=outs[4],
-               state=state, lens=ln_d, flat=h_d)
+               state=state, lens=ln_out if append else ln_d, flat=h_d)
     got = {k: v.cpu().numpy() for k, v in got.items()}
+    np.testing.assert_array_equal(ln_d.cpu().numpy(), ln)             # the lengths read stay
+    if not append:
+        assert (ln_out.cpu().numpy() == -77).all()                      # not touched
 
     op = _oparams(p)
     om, oe, od = oracle.lookup_propose(flat, ro, ln, op)
