@@ -1,0 +1,32 @@
+"""The CPU-baseline harness (oracle/lcd_oracle_bench.c) runs the oracle's own
+functions unchanged: its checksum over one step equals the same step computed
+through the oracle's batch calls, for any thread count."""
+
+import numpy as np
+
+import oracle
+from context_lookup_drafting_amd import workloads as wl
+
+
+def test_harness_runs_the_oracle_step_unchanged():
+    rng = np.random.Generator(np.random.PCG64(41))
+    hs = [rng.integers(0, 6, int(n)).astype(np.int32) for n in rng.integers(0, 3000, 37)]
+    flat, ro, ln = wl.pack_csr(hs)
+    B = len(hs)
+    q = rng.integers(0, 6, (B, 7)).astype(np.int32)
+    tgt = rng.integers(0, 6, (B, 16)).astype(np.int32)
+    m, e, d = oracle.lookup_propose(flat, ro, ln)
+    blk, bl = oracle.fuse_verify_block(d, m, q, np.zeros(B, np.int32))
+    acc = oracle.greedy_accept(blk, bl, tgt)
+    ln_next = np.array([oracle.lookup_schedule_step(np.zeros((1, 3), np.int32), m[r:r + 1],
+                                                    acc[r:r + 1], bl[r:r + 1])[0]
+                        for r in range(B)])
+    want = int(m.sum() + acc.sum() + ln_next.sum())
+    for nt in (1, 3, 8):
+        steps, wall, cpu, chk = oracle.bench_steps(flat, ro, ln, q, tgt, nthreads=nt,
+                                                   min_seconds=0.0, max_steps=1)
+        assert steps == 1 and wall >= 0 and cpu >= 0
+        assert chk == want
+    steps, _, _, chk = oracle.bench_steps(flat, ro, ln, q, tgt, nthreads=4, min_seconds=60.0,
+                                          max_steps=5)
+    assert steps == 5 and chk == 5 * want
