@@ -90,6 +90,7 @@ def load():
                P]
         L.lookup_decode_step.argtypes = dec
         L.lookup_decode_step_timed.argtypes = dec + [P, P]
+        L.lookup_decode_step_noalloc.argtypes = dec[:11] + dec[13:]
         L.greedy_accept.argtypes = [P, P, P, i32, P, P, P, P, P, P]
         L.lookup_schedule_step.argtypes = [P, P, P, P, i32, pp, P, P]
         L.lookup_telemetry_update.argtypes = [P, P, P, P, P, P, P, P, i32, pp, P]
@@ -114,7 +115,8 @@ def load():
         L.rejection_accept_timed.argtypes = rej + [P, P]
         for f in (L.lookup_propose, L.lookup_propose_timed, L.fuse_verify_block,
                   L.greedy_accept, L.lookup_schedule_step, L.lookup_decode_step,
-                  L.lookup_decode_step_timed, L.lookup_telemetry_update,
+                  L.lookup_decode_step_timed, L.lookup_decode_step_noalloc,
+                  L.lookup_telemetry_update,
                   L.lookup_telemetry_reduce, L.rejection_accept, L.rejection_accept_timed,
                   L.lookup_index_build, L.lookup_index_propose, L.lookup_index_propose_timed,
                   L.lookup_index_decode_step, L.lookup_index_decode_step_timed):
@@ -351,6 +353,25 @@ def lookup_decode_step_timed(hist, row_off, lens, cap, max_len, model_draft, tar
         hist, row_off, lens, cap, max_len, model_draft, target, state, workspace, match_len,
         match_end, draft, block, block_len, accept, long_next, append, p, telemetry, lens_out),
         ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
+
+
+NOALLOC_MAX_B = 1024
+
+
+def lookup_decode_step_noalloc(hist, row_off, lens, cap, max_len, model_draft, target, state,
+                               match_len, match_end, draft, block, block_len, accept,
+                               long_next=None, append=True, params: Params | None = None,
+                               telemetry=None, lens_out=None):
+    """lookup_decode_step without a workspace argument: the library's static
+    per-GPU array serves as the workspace (at most NOALLOC_MAX_B requests;
+    calls that overlap on one GPU race)."""
+    import torch
+    p = params or default_params()
+    dummy = torch.empty(0, dtype=torch.int64, device=lens.device)
+    a = _decode_args(hist, row_off, lens, cap, max_len, model_draft, target, state, dummy,
+                     match_len, match_end, draft, block, block_len, accept, long_next, append, p,
+                     telemetry, lens_out)
+    _check("lookup_decode_step_noalloc", load().lookup_decode_step_noalloc(*(a[:11] + a[13:])))
 
 
 TELE_WORDS = 32

@@ -62,6 +62,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "lcd.h"
 #include "lcd_finish.h"
 #include "lcd_rules.h"
@@ -1032,4 +1034,79 @@ extern "C" int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, c
                             block_len, accept, long_next, telemetry, append, stream,
                             reinterpret_cast<hipEvent_t>(ev_start),
                             reinterpret_cast<hipEvent_t>(ev_stop));
+}
+
+// ---------------------------------------------------------------------------
+// lookup_decode_step_noalloc: the decode step with its workspace in a static
+// device array, for callers that cannot allocate.  Each GPU the library runs
+// on holds its own copy of `scratch` (LCD_NOALLOC_MAX_B requests' workspace,
+// 8.0 MiB) until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is taken once per
+// device with hipGetSymbolAddress and only that address is passed on.
+// ---------------------------------------------------------------------------
+namespace lcd {
+namespace {
+
+constexpr int64_t kNoallocWords = (int64_t)LCD_NOALLOC_MAX_B * kReqWords;
+static __device__ __align__(256) u64 scratch[kNoallocWords];
+
+constexpr int kMaxDevices = 64;
+
+__global__ void __launch_bounds__(256) zero_words_kernel(u64 *__restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0;
+}
+
+struct ScratchTable {
+    std::once_flag once[kMaxDevices];
+    void *ptr[kMaxDevices] = {};
+    hipError_t err[kMaxDevices] = {};
+};
+
+ScratchTable &scratch_table() {
+    static ScratchTable t;
+    return t;
+}
+
+// The current device's copy of `scratch`, set up on the first call on that
+// device: its address, then one zero fill on the caller's stream (ordered
+// before this call's kernel; the array is left valid by every call after).
+void *device_scratch(hipStream_t st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    ScratchTable &t = scratch_table();
+    std::call_once(t.once[dev], [&] {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(zero_words_kernel, dim3(1024), dim3(256), 0, st,
+                               static_cast<u64 *>(ptr), kNoallocWords);
+            e = hipGetLastError();
+        }
+        t.err[dev] = e;
+        t.ptr[dev] = e == hipSuccess ? ptr : nullptr;
+    });
+    return t.ptr[dev];
+}
+
+}  // namespace
+}  // namespace lcd
+
+extern "C" int lookup_decode_step_noalloc(int32_t *hist, const int64_t *row_off, const int32_t *len,
+                                          int32_t *len_out, const int32_t *cap, int32_t B,
+                                          int32_t max_len, const int32_t *model_draft,
+                                          const int32_t *target, lcd_sched_state *state,
+                                          const lcd_params *p, int32_t *match_len,
+                                          int32_t *match_end, int32_t *draft, int32_t *block,
+                                          int32_t *block_len, int32_t *accept, int32_t *long_next,
+                                          uint32_t *telemetry, int32_t append, void *stream) {
+    if (B < 0 || B > LCD_NOALLOC_MAX_B) return LCD_EINVAL;
+    if (B == 0) return lcd_check_params(p) == LCD_OK ? LCD_OK : LCD_EINVAL;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    void *ws = lcd::device_scratch(st);
+    if (ws == nullptr) return LCD_EHIP;
+    return lcd::decode_step(hist, row_off, len, len_out, cap, B, max_len, model_draft, target, state,
+                            p, ws, (size_t)lcd::kNoallocWords * sizeof(lcd::u64), match_len,
+                            match_end, draft, block, block_len, accept, long_next, telemetry,
+                            append, stream, nullptr, nullptr);
 }

@@ -285,6 +285,29 @@ int lookup_decode_step_timed(int32_t *hist, const int64_t *row_off, const int32_
                              int32_t append, void *stream, void *ev_start, void *ev_stop);
 
 /*
+ * lookup_decode_step_noalloc -- lookup_decode_step for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, results and errors,
+ * without the workspace.  The workspace is a static device array inside the
+ * library, one per GPU (LCD_NOALLOC_MAX_B requests, 8.0 MiB, held until the
+ * process ends), zero-filled by a kernel on `stream` at the first call on a
+ * device and left valid by every call.  All calls on one GPU share it: calls
+ * that overlap on one GPU (other streams, other threads) race, so a caller
+ * orders them.  B > LCD_NOALLOC_MAX_B returns LCD_EINVAL before launching;
+ * LCD_EHIP when the array's device address cannot be taken.  Calls no
+ * allocating routine.
+ */
+#define LCD_NOALLOC_MAX_B 1024
+
+int lookup_decode_step_noalloc(int32_t *hist, const int64_t *row_off, const int32_t *len,
+                               int32_t *len_out, const int32_t *cap, int32_t B, int32_t max_len,
+                               const int32_t *model_draft, const int32_t *target,
+                               lcd_sched_state *state, const lcd_params *p, int32_t *match_len,
+                               int32_t *match_end, int32_t *draft, int32_t *block,
+                               int32_t *block_len, int32_t *accept, int32_t *long_next,
+                               uint32_t *telemetry, int32_t append, void *stream);
+
+/*
  * Acceptance telemetry -- the diagnostics the article's forum thread asks to
  * wire up first (hit rate and mean accepted length, with the distribution of
  * accepted lengths), per task class as in the Polish post's test procedure

@@ -157,6 +157,20 @@ def test_decode_step_rejects_misuse_without_launching():
     assert call(prm=ctypes.byref(bad)) == lcd.LCD_EINVAL
 
 
+def test_noalloc_step_rejects_misuse_without_launching():
+    L = lcd.load()
+    p = lcd.default_params()
+    f = ctypes.c_void_p(0x10000)
+
+    def call(B, prm=p):
+        return L.lookup_decode_step_noalloc(f, f, f, f, f, B, 100, f, f, f, ctypes.byref(prm), f, f,
+                                            f, f, f, f, f, None, 1, None)
+    assert call(lcd.NOALLOC_MAX_B + 1) == lcd.LCD_EINVAL       # more than the static array holds
+    assert call(-1) == lcd.LCD_EINVAL
+    assert call(0) == lcd.LCD_OK
+    assert call(0, lcd.default_params(k_max=16)) == lcd.LCD_EINVAL
+
+
 def test_binding_needs_a_second_length_array_to_append():
     import torch
     x = torch.zeros(4, dtype=torch.int32)
