@@ -1,22 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the context-lookup drafting hot path on one MI355X.
 
-One step = lookup + fusion + greedy acceptance + scheduler update over a whole
-batch (default: 64 requests of 25,000 tokens, 32 verbatim-restatement and 32
-ordinary Zipf texts, vocabulary 40,960), through the fused lookup_decode_step
+One step = lookup + fusion + greedy acceptance (appending the emitted tokens)
++ scheduler update over a whole batch, through the fused lookup_decode_step
 entry point (one kernel), or with --separate through the four entry points
-lookup_propose, fuse_verify_block, greedy_accept, lookup_schedule_step.
-Inputs are resident in HBM before timing.  The batch is copied into enough
-distinct buffers (>= 320 MB) that consecutive steps never hit the 256 MB
-Infinity Cache, and the steps are replayed from a HIP graph so the host does
-not throttle the launches.
+lookup_propose, fuse_verify_block, greedy_accept, lookup_schedule_step.  The
+headline batch is 64 requests of 25,000 tokens, 32 verbatim-restatement and 32
+ordinary Zipf texts, vocabulary 40,960 (--workload c3, the default); the same
+run also measures 64 x 150,000 tokens (c4) and 256 ragged rows of 1k-262k
+tokens (c5) and reports them under "more_configs".  Inputs are resident in HBM
+before timing.  Each batch is copied into enough distinct buffers (>= 320 MB)
+that consecutive steps never hit the 256 MB Infinity Cache, and the steps are
+replayed from a HIP graph so the host does not throttle the launches.  The
+fused step reads the rows' lengths from an array it never writes (the new
+lengths go to a second one), so every step scans the same history bytes and
+appends past them.
 
 Printed: one JSON line with the throughput (history tokens scanned per second),
 the roofline of the dominant kernel (the scan kernel that runs the whole step;
 its duration is stamped by the GPU on each dispatch through the *_timed entry
-point) and the CPU oracle timed on the host's cores as a baseline.
+point), the practical read ceiling and launch floor measured live, and the CPU
+oracle timed on the host's cores as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c4|c5]
+    python bench.py --floors        # read ceiling sweep and launch floor only
 """
 
 from __future__ import annotations
@@ -60,7 +67,18 @@ def parse():
                     help="profiling aid: only N eager lookup launches over the rotating sets")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="profiling aid: 5 plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--no-append", action="store_true",
+                    help="fused step without the append (the lookup outputs only feed fusion)")
+    ap.add_argument("--only", action="store_true",
+                    help="measure only --workload (no more_configs lines)")
+    ap.add_argument("--floors", action="store_true",
+                    help="only the launch floor and the read ceiling sweep at c3, c4, c5 sizes")
     return ap.parse_args()
+
+
+def log(msg):
+    """Progress of a run, on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
 
 def calibrate_copy(mib):
@@ -75,16 +93,17 @@ def calibrate_copy(mib):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 5}), flush=True)
 
 
-def per_request_bytes(separate, telemetry=False):
+def per_request_bytes(separate, telemetry=False, append=False):
     """Algorithmic bytes per request besides the history, for the timed kernel:
     the lookup alone reads row_off and len (12) and writes match_len, match_end
     and the draft (68); the whole step also reads the proposal, target tokens
     and scheduler state (104) and writes the block, block_len, accept, state
-    and long_next (84); telemetry reads the request's 32-word row (128) and
-    writes its 25 counters back (100)."""
+    and long_next (84); the append reads the capacity and writes the new length
+    (8, plus 4 per emitted token, counted apart); telemetry reads the request's
+    32-word row (128) and writes its 25 counters back (100)."""
     if separate:
         return 80
-    return 80 + 104 + 84 + (228 if telemetry else 0)
+    return 80 + 104 + 84 + (8 if append else 0) + (228 if telemetry else 0)
 
 
 KERNEL_SOURCES = ("context_lookup_drafting_amd/csrc/lcd_lookup.hip",
@@ -155,28 +174,46 @@ def cpu_model():
     return "unknown"
 
 
-def read_ceiling(lcd, sets, nbytes, n=200, blocks=(1024, 2048, 4096)):
-    """Practical HBM read ceiling at nbytes: lcd_read_probe over the rotating
-    buffers, GPU-stamped; the best mean over a few grid sizes."""
+def _event_mean_us(hev, launch, n, warm=10):
+    """Mean GPU-stamped duration (us) of n launches of launch(i, ev0, ev1),
+    the first `warm` left out."""
     import numpy as np
+    import torch
+    evs = [(hev.create(), hev.create()) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        launch(i, a, b)
+    torch.cuda.synchronize()
+    us = np.array([hev.elapsed_ms(a, b) for a, b in evs[warm:]]) * 1e3
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    return float(us.mean())
+
+
+def read_ceiling(lcd, sets, nbytes, n=200, blocks=(1024, 2048, 4096, 8192),
+                 variants=("contig4", "contig8", "interleave4", "interleave8", "interleave16")):
+    """Practical HBM read ceiling at nbytes: lcd_read_probe over the rotating
+    buffers, GPU-stamped, in every variant and grid; the best mean."""
     import torch
     nbytes = nbytes // 16 * 16
     hev = HipEvents(lcd.load())
+    out = torch.empty(max(blocks), dtype=torch.int32, device=sets[0].device)
     best = None
-    for nb in blocks:
-        out = torch.empty(nb, dtype=torch.float32, device=sets[0].device)
-        evs = [(hev.create(), hev.create()) for _ in range(n)]
-        for i, (a, b) in enumerate(evs):
-            lcd.read_probe(sets[i % len(sets)], nbytes, nb, out, a, b)
-        torch.cuda.synchronize()
-        us = float(np.mean([hev.elapsed_ms(a, b) for a, b in evs[10:]])) * 1e3
-        for a, b in evs:
-            hev.destroy(a)
-            hev.destroy(b)
-        if best is None or us < best[1]:
-            best = (nb, us)
-    return {"kernel": "lcd_read_probe", "bytes": nbytes, "blocks": best[0],
-            "us": round(best[1], 3), "gbps": round(nbytes / best[1] / 1e3, 1)}
+    for var in variants:
+        for nb in blocks:
+            us = _event_mean_us(hev, lambda i, a, b: lcd.read_probe(
+                sets[i % len(sets)], nbytes, nb, out, a, b, variant=var), n)
+            if best is None or us < best[2]:
+                best = (var, nb, us)
+    return {"kernel": "lcd_read_probe", "bytes": nbytes, "variant": best[0], "blocks": best[1],
+            "us": round(best[2], 3), "gbps": round(nbytes / best[2] / 1e3, 1)}
+
+
+def launch_floor(lcd, device, n=200):
+    """GPU-stamped duration of an empty kernel of 256 and of 2048 workgroups."""
+    hev = HipEvents(lcd.load())
+    return {f"empty_kernel_{nb}wg_us": round(_event_mean_us(
+        hev, lambda i, a, b: lcd.empty_probe(nb, device, a, b), n), 3) for nb in (256, 2048)}
 
 
 def prefilter_survival(w):
@@ -213,64 +250,249 @@ def work_spread(lcd, w, max_len, p):
             "max_over_mean": round(max(per) / mean, 3) if mean else None}
 
 
+def host_threads():
+    """(threads for the CPU baseline, CPUs this process may run on): the
+    affinity set, at most 16 -- a GPU machine's CPU share per GPU."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return max(1, min(aff, 16)), aff
+
+
 def cpu_baseline(w, work_seconds):
-    """The CPU oracle (as it is) over full steps of the same batch, threads over
-    requests; bounded to about `work_seconds` of CPU time summed over threads."""
+    """The CPU oracle (as it is) over whole steps of the same batch (lookup,
+    fusion, greedy accept, scheduler per request; no append), on native
+    threads over requests (oracle/lcd_oracle_bench.c) and on one thread;
+    bounded to about `work_seconds` of CPU time in all."""
     import numpy as np
-    from concurrent.futures import ThreadPoolExecutor
     import oracle
     if not os.path.exists(os.path.join(ROOT, "oracle", "liblcd_oracle.so")):
         oracle.build()
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
-    op = oracle.default_params()
+    from context_lookup_drafting_amd import workloads as wl
+    threads, aff = host_threads()
+    flat, ro, ln, _ = wl.pack_rows(w.hists)
     q, tgt = w.step_inputs(np.zeros(w.B, np.int64), 0)
-    hs = w.hists
-    chunks = [list(range(i, w.B, cores)) for i in range(cores)]
-
-    def run_chunk(idx):
-        for r in idx:
-            h = hs[r]
-            m, e, d = oracle.lookup_propose(h, np.zeros(1, np.int64), np.array([len(h)], np.int32), op)
-            blk, bl = oracle.fuse_verify_block(d, m, q[r:r + 1], np.zeros(1, np.int32), op)
-            acc = oracle.greedy_accept(blk, bl, tgt[r:r + 1])
-            st = np.zeros((1, 3), np.int32)
-            oracle.lookup_schedule_step(st, m, acc, bl, op)
-        return len(idx)
-
-    tokens = int(sum(len(h) for h in hs))
-    batches = 0
-    cpu0 = time.process_time()
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=cores) as pool:
-        while True:
-            list(pool.map(run_chunk, chunks))
-            batches += 1
-            if time.process_time() - cpu0 >= work_seconds or time.perf_counter() - t0 > 120:
-                break
-    wall = time.perf_counter() - t0
-    # the same oracle on one thread, over one request after another
-    t1 = time.perf_counter()
-    done = 0
-    while done < w.B and time.perf_counter() - t1 < max(2.0, work_seconds / 4):
-        run_chunk([done])
-        done += 1
-    one = sum(len(hs[r]) for r in range(done)) / (time.perf_counter() - t1)
+    tokens = int(ln.astype(np.int64).sum())
+    budget = max(1.0, 0.75 * work_seconds / threads)
+    steps, wall, cpu, _ = oracle.bench_steps(flat, ro, ln, q, tgt, nthreads=threads,
+                                             min_seconds=budget)
+    steps1, wall1, cpu1, _ = oracle.bench_steps(flat, ro, ln, q, tgt, nthreads=1,
+                                                min_seconds=max(1.0, 0.25 * work_seconds))
+    rate, rate1 = steps * tokens / wall, steps1 * tokens / wall1
     return {
-        "value": round(batches * tokens / wall, 1),
+        "value": round(rate, 1),
         "unit": "history tokens/s",
-        "cores": cores,
+        "cores": threads,
         "kind": "oracle",
-        "value_1thread": round(one, 1),
+        "affinity_cpus": aff,
+        "os_cpu_count": os.cpu_count(),
         "cpu_model": cpu_model(),
-        "sample": (f"{batches} full steps (lookup+fuse+accept+schedule) of the {w.B}-request "
-                   f"batch, {tokens} history tokens each, threads over requests, "
-                   f"{wall:.2f} s wall / {time.process_time() - cpu0:.1f} s CPU"),
-        "lookups_per_s": round(batches * w.B / wall, 1),
+        "value_1thread": round(rate1, 1),
+        "thread_scaling": round(rate / rate1, 2),
+        "sample": (f"{steps} whole steps (lookup+fuse+accept+schedule per request, no append) of "
+                   f"the {w.B}-request batch, {tokens} history tokens each, on {threads} native "
+                   f"threads over requests ({wall:.2f} s wall, {cpu:.1f} s CPU); {steps1} steps on "
+                   f"one thread ({wall1:.2f} s)"),
+        "lookups_per_s": round(steps * w.B / wall, 1),
     }
+
+
+def load_workload(name):
+    from context_lookup_drafting_amd import workloads as wl
+    return {"c2": wl.config2, "c3": wl.config3, "c4": wl.config4, "c5": wl.config5}[name]()
+
+
+def run_scan(args, name, K, W, cpu_seconds, extra=False):
+    """Graph-timed steps, GPU-stamped kernel durations, roofline, read ceiling
+    and launch floor of the scan step on workload `name`; returns a dict."""
+    import numpy as np
+    import torch
+
+    import context_lookup_drafting_amd as lcd
+    from context_lookup_drafting_amd import workloads as wl
+
+    lib = lcd.load()
+    dev = torch.device("cuda:0")
+    w = load_workload(name)
+    append = not (args.separate or args.no_append)
+    flat, ro, ln, cap = wl.pack_rows(w.hists, extra=16)
+    B = w.B
+    tokens = int(ln.astype(np.int64).sum())
+    max_len = int(ln.max())
+    set_bytes = flat.nbytes
+    R = max(2, -(-ROTATE_BYTES // set_bytes))
+    R += R % 2
+    p = lcd.default_params(scan_wgs=args.scan_wgs, scan_balance=int(args.balance))
+
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    hist_sets = [t(flat) for _ in range(R)]
+    ro_d, ln_d, cap_d = t(ro), t(ln), t(cap)
+    lens_out = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    q, tgt = w.step_inputs(np.zeros(B, np.int64), 0)
+    q_d, tgt_d = t(q), t(tgt)
+    ws = lcd.alloc_workspace(B, dev)
+    dws = lcd.alloc_decode_workspace(B, max_len, dev, p)
+    mk = lambda *sh: torch.empty(sh, dtype=torch.int32, device=dev)
+    m, e, d, blk, bl, acc, ln_next = mk(B), mk(B), mk(B, 15), mk(B, 15), mk(B), mk(B), mk(B)
+    state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
+    longs = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
+    tele = lcd.alloc_telemetry(B, dev) if args.telemetry else None
+
+    def step(i, ev=None):
+        if args.separate:
+            lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
+            lcd.fuse_verify_block(d, m, q_d, longs[i % 2], blk, bl, p)
+            lcd.greedy_accept(blk, bl, tgt_d, acc)
+            lcd.lookup_schedule_step(state, m, acc, bl, longs[(i + 1) % 2], p)
+            return
+        fn = lcd.lookup_decode_step if ev is None else lcd.lookup_decode_step_timed
+        evargs = () if ev is None else ev
+        fn(hist_sets[i % R], ro_d, ln_d, cap_d if append else None, max_len, q_d, tgt_d, state,
+           dws, m, e, d, blk, bl, acc, *evargs, long_next=ln_next, append=append, params=p,
+           telemetry=tele, lens_out=lens_out[i % 2] if append else None)
+
+    if args.kernel_only:
+        for i in range(args.kernel_only):
+            step(i)
+        torch.cuda.synchronize()
+        return {"kernel_only_launches": args.kernel_only, "workload": w.name,
+                "tokens_per_launch": tokens, "rotating_sets": R, "separate": args.separate}
+
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (m, e, d)]
+
+    def capture(nsteps):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(nsteps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        return g
+
+    g_full = capture(R)
+    g_tail = capture(K % R) if K % R else None
+    for _ in range(max(1, -(-W // R))):
+        g_full.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ------------------------------------
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K // R):
+        g_full.replay()
+    if g_tail is not None:
+        g_tail.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"{w.name}: {K} graph-timed steps, {elapsed / K * 1e6:.2f} us per step")
+
+    # every replay must reproduce the eager lookup (identical histories)
+    for x, y in zip((m, e, d), ref):
+        if not torch.equal(x, y):
+            print("bench.py: graph replay disagrees with the eager step", file=sys.stderr)
+            sys.exit(3)
+    acc_h = acc.cpu().numpy()
+    if append and (acc_h < 0).any():
+        print("bench.py: an append ran out of capacity", file=sys.stderr)
+        sys.exit(3)
+    emitted = float(np.maximum(acc_h, 0).mean() + 1) if append else 0.0
+
+    # ---- kernel duration of the scan, stamped by the GPU -------------------
+    hev = HipEvents(lib)
+    n_k = min(K, 400)
+    evs = [(hev.create(), hev.create()) for _ in range(n_k)]
+    for i in range(n_k):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    durs = np.array([hev.elapsed_ms(a, b) for a, b in evs]) * 1e-3
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    k_avg = float(durs.mean())
+    log(f"{w.name}: {n_k} GPU-stamped launches, kernel mean {k_avg * 1e6:.3f} us")
+
+    alg_bytes = int(4 * tokens + B * (per_request_bytes(args.separate, args.telemetry, append)
+                                      + 4 * emitted))
+    achieved = alg_bytes / k_avg / 1e9
+    ceiling = read_ceiling(lcd, hist_sets, 4 * tokens)
+    ceiling["frac_of_ceiling"] = round(achieved / ceiling["gbps"], 4)
+    log(f"{w.name}: read ceiling {ceiling['us']} us ({ceiling['variant']}, {ceiling['blocks']} wg)")
+    traffic = None if (args.separate or args.telemetry) else load_traffic(w.name)
+    value = K * tokens / elapsed
+    kernel = ("lookup_scan_kernel<4,kPropose>" if args.separate
+              else "lookup_scan_kernel<4,kStep>")
+    res = {
+        "value": round(value, 1),
+        "ms_per_step": round(elapsed / K * 1e3, 6),
+        "config": {
+            "workload": w.name,
+            "batch": B,
+            "tokens_per_step": tokens,
+            "max_len": max_len,
+            "vocab": w.vocab,
+            "rotating_sets": R,
+            "rotating_bytes": R * set_bytes,
+            "launch": (f"HIP graph of {R} steps, "
+                       + ("4 entry points (4 kernels) per step" if args.separate
+                          else "lookup_decode_step (1 kernel) per step"
+                          + (", appending" if append else ""))),
+            "telemetry": args.telemetry,
+            "scan_balance": int(args.balance),
+        },
+        "lookups_per_s": round(K * B / elapsed, 1),
+        "step_hbm_gbps": round(value * 4 / 1e9, 2),
+        "step_pct_peak": round(value * 4 / 1e9 / HBM_PEAK_GBPS * 100, 2),
+        "read_ceiling": ceiling,
+        "launch_floor": launch_floor(lcd, dev),
+        "prefilter_survival": round(prefilter_survival(w), 6),
+        "work_spread": work_spread(lcd, w, max_len, p),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": kernel,
+            "kernel_us_mean": round(k_avg * 1e6, 3),
+            "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, x)) * 1e6, 3)
+                                      for x in (10, 50, 90)],
+            "alg_bytes_per_launch": alg_bytes,
+            "emitted_per_request": round(emitted, 3),
+            "launches_timed": n_k,
+        },
+    }
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+        log(f"{w.name}: CPU oracle baseline done")
+    elif not extra:
+        res["cpu_baseline"] = None
+    del hist_sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_floors():
+    """Launch floor and read-ceiling sweep at the c3, c4 and c5 history sizes."""
+    import numpy as np
+    import torch
+    import context_lookup_drafting_amd as lcd
+    dev = torch.device("cuda:0")
+    out = {"launch_floor": launch_floor(lcd, dev)}
+    for name, nbytes in (("c3", 6_400_000), ("c4", 38_400_000), ("c5", 48_200_000)):
+        R = max(2, -(-ROTATE_BYTES // nbytes))
+        sets = [torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device=dev) for _ in range(R)]
+        out[name] = read_ceiling(lcd, sets, nbytes)
+        log(f"floors: {name} read ceiling {out[name]['us']} us")
+        del sets
+    torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -290,201 +512,48 @@ def main():
     if args.lookup == "index":
         bench_index(args)
         return
-
-    import numpy as np
-    import torch
-
-    import context_lookup_drafting_amd as lcd
-    from context_lookup_drafting_amd import workloads as wl
-
-    lib = lcd.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.workload == "c2":
-        w = wl.config2()
-    elif args.workload == "c3":
-        w = wl.config3()
-    elif args.workload == "c4":
-        w = wl.config4()
-    else:
-        w = wl.config5()
-    flat, ro, ln, cap = wl.pack_rows(w.hists)
-    B = w.B
-    tokens = int(ln.astype(np.int64).sum())
-    max_len = int(ln.max())
-    set_bytes = flat.nbytes
-    R = max(2, -(-ROTATE_BYTES // set_bytes))
-    R += R % 2                       # even, so the two long-mode buffers alternate cleanly
-    p = lcd.default_params(scan_wgs=args.scan_wgs, scan_balance=int(args.balance))
-
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    hist_sets = [t(flat) for _ in range(R)]
-    ro_d, ln_d = t(ro), t(ln)
-    q, tgt = w.step_inputs(np.zeros(B, np.int64), 0)
-    q_d, tgt_d = t(q), t(tgt)
-    ws = lcd.alloc_workspace(B, dev)
-    dws = lcd.alloc_decode_workspace(B, max_len, dev, p)
-    m = torch.empty(B, dtype=torch.int32, device=dev)
-    e = torch.empty_like(m)
-    d = torch.empty((B, 15), dtype=torch.int32, device=dev)
-    blk = torch.empty((B, 15), dtype=torch.int32, device=dev)
-    bl = torch.empty(B, dtype=torch.int32, device=dev)
-    acc = torch.empty(B, dtype=torch.int32, device=dev)
-    ln_next = torch.empty(B, dtype=torch.int32, device=dev)
-    state = torch.zeros((B, 3), dtype=torch.int32, device=dev)
-    longs = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(2)]
-    tele = lcd.alloc_telemetry(B, dev) if args.telemetry else None
     if args.telemetry and args.separate:
         print("bench.py: --telemetry applies to the fused step only", file=sys.stderr)
         sys.exit(2)
 
-    if args.kernel_only:
-        for i in range(args.kernel_only):
-            if args.separate:
-                lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
-            else:
-                lcd.lookup_decode_step(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d,
-                                       state, dws, m, e, d, blk, bl, acc, ln_next, False, p,
-                                       telemetry=tele)
-        torch.cuda.synchronize()
-        print(json.dumps({"kernel_only_launches": args.kernel_only, "workload": w.name,
-                          "tokens_per_launch": tokens,
-                          "alg_bytes_per_launch": (4 * tokens
-                                                   + per_request_bytes(args.separate, args.telemetry) * B),
-                          "rotating_sets": R, "separate": args.separate}), flush=True)
+    import torch
+    torch.cuda.set_device(torch.device("cuda:0"))
+    if args.floors:
+        run_floors()
         return
 
-    def step(i):
-        if args.separate:
-            lcd.lookup_propose(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d, p)
-            lcd.fuse_verify_block(d, m, q_d, longs[i % 2], blk, bl, p)
-            lcd.greedy_accept(blk, bl, tgt_d, acc)
-            lcd.lookup_schedule_step(state, m, acc, bl, longs[(i + 1) % 2], p)
-        else:
-            lcd.lookup_decode_step(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d, state,
-                                   dws, m, e, d, blk, bl, acc, ln_next, False, p, telemetry=tele)
-
-    # eager reference of one step, then the graphs
-    for i in range(2):
-        step(i)
-    torch.cuda.synchronize()
-    ref = [x.clone() for x in (m, e, d)]
-
-    def capture(nsteps):
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(nsteps):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(s)
-        return g
-
     K, W = args.steps, args.warmup
-    g_full = capture(R)
-    g_tail = capture(K % R) if K % R else None
-
-    # warmup
-    for _ in range(max(1, -(-W // R))):
-        g_full.replay()
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps ------------------------------------
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K // R):
-        g_full.replay()
-    if g_tail is not None:
-        g_tail.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-
-    # every replay must reproduce the eager lookup (identical sets)
-    for x, y in zip((m, e, d), ref):
-        if not torch.equal(x, y):
-            print("bench.py: graph replay disagrees with the eager step", file=sys.stderr)
-            sys.exit(3)
-
-    # ---- kernel duration of the lookup scan, stamped by the GPU -----------
-    hev = HipEvents(lib)
-    n_k = min(K, 400)
-    evs = [(hev.create(), hev.create()) for _ in range(n_k)]
-    for i in range(n_k):
-        if args.separate:
-            lcd.lookup_propose_timed(hist_sets[i % R], ro_d, ln_d, max_len, ws, m, e, d,
-                                     evs[i][0], evs[i][1], p)
-        else:
-            lcd.lookup_decode_step_timed(hist_sets[i % R], ro_d, ln_d, None, max_len, q_d, tgt_d,
-                                         state, dws, m, e, d, blk, bl, acc, evs[i][0], evs[i][1],
-                                         ln_next, False, p, telemetry=tele)
-    torch.cuda.synchronize()
-    durs = np.array([hev.elapsed_ms(a, b) for a, b in evs]) * 1e-3
-    for a, b in evs:
-        hev.destroy(a)
-        hev.destroy(b)
-    k_avg = float(durs.mean())
-
-    alg_bytes = 4 * tokens + per_request_bytes(args.separate, args.telemetry) * B
-    achieved = alg_bytes / k_avg / 1e9
-    ceiling = read_ceiling(lcd, hist_sets, set_bytes)
-    ceiling["frac_of_ceiling"] = round(achieved / ceiling["gbps"], 4)
-    traffic = None if (args.separate or args.telemetry) else load_traffic(w.name)
-    value = K * tokens / elapsed
+    res = run_scan(args, args.workload, K, W, args.cpu_work_seconds)
+    if args.kernel_only:
+        print(json.dumps(res), flush=True)
+        return
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": res.pop("value"),
         "unit": "history tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(elapsed / K * 1e3, 6),
+        "ms_per_step": res.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "batch": B,
-            "tokens_per_step": tokens,
-            "max_len": max_len,
-            "vocab": w.vocab,
-            "rotating_sets": R,
-            "rotating_bytes": R * set_bytes,
-            "launch": (f"HIP graph of {R} steps, "
-                       + ("4 entry points (4 kernels) per step" if args.separate
-                          else "lookup_decode_step (1 kernel) per step")),
-            "telemetry": args.telemetry,
-            "scan_balance": int(args.balance),
-        },
-        "lookups_per_s": round(K * B / elapsed, 1),
-        "step_hbm_gbps": round(value * 4 / 1e9, 2),
-        "step_pct_peak": round(value * 4 / 1e9 / HBM_PEAK_GBPS * 100, 2),
-        "read_ceiling": ceiling,
-        "prefilter_survival": round(prefilter_survival(w), 6),
-        "work_spread": work_spread(lcd, w, max_len, p),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel": ("lookup_scan_kernel<4,kPropose>" if args.separate
-                       else "lookup_scan_kernel<4,kStep>"),
-            "kernel_us_mean": round(k_avg * 1e6, 3),
-            "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, x)) * 1e6, 3)
-                                      for x in (10, 50, 90)],
-            "alg_bytes_per_launch": alg_bytes,
-            "launches_timed": n_k,
-        },
     }
-    if args.cpu_work_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_work_seconds)
-    else:
-        out["cpu_baseline"] = None
+    out.update(res)
+    if args.workload == "c3" and not args.only:
+        # the target configuration (64 x 150k) and the ragged batch, measured
+        # in the same run: kernel, roofline and ceiling, and a shorter
+        # graph-timed run of whole steps
+        more = {}
+        for name in ("c4", "c5"):
+            r = run_scan(args, name, min(K, 4000), min(W, 400), 0, extra=True)
+            more[name] = {k: r[k] for k in ("value", "ms_per_step", "config", "lookups_per_s",
+                                            "step_pct_peak", "read_ceiling", "launch_floor",
+                                            "roofline", "work_spread")}
+            more[name]["steps"] = min(K, 4000)
+        out["more_configs"] = more
     print(json.dumps(out), flush=True)
 
 
@@ -675,11 +744,7 @@ def cpu_baseline_sampled(sb, work_seconds):
     import oracle
     if not os.path.exists(os.path.join(ROOT, "oracle", "liblcd_oracle.so")):
         oracle.build()
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores, aff = host_threads()
     chunks = [list(range(i, sb.B, cores)) for i in range(cores)]
 
     def run_chunk(idx):
@@ -709,6 +774,8 @@ def cpu_baseline_sampled(sb, work_seconds):
         "unit": "vocabulary probabilities/s",
         "cores": cores,
         "kind": "oracle",
+        "affinity_cpus": aff,
+        "cpu_model": cpu_model(),
         "sample": (f"{batches} full sampled-verification steps of the {sb.B}-request batch "
                    f"({probs} probabilities scanned each), threads over requests, "
                    f"{wall:.1f} s wall"),

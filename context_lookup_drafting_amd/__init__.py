@@ -100,8 +100,10 @@ def load():
         L.lookup_launch_shape.argtypes = [i32, i32, pp, P, P, P]
         L.lookup_launch_shape.restype = ctypes.c_int
         L.lookup_scan_occupancy.argtypes = [i32, P]
-        L.lcd_read_probe.argtypes = [P, ctypes.c_int64, i32, P, P, P, P]
+        L.lcd_read_probe.argtypes = [P, ctypes.c_int64, i32, i32, P, P, P, P]
         L.lcd_read_probe.restype = ctypes.c_int
+        L.lcd_empty_probe.argtypes = [i32, P, P, P]
+        L.lcd_empty_probe.restype = ctypes.c_int
         L.lookup_index_plan.argtypes = [P, i32, pp, P, P]
         L.lookup_index_plan.restype = ctypes.c_int64
         L.lookup_index_build.argtypes = [P, P, P, i32, pp, i32, P, P, P, ctypes.c_size_t, P, P, i32, P]
@@ -618,16 +620,29 @@ def scan_occupancy(waves: int) -> int:
     return n.value
 
 
-def read_probe(buf, nbytes: int, blocks: int, out, ev_start=None, ev_stop=None):
-    """Plain streaming read of the first `nbytes` of a device tensor (measurement)."""
+PROBE_VARIANTS = {"contig4": 0, "contig8": 1, "interleave4": 2, "interleave8": 3,
+                  "interleave16": 4}
+
+
+def read_probe(buf, nbytes: int, blocks: int, out, ev_start=None, ev_stop=None,
+               variant: str = "contig4"):
+    """Plain streaming read of the first `nbytes` of a device tensor
+    (measurement); ``out`` is int32 [blocks]."""
     import torch
     dev = buf.device
     if nbytes > buf.numel() * buf.element_size():
         raise ValueError("read beyond the buffer")
     _check("lcd_read_probe", load().lcd_read_probe(
         ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(int(nbytes)), ctypes.c_int32(int(blocks)),
-        _dev(out, "out", torch.float32, int(blocks), dev), _stream(dev),
-        ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
+        ctypes.c_int32(PROBE_VARIANTS[variant]), _dev(out, "out", torch.int32, int(blocks), dev),
+        _stream(dev), ctypes.c_void_p(ev_start or None), ctypes.c_void_p(ev_stop or None)))
+
+
+def empty_probe(blocks: int, device, ev_start=None, ev_stop=None):
+    """A kernel of `blocks` workgroups that does nothing (launch floor)."""
+    _check("lcd_empty_probe", load().lcd_empty_probe(
+        ctypes.c_int32(int(blocks)), _stream(device), ctypes.c_void_p(ev_start or None),
+        ctypes.c_void_p(ev_stop or None)))
 
 
 from .drafter import LookupDrafter  # noqa: E402  (the stateful wrapper over the calls above)

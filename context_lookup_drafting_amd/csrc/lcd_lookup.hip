@@ -10,8 +10,8 @@
 // nothing.  The article runs one Triton program per request on a consumer GPU;
 // the design here is built around gfx950 instead:
 //
-//  * The candidate ends of every request are cut into chunks of T tokens
-//    (whole 256-token tiles; the host derives T from the longest row), one
+//  * The candidate ends of every request are cut into chunks of T tokens (a
+//    multiple of 256; the host derives T from the longest row), one
 //    workgroup per chunk, B x cpr workgroups per launch: four waves each, or
 //    sixteen for batches of at most 128 long rows (one workgroup per CU from
 //    32 rows of 16k+ tokens, or of 8k+ tokens and 1.2M+ in all; one per ~12k
@@ -24,19 +24,24 @@
 //    suffix tokens (one per lane) and the wave's first batch of tiles go into
 //    the vector memory queue back to back, so the suffix is waited for alone
 //    and each tile as it lands.
-//  * Lane i of a wave holds tokens 4i..4i+3 of a tile from one 16-byte load:
-//    one wave-wide load moves 1 KiB, fully coalesced.
+//  * A tile is one 16-byte load per lane, 1 KiB per wave-wide load, fully
+//    coalesced: lanes 4..63 hold 240 candidate ends and lanes 0..3 the 16
+//    tokens before them, which the tile before also loaded.  Every test of a
+//    tile then reads only its own registers, so tiles need no order: the
+//    waves of a workgroup take them from a counter in LDS as they go, and
+//    waves whose loads return early take over the tiles of waves whose loads
+//    return late (in one launch the loads of the first round arrive over
+//    about 3 us, and with fixed shares the last wave of a workgroup finished
+//    that much after its first).
 //  * Quick test: a tile can hold a candidate only if it holds the rarest
-//    adjacent pair of suffix tokens (s_j, s_j+1), possibly straddling the tile
-//    before it, or the tile before it holds one in its last lane: eight
-//    compares per lane and one scalar branch per tile.  A wave whose pair
-//    turns out to be common drops the quick test and runs the full one.
+//    adjacent pair of suffix tokens (s_j, s_j+1): eight compares per lane and
+//    one scalar branch per tile.  A wave whose pair turns out to be common
+//    drops the quick test and runs the full one.
 //  * Flagged tiles get the full 4-token test: each lane receives the previous
 //    lane's last three tokens by one wave-wide DPP lane shift, compares the
 //    four tokens ending at each of its positions, and one ballot per
 //    component gives the wave-uniform survivor masks.  Survivors are extended
-//    up to l_max tokens with ballot masks shifted by whole lanes, from the
-//    registers holding the tile and the one before it.
+//    up to l_max tokens with ballot masks shifted by whole lanes.
 //  * A packed key (length, end) orders candidates.  Every workgroup of a
 //    request takes an arrival ticket when it starts (one atomic add, in flight
 //    during its scan), and at the end publishes its best key together with the
@@ -86,7 +91,8 @@ constexpr int kNumCUs = 256;
 // 19.9-20.7 us at 1792).  Forcing 8 waves per SIMD with a launch bound cost
 // more in spilled registers than it gained.
 constexpr int kResidentSmall = 7;
-constexpr int kTileTok = 256;   // 64 lanes x 4 tokens
+constexpr int kTileTok = 256;   // chunk lengths are multiples of this
+constexpr int64_t kMaxChunk = int64_t(1) << 28;   // a chunk's descriptor range stays below 2^32 bytes
 #ifndef LCD_UNROLL
 #define LCD_UNROLL 4
 #endif
@@ -110,7 +116,6 @@ constexpr int kReqWords = 2 + kMaxCpr * kSlotWords;
 constexpr u64 kTagLimit = (1ull << 28) - 1;               // epochs 0 .. kTagLimit - 1
 constexpr int kPollMax = 1 << 20;                         // gathering polls, at most (default)
 constexpr int kBufferWord3 = 0x00020000;                  // gfx9 buffer descriptor, dword 3
-constexpr int kNoTile = 1 << 19;                          // a tile index past every descriptor
 constexpr int kFullAfter = 4;                             // flagged tiles before a wave drops the quick test
 
 struct ScanArgs {
@@ -144,7 +149,7 @@ __host__ __device__ inline int32_t balanced_chunk_len(int64_t total, int64_t lon
     if (t < t2) t = t2;
     t = (t + 255) / 256 * 256;
     if (t < 256) t = 256;
-    return (int32_t)(t < (int64_t(1) << 30) ? t : (int64_t(1) << 30));
+    return (int32_t)(t < kMaxChunk ? t : kMaxChunk);
 }
 
 __host__ __device__ inline int balanced_chunks(int64_t nc, int32_t t) {
@@ -160,9 +165,24 @@ __device__ __forceinline__ int tok(const int4 &t, int c) {
     return c == 0 ? t.x : (c == 1 ? t.y : (c == 2 ? t.z : t.w));
 }
 
-// Replace the tokens of this lane's granule that lie before the row start by
-// `sent`; `rel` is the row start minus the granule's first position.
-__device__ __forceinline__ int4 mask_before(int4 t, int rel, int sent) {
+// Tiles.  A tile is one wave-wide load of 256 consecutive tokens, 16 bytes
+// per lane: lanes 0..3 repeat the last 16 tokens of the tile before it and
+// lanes 4..63 hold the tile's own 240 candidate ends.  A candidate's 4-token
+// test and its extension up to 16 tokens reach back at most 4 lanes, so every
+// test of a tile reads only its own registers: any wave can take any tile, in
+// any order, with no halo load and nothing carried from tile to tile.
+constexpr int kHaloLanes = 4;
+constexpr int kTileCand = (64 - kHaloLanes) * 4;          // 240 candidate ends per tile
+constexpr int kHaloTok = kHaloLanes * 4;                  // 16 tokens before them
+constexpr u64 kCandLanes = ~0ull << kHaloLanes;           // lanes holding candidates
+constexpr u64 kPairLanes = ~0ull << (kHaloLanes - 1);     // pair positions a candidate can need
+constexpr unsigned kNoTileOff = 0x80000000u;              // past every chunk's descriptor
+
+// Lanes 0..3 and the tokens of lane 4 before the row start (`lo`: the row
+// start's position within lane 4's granule) become `sent`: the head chunk's
+// first tile.
+__device__ __forceinline__ int4 mask_head(int4 t, int lane, int lo, int sent) {
+    const int rel = lane < kHaloLanes ? 4 : (lane == kHaloLanes ? lo : 0);
     t.x = (0 < rel) ? sent : t.x;
     t.y = (1 < rel) ? sent : t.y;
     t.z = (2 < rel) ? sent : t.z;
@@ -170,20 +190,20 @@ __device__ __forceinline__ int4 mask_before(int4 t, int rel, int sent) {
     return t;
 }
 
-// Prefilter survivors of tile t (previous tile pt) whose tile index is kt,
-// restricted to candidate ends in [c_lo, c_hi): bit i of P[c] is set when the
-// PF tokens ending at position 4i+c equal s_0..s_PF-1.  Positions before the
-// lane's own granule are the previous lane's last three tokens, brought over
-// by one wave-wide lane shift (lane 0 takes the previous tile's lane 63), so
-// every test is a per-lane compare and one ballot per component.
+// Prefilter survivors of tile t (tile index kt), restricted to candidate
+// ends in [c_lo, c_hi) (positions relative to the chunk's first granule):
+// bit i of P[c] is set when the PF tokens ending at position 4i+c of the tile
+// equal s_0..s_PF-1.  Positions before the lane's own granule are the
+// previous lane's last three tokens, brought over by one wave-wide lane shift,
+// so every test is a per-lane compare and one ballot per component.
 constexpr int kDppWaveShr1 = 0x138;          // DPP: lane i reads lane i-1
 
 template <int PF>
-__device__ __forceinline__ void survivors(const int4 &t, const int4 &pt, const int (&s)[4], int kt,
-                                          int c_lo, int c_hi, int lane, u64 (&P)[4]) {
-    const int q1 = __builtin_amdgcn_update_dpp(__builtin_amdgcn_readlane(pt.y, 63), t.y, kDppWaveShr1, 0xf, 0xf, false);
-    const int q2 = __builtin_amdgcn_update_dpp(__builtin_amdgcn_readlane(pt.z, 63), t.z, kDppWaveShr1, 0xf, 0xf, false);
-    const int q3 = __builtin_amdgcn_update_dpp(__builtin_amdgcn_readlane(pt.w, 63), t.w, kDppWaveShr1, 0xf, 0xf, false);
+__device__ __forceinline__ void survivors(const int4 &t, const int (&s)[4], int kt, int c_lo,
+                                          int c_hi, int lane, u64 (&P)[4]) {
+    const int q1 = __builtin_amdgcn_update_dpp(0, t.y, kDppWaveShr1, 0xf, 0xf, true);
+    const int q2 = __builtin_amdgcn_update_dpp(0, t.z, kDppWaveShr1, 0xf, 0xf, true);
+    const int q3 = __builtin_amdgcn_update_dpp(0, t.w, kDppWaveShr1, 0xf, 0xf, true);
     // token at position 4i+c-j: component c-j of this lane, or component
     // c-j+4 (1..3) of the previous lane
     auto at = [&](int c, int j) -> int {
@@ -195,26 +215,27 @@ __device__ __forceinline__ void survivors(const int4 &t, const int4 &pt, const i
         bool ok = true;
 #pragma unroll
         for (int j = 0; j < PF; ++j) ok = ok && (at(c, j) == s[j]);
-        P[c] = ballot(ok);
+        P[c] = ballot(ok) & kCandLanes;
     }
-    const int A = kTileTok * kt;
-    if (A < c_lo || A + kTileTok > c_hi) {
+    const int A = kTileCand * kt;                  // the tile's first candidate position
+    if (A < c_lo || A + kTileCand > c_hi) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int x = A + 4 * lane + c;
+            const int x = A + 4 * (lane - kHaloLanes) + c;
             P[c] &= ballot(x >= c_lo && x < c_hi);
         }
     }
 }
 
-// Extend the survivors M[c] of tile t (previous tile pt), which match PF
-// suffix tokens, one token at a time while some candidate still matches, up
-// to J tokens; sv holds suffix token s_j in lane j.  Returns the length
+// Extend the survivors M[c] of tile t, which match PF suffix tokens, one
+// token at a time while some candidate still matches, up to J tokens; sv
+// holds suffix token s_j in lane j.  Position e-j lies k = ceil((j-c)/4) <= 4
+// lanes back, inside the tile for every candidate lane.  Returns the length
 // reached and leaves in M the candidates reaching it.  Fully unrolled: a loop
 // here, inside the unrolled tile loop, would make the compiler wait for every
 // load in flight at its header.
 template <int PF>
-__device__ __forceinline__ int extend(const int4 &t, const int4 &pt, int sv, int J, u64 (&M)[4]) {
+__device__ __forceinline__ int extend(const int4 &t, int sv, int J, u64 (&M)[4]) {
     // J is opaque here, so the compiler cannot hoist the per-length tests
     // j < J out of the tile loop: held there, they took about twenty scalar
     // registers for the whole scan and were spilled into vector lanes.
@@ -231,13 +252,7 @@ __device__ __forceinline__ int extend(const int4 &t, const int4 &pt, int sv, int
             for (int c = 0; c < 4; ++c) {
                 const int k = (j - c + 3) >> 2;      // lanes back: ceil((j-c)/4), 0..4
                 const int cc = (c - j) & 3;          // component of position e-j
-                const u64 cur = ballot(tok(t, cc) == sj);
-                u64 term = cur;
-                if (k > 0) {
-                    const u64 prv = ballot(tok(pt, cc) == sj);
-                    term = (cur << k) | (prv >> (64 - k));
-                }
-                N[c] = M[c] & term;
+                N[c] = M[c] & (ballot(tok(t, cc) == sj) << k);
                 any |= N[c];
             }
             if (any != 0) {
@@ -252,20 +267,12 @@ __device__ __forceinline__ int extend(const int4 &t, const int4 &pt, int sv, int
     return L;
 }
 
-// A register copy the compiler cannot fold away: the copy, not the source,
-// lives on, so a load can reuse the source's registers (a folded copy would
-// make the compiler load elsewhere and wait for the data to move it back).
-__device__ __forceinline__ int4 copy_tile(const int4 &t) {
-    int4 c;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(c.x) : "v"(t.x));
-    asm volatile("v_mov_b32 %0, %1" : "=v"(c.y) : "v"(t.y));
-    asm volatile("v_mov_b32 %0, %1" : "=v"(c.z) : "v"(t.z));
-    asm volatile("v_mov_b32 %0, %1" : "=v"(c.w) : "v"(t.w));
-    return c;
-}
-
-__device__ __forceinline__ int4 load_granule(const int32_t *__restrict__ hist, int64_t pos) {
-    return *reinterpret_cast<const int4 *>(hist + pos);
+// Workgroup barrier ordering LDS only: the tile loads in flight are not
+// waited for (a full __syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Kernel modes.  kPropose: the lookup only.  kStep: the whole decode step; the
@@ -457,6 +464,13 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
     // (e its end, D = n-1-e); loaded when the match is found, so the load is
     // off the path that follows the scan
     int btok = 0;
+    // Tiles of a chunk are handed out inside the workgroup: slot u of wave w
+    // starts with tile w + kWaves*u, and every slot refilled after that takes
+    // the next tile from this counter (taken one refill ahead), so waves
+    // whose loads return early take over the tiles of waves whose loads
+    // return late.  A chunk of at most kWaves*kUnroll tiles is all in the
+    // first round: no counter.
+    __shared__ int s_next;
     // One chunk per workgroup when every row fits in cpr chunks of T; a longer
     // row is covered by letting each workgroup take every cpr-th chunk.
     for (int ch = c0; ch < contrib; ch += cpr) {
@@ -465,38 +479,47 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         const bool head = (seg_a == 0);                                   // holds the row start
 
         // Candidate ends of this chunk, as positions relative to X0 (the
-        // 16-byte granule holding the first one); this wave's tiles.
+        // 16-byte granule holding the first one), and its tiles.
         const int64_t cand_lo = ro + seg_a;
         const int64_t X0 = cand_lo & ~(int64_t)3;
-        const int32_t *__restrict__ hb = hist + X0;                        // uniform base
         const int c_lo = (int)(cand_lo - X0);                              // 0..3 (the row start if head)
         const int c_hi = c_lo + (int)(seg_b - seg_a);                      // exclusive
-        const int nt = (c_hi + kTileTok - 1) / kTileTok;                   // >= 1
-        const int tpw = (nt + kWaves - 1) / kWaves;
-        const int k0 = uni(tpw * wave);
-        const int k1 = uni(min(k0 + tpw, nt));
+        const int nt = (c_hi + kTileCand - 1) / kTileCand;                 // >= 1
         const int g_last = (c_hi - 1) & ~3;        // last granule with a candidate
 
-        // Tiles are read through a buffer descriptor covering exactly the
-        // chunk's granules: the hardware range check turns reads past the last
-        // candidate's granule into zeros (those positions are never
-        // candidates), so no load leaves the chunk.  In the head chunk the
-        // halo before the first tile re-reads granule 0 (and is masked).
+        // Tiles are read through a buffer descriptor from the 16 tokens
+        // before the chunk's first granule to the last candidate's granule:
+        // the hardware range check turns reads past it into zeros (those
+        // positions are never candidates), so no load leaves the chunk.  In
+        // the head chunk the 16 tokens before the row are not read: those
+        // lanes of its first tile re-read the first granule and are masked.
+        // (The descriptor's base may then lie before the buffer; nothing is
+        // read there.)
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<int32_t *>(hb), 0, (g_last + 4) * 4, kBufferWord3);
+            const_cast<int32_t *>(hist + X0 - kHaloTok), 0, (g_last + 4 + kHaloTok) * 4,
+            kBufferWord3);
+        const unsigned lane_off = 16u * (unsigned)lane;
+        const unsigned head_off = head ? (unsigned)kHaloTok * 4u : 0u;
         auto load_tile = [&](int kt) -> int4 {
-            return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rsrc, kTileTok * 4 * kt + 16 * lane, 0, 0));
+            unsigned off = (unsigned)(kTileCand * 4) * (unsigned)kt + lane_off;
+            off = kt < nt ? off : kNoTileOff;
+            off = off < head_off ? head_off : off;
+            return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
         };
-        const int kl = (k1 > k0) ? k1 - 1 : nt - 1;
+        int idx[kUnroll];
         int4 buf[kUnroll];
-        int4 halo;                                 // 16 tokens before tile k0 (lanes 60..63)
-        {
-            const int off = kTileTok * min(k0, kl) - kTileTok + 4 * max(lane, 60);
-            halo = load_granule(hb, head ? max(off, 0) : off);
-        }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) buf[u] = load_tile(min(k0 + u, kl));
+        for (int u = 0; u < kUnroll; ++u) {
+            idx[u] = wave + kWaves * u;
+            buf[u] = load_tile(idx[u]);
+        }
+        // the counter of this chunk: every wave is done with the last one's
+        const bool dyn = nt > kWaves * kUnroll;
+        if (dyn) {
+            if (ch != c0) lds_barrier();
+            if (tid == 0) s_next = 0;
+            lds_barrier();
+        }
 
         // The suffix is needed now; the empty asm keeps its lane reads here,
         // behind the tile loads, instead of hoisted ahead of them.
@@ -528,23 +551,18 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
             }
         }
 
-        if (k0 < k1) {
-            // Only the head chunk's first tile and the halo before it can hold
-            // positions before the row start; they become `sent`.
-            if (head && k0 == 0) {
-                halo = make_int4(sent, sent, sent, sent);
-                if (c_lo > 0) buf[0] = mask_before(buf[0], c_lo - 4 * lane, sent);
-            }
+        if (wave < nt) {
+            // The head chunk's first tile is wave 0's first: its lanes before
+            // the row start become `sent`.
+            if (head && wave == 0) buf[0] = mask_head(buf[0], lane, c_lo, sent);
             // Quick test.  A candidate end e needs h[e-j] == s_j for every
             // j < PF; with PF >= 2 it needs in particular the adjacent pair
-            // s_j at p = e-j and s_{j+1} at p-1.  So a tile can hold a
-            // candidate only if it holds such a pair (the pair's second token
-            // may be the previous tile's last position), or if the previous
-            // tile holds one in its last lane (then e may lie in this tile).
-            // Each wave picks the pair that is rarest in its first tile; the
-            // choice only changes how many tiles get the full test, never the
-            // result.  Pairs, unlike single tokens, stay rare when every
-            // suffix token is a common one.  (PF = 1: the single token s_0.)
+            // s_j at p = e-j and s_{j+1} at p-1, both inside e's tile.  So a
+            // tile can hold a candidate only if it holds such a pair.  Each
+            // wave picks the pair that is rarest in its first tile; the choice
+            // only changes how many tiles get the full test, never the result.
+            // Pairs, unlike single tokens, stay rare when every suffix token
+            // is a common one.  (PF = 1: the single token s_0.)
             int cnt[4] = {0, 0, 0, 0};
             {
                 const int4 t = buf[0];
@@ -564,48 +582,40 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
             }
             const int sa = uni(jp == 0 ? s4[0] : jp == 1 ? s4[1] : s4[2]);                   // s_jp
             const int sb = uni(PF >= 2 ? (jp == 0 ? s4[1] : jp == 1 ? s4[2] : s4[3]) : s4[0]);  // s_jp+1
-            u64 cb = 0;          // the previous tile's last position holds s_jp+1
-            // pair hits of tile t (bit i of the result: a pair with p in lane i)
+            // pair hits of tile t (bit i: a pair whose later token p lies in lane i)
             auto quick = [&](const int4 &t) -> u64 {
-                if (PF < 2) return ballot(t.x == sa) | ballot(t.y == sa) | ballot(t.z == sa) | ballot(t.w == sa);
+                if (PF < 2)
+                    return (ballot(t.x == sa) | ballot(t.y == sa) | ballot(t.z == sa) | ballot(t.w == sa)) &
+                           kCandLanes;
                 const u64 a0 = ballot(t.x == sa), a1 = ballot(t.y == sa);
                 const u64 a2 = ballot(t.z == sa), a3 = ballot(t.w == sa);
                 const u64 b0 = ballot(t.x == sb), b1 = ballot(t.y == sb);
                 const u64 b2 = ballot(t.z == sb), b3 = ballot(t.w == sb);
-                const u64 q = (a1 & b0) | (a2 & b1) | (a3 & b2) | (a0 & ((b3 << 1) | cb));
-                cb = b3 >> 63;
-                return q;
+                return ((a1 & b0) | (a2 & b1) | (a3 & b2) | (a0 & (b3 << 1))) & kPairLanes;
             };
-            int4 prev = halo;                        // the tile before the next one processed
-            u64 carry = quick(prev) >> 63;           // a hit in its last lane
             // A wave whose pair turns out to be common stops running the quick
             // test after kFullAfter flagged tiles and gives every tile the
             // full test (which the quick test would have passed anyway).
             int nflag = 0;
-            // Test tile kt (tokens t) against its predecessor prev.
             auto test_tile = [&](const int4 &t, int kt) {
                 bool flagged = true;
-                if (nflag < kFullAfter) {
-                    const u64 q = quick(t);
-                    flagged = (q | carry) != 0;
-                    carry = q >> 63;
-                }
+                if (nflag < kFullAfter) flagged = quick(t) != 0;
                 if (flagged) {
                     ++nflag;
-                    u64 P[4];
-                    survivors<PF>(t, prev, s4, kt, c_lo, c_hi, lane, P);
-                    if ((P[0] | P[1] | P[2] | P[3]) != 0) {
-                        const int L = extend<PF>(t, prev, sv, J, P);
+                    u64 P4[4];
+                    survivors<PF>(t, s4, kt, c_lo, c_hi, lane, P4);
+                    if ((P4[0] | P4[1] | P4[2] | P4[3]) != 0) {
+                        const int L = extend<PF>(t, sv, J, P4);
                         if (L >= a.l_min) {
                             int ebest = -1;
 #pragma unroll
                             for (int c = 0; c < 4; ++c) {
-                                if (P[c] != 0) {
-                                    const int e = 4 * (63 - __clzll(P[c])) + c;
+                                if (P4[c] != 0) {
+                                    const int e = 4 * (63 - __clzll(P4[c])) + c;
                                     ebest = e > ebest ? e : ebest;
                                 }
                             }
-                            const int64_t e_abs = X0 + kTileTok * (int64_t)kt + ebest;
+                            const int64_t e_abs = X0 + kTileCand * (int64_t)kt + ebest - kHaloTok;
                             const u64 key = ((u64)L << kLenShift) | (u64)(uint32_t)(e_abs - ro);
                             if (key > best) {
                                 best = key;
@@ -615,26 +625,36 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
                         }
                     }
                 }
-                prev = copy_tile(t);                 // frees the slot's registers for a refill
             };
-            // Each wave keeps kUnroll tiles in flight.  While tiles remain
-            // beyond the current round, every slot is refilled with the tile
-            // kUnroll ahead as soon as its own tile has been tested (a refill
-            // past the wave's range points outside the descriptor: zeros, no
-            // memory access), so the loads form one regular sequence.
-            int kb = k0;
-            for (; kb + kUnroll < k1; kb += kUnroll) {
+            // Each wave keeps kUnroll tiles in flight: a slot is refilled as
+            // soon as its tile has been tested, with the tile taken from the
+            // counter one refill earlier (a tile past the chunk points outside
+            // the descriptor: zeros, no memory access).  The tiles a wave
+            // takes only grow, so once slot 0 holds none, no slot does.
+            auto take = [&]() -> int {
+                int v = 0;
+                if (lane == 0)
+                    v = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                return v;
+            };
+            if (dyn) {
+                int pend = take();
+                for (;;) {
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    test_tile(buf[u], kb + u);
-                    const int nx = kb + u + kUnroll;
-                    buf[u] = load_tile(nx < k1 ? nx : kNoTile);
+                    for (int u = 0; u < kUnroll; ++u) {
+                        if (idx[u] < nt) test_tile(buf[u], idx[u]);
+                        const int nx = uni(pend) + kWaves * kUnroll;
+                        idx[u] = nx;
+                        buf[u] = load_tile(nx);
+                        pend = take();
+                    }
+                    if (idx[0] >= nt) break;
                 }
-            }
-            // the last round: the remaining tiles are in the slots already
+            } else {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                if (kb + u < k1) test_tile(buf[u], kb + u);
+                for (int u = 0; u < kUnroll; ++u)
+                    if (idx[u] < nt) test_tile(buf[u], idx[u]);
+            }
         }
         // Nothing is in flight here; saying so keeps the compiler from waiting
         // on the next chunk's loads for registers this chunk's loads used.
@@ -746,12 +766,12 @@ int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
 }
 
 // Chunk length: the longest row's candidate ends (max_len - 1) split over cpr
-// chunks, in whole tiles, at most 2^30 so chunk-relative positions fit in 32 bits.
+// chunks, a multiple of kTileTok, at most kMaxChunk.
 int32_t chunk_len(int32_t max_len, int cpr) {
     const int64_t nc = max_len > 1 ? (int64_t)max_len - 1 : 1;
     int64_t T = (nc + cpr - 1) / cpr;
     T = (T + kTileTok - 1) / kTileTok * kTileTok;
-    return (int32_t)(T < (int64_t(1) << 30) ? T : (int64_t(1) << 30));
+    return (int32_t)(T < kMaxChunk ? T : kMaxChunk);
 }
 
 template <int PF, int kMode, bool kBal, int kW>

@@ -488,12 +488,27 @@ int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, const i
 /*
  * lcd_read_probe -- measurement only: a plain streaming read of `bytes`
  * (a multiple of 16, 16-byte aligned device buffer) by `blocks` workgroups of
- * 256 threads, each writing one float to out[blocks] (device).  The GPU stamps
- * the kernel's start and end into ev_start / ev_stop (hipEvent_t, nullable).
- * It gives the practical HBM read ceiling at a byte count on the running GPU.
+ * 256 threads, each writing one int32 to out[blocks] (device), in one of the
+ * variants below (loads in flight per lane; each workgroup reading one
+ * contiguous share, or the workgroups interleaved over blocks of 256 x depth
+ * granules).  The GPU stamps the kernel's start and end into ev_start /
+ * ev_stop (hipEvent_t, nullable).  The best variant and grid gives the
+ * practical HBM read ceiling at a byte count on the running GPU.
  */
-int lcd_read_probe(const void *buf, int64_t bytes, int32_t blocks, float *out, void *stream,
-                   void *ev_start, void *ev_stop);
+#define LCD_PROBE_CONTIG_4 0
+#define LCD_PROBE_CONTIG_8 1
+#define LCD_PROBE_INTERLEAVE_4 2
+#define LCD_PROBE_INTERLEAVE_8 3
+#define LCD_PROBE_INTERLEAVE_16 4
+int lcd_read_probe(const void *buf, int64_t bytes, int32_t blocks, int32_t variant, int32_t *out,
+                   void *stream, void *ev_start, void *ev_stop);
+
+/*
+ * lcd_empty_probe -- measurement only: a kernel of `blocks` workgroups of 256
+ * threads that does nothing, with GPU-stamped events as for lcd_read_probe:
+ * the floor of one launch (dispatch and completion) on the running GPU.
+ */
+int lcd_empty_probe(int32_t blocks, void *stream, void *ev_start, void *ev_stop);
 
 /* Largest vocabulary rejection_accept takes (2^22). */
 #define LCD_SAMPLE_MAX_VOCAB 4194304
