@@ -289,32 +289,74 @@ __device__ __forceinline__ u64 wave_max(u64 v) {
     return v;
 }
 
+__device__ __forceinline__ u64 readlane64(u64 v, int l) {
+    return ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+}
+
+// Running maximum within each row of 16 lanes (DPP row shifts by 1, 2, 4, 8;
+// lanes with no source read 0): lane 15 ends with the maximum of lanes 0..15.
+template <int kCtrl>
+__device__ __forceinline__ u64 dpp_shr64(u64 v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kCtrl, 0xf, 0xf, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), kCtrl, 0xf, 0xf, true);
+    return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ u64 row_max64(u64 v) {
+    u64 o = dpp_shr64<0x111>(v);
+    v = o > v ? o : v;
+    o = dpp_shr64<0x112>(v);
+    v = o > v ? o : v;
+    o = dpp_shr64<0x114>(v);
+    v = o > v ? o : v;
+    o = dpp_shr64<0x118>(v);
+    return o > v ? o : v;
+}
+
+// A struct of 4-byte words spread over lanes (word k in lane k), read back
+// into scalar registers without a memory access.
+template <typename T>
+__device__ __forceinline__ T from_lanes(int v) {
+    static_assert(sizeof(T) % 4 == 0 && sizeof(T) <= 256, "one word per lane");
+    int w[sizeof(T) / 4];
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(T) / 4); ++k) w[k] = __builtin_amdgcn_readlane(v, k);
+    return __builtin_bit_cast(T, w);
+}
+
+// The lookup's outputs and the rest of the step's inputs and outputs: the
+// scan kernel's first argument.
+struct ScanOut {
+    int32_t *match_len, *match_end, *draft;
+    StepIO io;
+};
+constexpr int kOutWords = (int)(sizeof(ScanOut) / 4);
+
 // Result of request r (row of lr tokens as stored, n = max(lr, 0), at ro)
-// given its best key, run by one whole wave: lane k < 15 holds tok =
-// h[e+1+min(k, D-1)], D = n-1-e, the tokens following the match.  Writes the
-// match and draft and, in kStep mode, the rest of the step (sin: the per-lane
-// step inputs).  `failed`: the merge gave up, reported as m = -1, e = -1 and
-// an empty draft (the step then goes on as without a match).
+// given its best key, run by one whole wave.  The tokens following the
+// match, h[e+1+min(k, D-1)] for k < 15 with D = n-1-e, are in lanes base+k of
+// `src`.  Writes the match and draft and, in kStep mode, the rest of the step
+// (sin: the per-lane step inputs) to the outputs in `so`.  `failed`: the merge
+// gave up, reported as m = -1, e = -1 and an empty draft (the step then goes
+// on as without a match).
 template <int kMode>
-__device__ __forceinline__ void finish_request(int r, u64 key, bool failed, int tok, int sin,
-                                               uint32_t tin, int lane, int64_t ro, int32_t lr, int n,
-                                               int k_max, int32_t *__restrict__ match_len,
-                                               int32_t *__restrict__ match_end,
-                                               int32_t *__restrict__ draft, const StepIO &io) {
+__device__ __forceinline__ void finish_request(int r, u64 key, bool failed, int src, int base,
+                                               int sin, uint32_t tin, int lane, int64_t ro,
+                                               int32_t lr, int n, int k_max, const ScanOut &so) {
     if (failed) key = 0;
     const int m = failed ? -1 : (key ? (int)(key >> kLenShift) : 0);
     const int e = key ? (int)(key & kEndMask) : -1;
     const int D = key ? n - 1 - e : 1;
-    // LZ-style copy: d[k] = h[n - D + (k mod D)], the tok of lane (k mod D)
+    // LZ-style copy: d[k] = h[n - D + (k mod D)], token (k mod D) of the match
     const int kk = lane < LCD_DRAFT_STRIDE ? lane : 0;
-    int dk = __shfl(tok, kk % D);
+    int dk = __shfl(src, base + kk % D);
     dk = (m > 0 && lane < k_max) ? dk : LCD_PAD;
-    if (lane < LCD_DRAFT_STRIDE) draft[(int64_t)r * LCD_DRAFT_STRIDE + lane] = dk;
+    if (lane < LCD_DRAFT_STRIDE) so.draft[(int64_t)r * LCD_DRAFT_STRIDE + lane] = dk;
     if (lane == 0) {
-        match_len[r] = m;
-        match_end[r] = e;
+        so.match_len[r] = m;
+        so.match_end[r] = e;
     }
-    if (kMode == kStep) finish_step(r, m, dk, sin, tin, lane, ro, lr, n, io);
+    if (kMode == kStep) finish_step(r, m, dk, sin, tin, lane, ro, lr, n, so.io);
 }
 
 constexpr int kBalPer = LCD_BALANCE_MAX_B / 64;           // lengths held per lane
@@ -373,13 +415,6 @@ __device__ __forceinline__ bool balanced_assignment(const int32_t *__restrict__ 
     return false;
 }
 
-// The lookup's outputs and the rest of the step's inputs and outputs: the
-// scan kernel's first argument, read where it is used (see the kernel).
-struct ScanOut {
-    int32_t *match_len, *match_end, *draft;
-    StepIO io;
-};
-
 template <int PF, int kMode, bool kBal, int kWaves>
 __global__ void __launch_bounds__(64 * kWaves)
 lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
@@ -417,6 +452,19 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
     }
     int sin = 0;
     uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
+    // 16-wave workgroups: word k of the first argument (the outputs and the
+    // step's pointers and rules) in lane k, loaded now so that the finish
+    // reads them from a register instead of waiting on one argument load
+    // after another (0.1 us at 64 x 25k).  4-wave workgroups, many more per
+    // launch, read them at the finish: the extra load in front of wave 0's
+    // tiles cost them more (0.4 us at 256 ragged rows).
+    constexpr bool kArgsInLanes = kWaves == kWavesLarge;
+    int outv = 0;
+    if (kArgsInLanes && wave == 0) outv = reinterpret_cast<const int *>(op)[lane < kOutWords ? lane : 0];
+    auto outputs = [&]() -> ScanOut {
+        if constexpr (kArgsInLanes) return from_lanes<ScanOut>(outv);
+        else return *op;
+    };
     if (kMode == kStep && wave == 0) {
         const StepIO io0 = op->io;
         sin = load_step_input(r, lane, io0);
@@ -429,8 +477,8 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
     const int nc = n - 1;             // candidate ends 0..n-2
     if (nc <= 0) {                    // no earlier position: chunk 0 finishes the request
         if (c0 == 0 && wave == 0)
-            finish_request<kMode>(r, 0, false, 0, sin, tin, lane, ro, lr, n, a.k_max, op->match_len,
-                                  op->match_end, op->draft, op->io);
+            finish_request<kMode>(r, 0, false, 0, 0, sin, tin, lane, ro, lr, n, a.k_max,
+                                  outputs());
         return;
     }
     if ((int64_t)c0 * T >= nc) return;                  // past the row's last chunk
@@ -661,21 +709,16 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         __builtin_amdgcn_s_waitcnt(0);
     }
 
-    if (lane == 0) s_wkey[wave] = best;
+    // The workgroup's best key: each wave's key with its index in the low 4
+    // bits (keys of different waves differ unless zero), reduced by wave 0
+    // across lanes in one DPP row pass; the winner's staged tokens from LDS.
+    if (lane == 0) s_wkey[wave] = (best << 4) | (u64)wave;
     if (lane < kSlotWords) s_wtok[wave * kSlotWords + lane] = btok;
     __syncthreads();
     if (wave != 0) return;
-    // the workgroup's best key and the tokens its wave staged (lanes 0..14)
-    u64 key = s_wkey[0];
-    int wbest = 0;
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-        if (s_wkey[w] > key) {
-            key = s_wkey[w];
-            wbest = w;
-        }
-    }
-    int tok = s_wtok[wbest * kSlotWords + (lane < kSlotWords ? lane : 0)];
+    const u64 kw = readlane64(row_max64(lane < kWaves ? s_wkey[lane] : 0ull), 15);
+    u64 key = kw >> 4;
+    int tok = s_wtok[(int)(kw & 15) * kSlotWords + (lane < kSlotWords ? lane : 0)];
     if (P > 1) {
         u64 *__restrict__ slots = req + 2;
         // lane 0 took the ticket (P > 1): the arrival count and the call's tag
@@ -692,39 +735,64 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         }
         // Last to start: every other workgroup taking part has started, and
         // publishes without waiting for anything, so the gathering ends.  Its
-        // own key and tokens stay in registers.
+        // own key and tokens stay in registers.  Up to 4 slots (64 words)
+        // are polled one word per lane and kept in registers; more go
+        // through LDS.
         const int nu = P * kSlotWords;
+        const bool in_regs = nu <= 64;
+        const bool is_key = (lane & (kSlotWords - 1)) == kSlotWords - 1;
+        u64 v0 = 0;
         bool all = false;
         for (int tries = 0; tries < a.polls && !all; ++tries) {
             bool ok = true;
-            for (int u = lane; u < nu; u += 64) {
-                if (u / kSlotWords != c0) {
-                    const u64 v = __hip_atomic_load(slots + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    s_units[u] = v;
-                    const bool is_key = (u & (kSlotWords - 1)) == kSlotWords - 1;
-                    ok = ok && ((v >> (is_key ? 36 : 32)) == tag);
+            if (in_regs) {
+                if (lane < nu && lane / kSlotWords != c0) {
+                    v0 = __hip_atomic_load(slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok = (v0 >> (is_key ? 36 : 32)) == tag;
+                }
+            } else {
+                for (int u = lane; u < nu; u += 64) {
+                    if (u / kSlotWords != c0) {
+                        const u64 v = __hip_atomic_load(slots + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        s_units[u] = v;
+                        ok = ok && ((v >> (((u & (kSlotWords - 1)) == kSlotWords - 1) ? 36 : 32)) == tag);
+                    }
                 }
             }
             all = ballot(!ok) == 0;
         }
-        // best key over the slots (keys of different slots differ unless zero):
-        // a scalar pass over the P slot keys, which are few (a 64-bit wave-wide
-        // shuffle reduction is six dependent LDS round trips)
+        // best key over the slots (keys of different slots differ unless
+        // zero): a scalar pass over the P slot keys, which are few
         const u64 kKeyMask = (1ull << 36) - 1;
-        const u64 ks = lane >= P ? 0
-                       : lane == c0 ? key
-                                    : (s_units[lane * kSlotWords + kSlotWords - 1] & kKeyMask);
         u64 kbest = 0;
         int w = c0;
-        for (int j = 0; j < P; ++j) {
-            const u64 kj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(ks >> 32), j) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ks, j);
-            if (kj > kbest) { kbest = kj; w = j; }
+        if (in_regs) {
+            for (int j = 0; j < P; ++j) {
+                const u64 kj = j == c0 ? key : (readlane64(v0, j * kSlotWords + kSlotWords - 1) & kKeyMask);
+                if (kj > kbest) { kbest = kj; w = j; }
+            }
+        } else {
+            const u64 ks = lane >= P ? 0
+                           : lane == c0 ? key
+                                        : (s_units[lane * kSlotWords + kSlotWords - 1] & kKeyMask);
+            for (int j = 0; j < P; ++j) {
+                const u64 kj = readlane64(ks, j);
+                if (kj > kbest) { kbest = kj; w = j; }
+            }
         }
         if (kbest == 0) w = c0;
-        if (w != c0) tok = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
-        finish_request<kMode>(r, kbest, !all, tok, sin, tin, lane, ro, lr, n, a.k_max, op->match_len,
-                              op->match_end, op->draft, op->io);
+        // the winner's tokens: own (in tok), in the polled words, or in LDS
+        int src = tok, base = 0;
+        if (w != c0) {
+            if (in_regs) {
+                src = (int)(uint32_t)v0;
+                base = w * kSlotWords;
+            } else {
+                src = (int)(uint32_t)s_units[w * kSlotWords + (lane < kSlotWords - 1 ? lane : 0)];
+            }
+        }
+        finish_request<kMode>(r, kbest, !all, src, base, sin, tin, lane, ro, lr, n, a.k_max,
+                              outputs());
         // Re-zero the slots for the next call (after the outputs: a wait for
         // these stores' acknowledgement must not sit in front of the finish),
         // unless the gathering gave up: a late publisher may still write into
@@ -735,8 +803,8 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         if (lane == 0) __hip_atomic_store(req, next_header(hdr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    finish_request<kMode>(r, key, false, tok, sin, tin, lane, ro, lr, n, a.k_max, op->match_len,
-                          op->match_end, op->draft, op->io);
+    finish_request<kMode>(r, key, false, tok, 0, sin, tin, lane, ro, lr, n, a.k_max,
+                          outputs());
 }
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
