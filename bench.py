@@ -63,6 +63,8 @@ def parse():
                     help="fused step with per-request acceptance telemetry on")
     ap.add_argument("--lookup", default="scan", choices=["scan", "index"],
                     help="index: decode steps whose lookup comes from the incremental n-gram index")
+    ap.add_argument("--index-load", type=int, default=3,
+                    help="index table slots per indexed length and token of capacity (2..16)")
     ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
                     help="profiling aid: only N eager lookup launches over the rotating sets")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -582,8 +584,8 @@ def bench_index(args):
     extra = 16 * (K + W + 2 * R + 8 + n_k)
     flat, ro, ln, cap = wl.pack_rows(w.hists, extra=extra)
     B = w.B
-    p = lcd.default_params()
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    p = lcd.default_params(index_load=args.index_load)
     h_d, ro_d, ln_d, cap_d = t(flat), t(ro), t(ln.copy()), t(cap)
     q, tgt = w.step_inputs(np.zeros(B, np.int64), 0)
     q_d, tgt_d = t(q), t(tgt)
@@ -683,6 +685,9 @@ def bench_index(args):
                           else "lookup_index_decode_step (1 kernel) per step")),
             "index_build_ms": round(build_ms, 3),
             "index_table_bytes": idx.table_bytes,
+            "index_load": args.index_load,
+            "index_bytes_per_capacity_token": round(idx.table_bytes / float(cap.astype(np.int64).sum()), 2),
+            "index_bytes_per_history_token": round(idx.table_bytes / tokens, 2),
         },
         "lookups_per_s": round(steps_run * B / elapsed, 1),
         "roofline": {

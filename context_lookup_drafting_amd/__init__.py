@@ -55,7 +55,7 @@ class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "l_min", "l_max", "k_max", "n_head", "n_block", "head_full", "head_agree",
         "agree_n", "tail_min", "entry_steps", "sticky", "near_full_slack", "scan_wgs",
-        "scan_balance", "merge_polls")]
+        "scan_balance", "merge_polls", "index_load")]
 
     def __repr__(self):
         return "Params(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -512,18 +512,18 @@ class LookupIndex:
         cap = np.ascontiguousarray(cap, dtype=np.int32)
         self.B = len(cap)
         off = np.zeros(max(self.B, 1), np.int64)
-        bits = np.zeros(max(self.B, 1), np.int32)
+        slots = np.zeros(max(self.B, 1), np.int32)
         nbytes = int(load().lookup_index_plan(cap.ctypes.data_as(ctypes.c_void_p), self.B,
                                                 ctypes.byref(self.p),
                                                 off.ctypes.data_as(ctypes.c_void_p),
-                                                bits.ctypes.data_as(ctypes.c_void_p)))
+                                                slots.ctypes.data_as(ctypes.c_void_p)))
         if nbytes < 0:
             raise LCDError("lookup_index_plan", nbytes)
         self.device = torch.device(device)
         self.table_bytes = max(nbytes, 8)
         self.tables = torch.empty(self.table_bytes // 8, dtype=torch.int64, device=self.device)
         self.table_off = torch.from_numpy(off[:self.B].copy()).to(self.device)
-        self.table_bits = torch.from_numpy(bits[:self.B].copy()).to(self.device)
+        self.table_slots = torch.from_numpy(slots[:self.B].copy()).to(self.device)
         self.indexed_len = torch.zeros(self.B, dtype=torch.int32, device=self.device)
         self._scratch = torch.zeros(max(self.B, 1), dtype=torch.int32, device=self.device)
 
@@ -535,7 +535,7 @@ class LookupIndex:
             _dev(row_off, "row_off", torch.int64, B, dev),
             _dev(lens, "lens", torch.int32, B, dev), ctypes.c_int32(B), ctypes.byref(self.p),
             ctypes.c_int32(self.fp_bits), _dev(self.table_off, "table_off", torch.int64, B, dev),
-            _dev(self.table_bits, "table_bits", torch.int32, B, dev),
+            _dev(self.table_slots, "table_slots", torch.int32, B, dev),
             ctypes.c_void_p(self.tables.data_ptr()), ctypes.c_size_t(self.table_bytes),
             _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
             ctypes.c_void_p(self._scratch.data_ptr()), ctypes.c_int32(int(max_len)), _stream(dev)))
@@ -554,7 +554,7 @@ class LookupIndex:
             _dev(row_off, "row_off", torch.int64, B, dev),
             _dev(lens, "lens", torch.int32, B, dev), ctypes.c_int32(B), ctypes.byref(self.p),
             ctypes.c_int32(self.fp_bits), _dev(self.table_off, "table_off", torch.int64, B, dev),
-            _dev(self.table_bits, "table_bits", torch.int32, B, dev),
+            _dev(self.table_slots, "table_slots", torch.int32, B, dev),
             ctypes.c_void_p(self.tables.data_ptr()),
             _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
             _dev(match_len, "match_len", torch.int32, B, dev),
@@ -581,7 +581,7 @@ class LookupIndex:
             _dev(cap, "cap", torch.int32, B, dev) if cap is not None else nul,
             ctypes.c_int32(B), ctypes.byref(self.p), ctypes.c_int32(self.fp_bits),
             _dev(self.table_off, "table_off", torch.int64, B, dev),
-            _dev(self.table_bits, "table_bits", torch.int32, B, dev),
+            _dev(self.table_slots, "table_slots", torch.int32, B, dev),
             ctypes.c_void_p(self.tables.data_ptr()),
             _dev(self.indexed_len, "indexed_len", torch.int32, B, dev),
             _dev(model_draft, "model_draft", torch.int32, B * Q_STRIDE, dev),

@@ -22,16 +22,19 @@
 // 0 = empty.  Inserting is a compare-and-swap into an empty slot, or a 64-bit
 // atomic max into the slot holding the same fingerprint (same high word, so
 // the max is the larger position); linear probing past other fingerprints.
-// Tables hold at most 1/4 of their slots (the plan sizes them from the
-// capacity of each row).
+// A key's home slot is a multiply-shift of its low word onto the table's
+// exact size (no power-of-two rounding); the plan sizes each table from the
+// row's capacity and lcd_params.index_load (slots per indexed length and
+// token, default 3: at most 1/3 of the slots ever taken).
 //
-// lookup_index_propose: one wave per request.  The positions appended since
-// the last call (lanes over positions) are matched against the suffix
-// directly and inserted (every length's compare-and-swap in flight at once);
-// concurrently the table is queried for all lengths at once (lane k takes
-// L = l_min + k) and the hits verified; the answer is the better of the two.
-// About five dependent memory round trips per step, whatever the history
-// length.
+// lookup_index_propose: one workgroup of two waves per request.  Wave 1
+// inserts the positions appended since the last call (lanes over positions,
+// every length's compare-and-swap in flight at once, collisions probed in
+// rounds).  Wave 0 matches those positions against the suffix directly and
+// queries the table for all lengths at once (lane k takes L = l_min + k),
+// verifying the hits; the answer is the better of the two.  The waves do not
+// wait for each other's memory traffic, so a step costs the longer of the two
+// chains of dependent round trips (about five), whatever the history length.
 //
 // lookup_index_decode_step: the same kernel, whose wave then also does the
 // rest of the decode step for its request (fusion, greedy acceptance with the
@@ -50,10 +53,6 @@ namespace {
 
 using u64 = unsigned long long;
 
-// One wave per workgroup: a request's wave issues scattered probes and
-// atomics, and spreading the waves over more CUs measured 0.1-0.45 us faster
-// per step than four per workgroup (1 x 25k, 64 x 25k, 256 ragged rows).
-constexpr int kWavesPerBlock = 1;
 constexpr int kBuildThreads = 256;
 constexpr int kMaxL = LCD_MAX_SUFFIX;            // 16
 constexpr int kMaxProbe = 1 << 20;               // bound on a probe sequence
@@ -91,11 +90,14 @@ __device__ __forceinline__ u64 entry_of(u64 key, uint32_t mask, int32_t p) {
     return ((u64)fingerprint(key, mask) << 32) | (uint32_t)(p + 1);
 }
 
-// Inserts entry `ent` (key's fingerprint | p + 1) into table T of 2^bits slots,
+// A key's home slot in a table of ns slots, and the slot after slot i.
+__device__ __forceinline__ u64 home_slot(u64 key, uint32_t ns) { return ((u64)(uint32_t)key * ns) >> 32; }
+__device__ __forceinline__ u64 next_slot(u64 i, uint32_t ns) { return i + 1 < ns ? i + 1 : 0; }
+
+// Inserts entry `ent` (key's fingerprint | p + 1) into table T of ns slots,
 // probing from slot i; returns false only if the probe bound was hit (never at
 // the planned load).
-__device__ bool insert_from(u64 *__restrict__ T, int bits, u64 ent, u64 i) {
-    const u64 cmask = ((u64)1 << bits) - 1;
+__device__ bool insert_from(u64 *__restrict__ T, uint32_t ns, u64 ent, u64 i) {
     const u64 fp = ent >> 32;
     for (int probes = 0; probes < kMaxProbe; ++probes) {
         const u64 old = atomicCAS(T + i, 0ull, ent);
@@ -104,14 +106,14 @@ __device__ bool insert_from(u64 *__restrict__ T, int bits, u64 ent, u64 i) {
             atomicMax(T + i, ent);
             return true;
         }
-        i = (i + 1) & cmask;
+        i = next_slot(i, ns);
     }
     return false;
 }
 
-__device__ __forceinline__ bool insert_one(u64 *__restrict__ T, int bits, u64 key, uint32_t mask,
+__device__ __forceinline__ bool insert_one(u64 *__restrict__ T, uint32_t ns, u64 key, uint32_t mask,
                                            int32_t p) {
-    return insert_from(T, bits, entry_of(key, mask, p), key & (((u64)1 << bits) - 1));
+    return insert_from(T, ns, entry_of(key, mask, p), home_slot(key, ns));
 }
 
 // Exact lookup by scanning the whole history (the slow path): one wave, one
@@ -139,13 +141,186 @@ __device__ u64 exact_scan(const int32_t *__restrict__ h, int n, const IndexArgs 
     return best;
 }
 
-// kStep: the wave also finishes its request's decode step (io).
+// Slots read per round trip: by an insert (kWin) and by a query (kQWin).
+// Linear probing keeps a key's run of slots together, so one window of
+// neighbouring slots answers what a probe sequence would ask one slot at a
+// time (the tables hold at least 16 slots, so a window never wraps twice).
+constexpr int kWin = 8;
+constexpr int kQWin = 4;
+constexpr int kLanePairs = 4;          // queued entries one lane probes at once
+constexpr int kQueue = 64 * kMaxL;     // (position, length) entries per 64 positions
+
+__device__ __forceinline__ uint32_t wrap_add(uint32_t i, uint32_t k, uint32_t ns) {
+    const uint32_t j = i + k;          // i < ns <= INT32_MAX and k <= 16 <= ns
+    return j >= ns ? j - ns : j;
+}
+
+__device__ __forceinline__ int wave_exclusive_sum(int x, int lane) {
+    int incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        incl += lane >= d ? y : 0;
+    }
+    return incl - x;
+}
+
+__device__ __forceinline__ void lds_wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Enters the queued entries b.. (up to kLanePairs per lane, all probed at
+// once).  A round reads a window of kWin slots from each entry's next slot,
+// takes the first that is empty or holds the entry's fingerprint, and
+// compare-and-swaps it (empty) or atomically maxes it (same fingerprint).  A
+// compare-and-swap lost to another lane of the wave goes on past that slot.
+// The maxes need no answer and are issued after the round's results are read
+// (a read behind one would wait for it).  Returns false if the probe bound
+// was hit.
+__device__ bool probe_batch(u64 *__restrict__ T, uint32_t ns, const u64 *q_ent,
+                            const uint32_t *q_slot, int b, int total, int lane) {
+    u64 ent[kLanePairs];
+    uint32_t st[kLanePairs], at[kLanePairs];
+    uint32_t act = 0;
+#pragma unroll
+    for (int c = 0; c < kLanePairs; ++c) {
+        const int q = b + lane + 64 * c;
+        ent[c] = q < total ? q_ent[q] : 0ull;
+        st[c] = q < total ? q_slot[q] : 0u;
+        at[c] = 0;
+        act |= q < total ? 1u << c : 0u;
+    }
+    bool ok = true;
+    for (int probed = 0; __ballot(act != 0) != 0; probed += kWin) {
+        if (probed >= kMaxProbe) {
+            ok = act == 0;
+            break;
+        }
+        u64 win[kLanePairs][kWin];
+#pragma unroll
+        for (int c = 0; c < kLanePairs; ++c)
+#pragma unroll
+            for (int w = 0; w < kWin; ++w)
+                win[c][w] = (act >> c) & 1u
+                                ? __hip_atomic_load(T + wrap_add(st[c], w, ns), __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 0ull;
+        uint32_t cas = 0, mx = 0;
+#pragma unroll
+        for (int c = 0; c < kLanePairs; ++c) {
+            if (!((act >> c) & 1u)) continue;
+            const uint32_t fp = (uint32_t)(ent[c] >> 32);
+            int hw = -1;
+            bool same = false;
+#pragma unroll
+            for (int w = kWin - 1; w >= 0; --w) {
+                const bool stop = win[c][w] == 0 || (uint32_t)(win[c][w] >> 32) == fp;
+                hw = stop ? w : hw;
+                same = stop ? win[c][w] != 0 : same;
+            }
+            if (hw < 0) {
+                st[c] = wrap_add(st[c], kWin, ns);            // the whole window taken
+            } else {
+                at[c] = wrap_add(st[c], (uint32_t)hw, ns);
+                if (same) mx |= 1u << c; else cas |= 1u << c;
+            }
+        }
+        u64 old[kLanePairs];
+#pragma unroll
+        for (int c = 0; c < kLanePairs; ++c)
+            old[c] = (cas >> c) & 1u ? atomicCAS(T + at[c], 0ull, ent[c]) : 0ull;
+#pragma unroll
+        for (int c = 0; c < kLanePairs; ++c) {
+            if (!((cas >> c) & 1u)) continue;
+            if (old[c] == 0) {
+                act &= ~(1u << c);
+            } else if ((uint32_t)(old[c] >> 32) == (uint32_t)(ent[c] >> 32)) {
+                mx |= 1u << c;
+            } else {
+                st[c] = wrap_add(at[c], 1, ns);               // taken meanwhile: go on past it
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kLanePairs; ++c)
+            if ((mx >> c) & 1u) atomicMax(T + at[c], ent[c]);
+        act &= ~mx;
+    }
+    return ok;
+}
+
+// The inserting wave: enters the positions p_lo..p_hi (appended since the
+// last call) for every indexed length.  Per 64 positions (lanes), each
+// lane's (position, length) entries are queued in LDS, then probed spread
+// over the lanes (probe_batch), so a position with many entries does not
+// hold its lane for all of them.  Returns false if a probe bound was hit.
+__device__ bool insert_positions(const int32_t *__restrict__ h, u64 *__restrict__ T, uint32_t ns,
+                                 int p_lo, int p_hi, const IndexArgs &a, int lane,
+                                 const int32_t (&t0)[kMaxL], u64 *q_ent, uint32_t *q_slot) {
+    bool ok = true;
+    for (int p0 = p_lo; p0 <= p_hi; p0 += 64) {
+        const int p = p0 + lane;
+        const bool ins = p <= p_hi;
+        // opaque copies of the length bounds: tests against them hoisted out
+        // of this loop were held (and spilled) through the whole kernel
+        int lmin = a.l_min, lmax = a.l_max;
+        asm volatile("" : "+s"(lmin), "+s"(lmax));
+        int32_t t[kMaxL];
+#pragma unroll
+        for (int j = 0; j < kMaxL; ++j)
+            t[j] = p0 == p_lo ? t0[j] : ((ins && j < lmax && p - j >= 0) ? h[p - j] : 0);
+        uint32_t vm = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxL; ++j) {
+            const int Lj = j + 1;
+            vm |= (ins && Lj >= lmin && Lj <= lmax && p - j >= 0) ? 1u << j : 0u;
+        }
+        const int cnt = __builtin_popcount(vm);
+        const int off = wave_exclusive_sum(cnt, lane);
+        const int total = __builtin_amdgcn_readlane(off + cnt, 63);
+        if (p0 != p_lo) lds_wave_sync();                     // the last batch has read the queue
+        u64 hs = kHashSeed;
+        int k = off;
+#pragma unroll
+        for (int j = 0; j < kMaxL; ++j) {
+            hs = roll(hs, t[j]);
+            if ((vm >> j) & 1u) {
+                const u64 key = finish_key(hs, j + 1);
+                q_ent[k] = entry_of(key, a.fp_mask, p);
+                q_slot[k] = (uint32_t)home_slot(key, ns);
+                ++k;
+            }
+        }
+        lds_wave_sync();
+        for (int b = 0; b < total; b += 64 * kLanePairs)
+            ok = probe_batch(T, ns, q_ent, q_slot, b, total, lane) && ok;
+    }
+    return __ballot(!ok) == 0;
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Two waves per request (one workgroup).  Wave 1 inserts the appended
+// positions and records the indexed length; wave 0 answers the lookup (the
+// table query, and the direct match over the appended positions, which the
+// query need not find in the table) and, with kStep, finishes the decode
+// step.  Neither waits for the other's memory operations: the inserts'
+// round trips run beside the query's.  Wave 0 alone reads len and
+// indexed_len and hands them to wave 1 through LDS, so wave 1's write of
+// indexed_len follows wave 0's read of it, and wave 0's append of the new
+// length has no reader in the other wave.  A failed insert (probe bound)
+// leaves this call's answer exact (the direct match covers the new
+// positions) and marks the index stale for the next calls.
 template <bool kStep>
-__global__ void __launch_bounds__(64 * kWavesPerBlock)
+__global__ void __launch_bounds__(128)
 index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
                      const int64_t *__restrict__ row_off, const int32_t *__restrict__ len,
                      int32_t B, IndexArgs a,
-                     const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_bits,
+                     const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_slots,
                      u64 *__restrict__ tables, int32_t *__restrict__ indexed_len,
                      int32_t *__restrict__ match_len, int32_t *__restrict__ match_end,
                      int32_t *__restrict__ draft) {
@@ -155,56 +330,83 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
     (void)io_arg;
     const StepIO *iop = (const StepIO *)__builtin_amdgcn_kernarg_segment_ptr();
     const int lane = threadIdx.x & 63;
-    const int r = uni(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    const bool inserter = uni(threadIdx.x >> 6) == 1;
+    const int r = blockIdx.x;
     if (r >= B) return;
     // the rest of the step's inputs, in flight during the lookup
     int sin = 0;
     uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
-    if (kStep) {
+    if (kStep && !inserter) {
         const StepIO io0 = *iop;
         sin = load_step_input(r, lane, io0);
         if (io0.tele != nullptr)
             tin = io0.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
     }
-    const int32_t n0 = len[r];
-    const int n = n0 > 0 ? n0 : 0;
-    const int64_t ro = row_off[r];
-    const int il = indexed_len[r];
-    const int bits = table_bits[r];
-    u64 *__restrict__ T = tables + table_off[r];
-    const int32_t *__restrict__ h = hist + ro;
-    const int nL = a.l_max - a.l_min + 1;
-
-    bool exact = il < 0 || il > n;           // stale index: answered by a scan from now on
-    bool overfull = false;
-    u64 key = 0;
-    if (!exact) {
-        // The suffix s_j = h[n-1-j]: lane j < 16 loads it (one vector load,
-        // in flight with the appended positions' tokens below) and every lane
-        // reads them all.  (As uniform loads they became one scalar load per
-        // token, each waited for before the next.)
-        int32_t sv = 0;
-        if (n > 0) {
-            const int sp = n - 1 - (lane < kMaxL ? lane : 0);
-            sv = h[sp > 0 ? sp : 0];
+    __shared__ int s_meta[2];
+    int32_t n0 = 0;
+    int il = 0;
+    if (!inserter) {
+        n0 = len[r];
+        il = indexed_len[r];
+        if (lane == 0) {
+            s_meta[0] = n0;
+            s_meta[1] = il;
         }
+    }
+    const int64_t ro = row_off[r];
+    lds_barrier();
+    if (inserter) {
+        n0 = s_meta[0];
+        il = s_meta[1];
+    }
+    const int n = n0 > 0 ? n0 : 0;
+    const int32_t *__restrict__ h = hist + ro;
+    const bool stale = il < 0 || il > n;     // answered by a scan from now on
+    const int p_lo = il > 0 ? il - 1 : 0;    // positions appended since the last call
+    const int p_hi = n - 2;
+
+    // tokens ending at the first 64 appended positions (lane k: p_lo + k), for
+    // the inserts (wave 1) or the direct match (wave 0)
+    int32_t t[kMaxL];
+    {
+        const int p = p_lo + lane;
+        const bool ins = !stale && p <= p_hi;
+#pragma unroll
+        for (int j = 0; j < kMaxL; ++j) t[j] = (ins && j < a.l_max && p - j >= 0) ? h[p - j] : 0;
+    }
+
+    if (inserter) {
+        const uint32_t ns = (uint32_t)table_slots[r];
+        u64 *__restrict__ T = tables + table_off[r];
+        if (stale) {
+            if (lane == 0 && il > n) indexed_len[r] = -1;
+            return;
+        }
+        __shared__ u64 q_ent[kQueue];
+        __shared__ uint32_t q_slot[kQueue];
+        const bool ok = insert_positions(h, T, ns, p_lo, p_hi, a, lane, t, q_ent, q_slot);
+        if (lane == 0) indexed_len[r] = ok ? n : -1;
+        return;
+    }
+
+    const int nL = a.l_max - a.l_min + 1;
+    bool exact = stale;
+    u64 key = 0;
+    // The suffix s_j = h[n-1-j]: lane j < 16 loads it (one vector load) and
+    // every lane reads them all.  (As uniform loads they became one scalar
+    // load per token, each waited for before the next.)
+    int32_t sv = 0;
+    if (!stale && n > 0) {
+        const int sp = n - 1 - (lane < kMaxL ? lane : 0);
+        sv = h[sp > 0 ? sp : 0];
+    }
+    if (!exact) {
+        const uint32_t ns = (uint32_t)table_slots[r];
+        const u64 *__restrict__ T = tables + table_off[r];
         int32_t s[kMaxL];
 #pragma unroll
         for (int j = 0; j < kMaxL; ++j)
             s[j] = (j < a.l_max && n - 1 - j >= 0) ? __builtin_amdgcn_readlane(sv, j) : 0;
-
-        // ---- the positions appended since the last call: p_lo..p_hi --------
-        // Each is matched against the suffix directly (from its tokens in
-        // registers) and inserted into the table.  The table query does not
-        // wait for these inserts: its first probe is issued together with the
-        // inserts' compare-and-swaps, and the answer is the better of the
-        // table's (old positions, or a new one whose insert it happened to
-        // see) and the direct match over the new positions.
-        const int p_lo = il > 0 ? il - 1 : 0;
-        const int p_hi = n - 2;
-        const u64 cmask = ((u64)1 << bits) - 1;
-        bool ok = true;
-        u64 key_new = 0;
 
         // the query's key for length L = l_min + lane (ALU only)
         const int L = a.l_min + lane;
@@ -223,21 +425,26 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
             qk = finish_key(hl, L);
         }
         const uint32_t qfp = fingerprint(qk, a.fp_mask);
-        u64 qi = qk & cmask;
-        u64 v = 0;
+        uint32_t qi = (uint32_t)home_slot(qk, ns);
+        u64 v[kQWin];                        // a window of slots from the key's home slot
+#pragma unroll
+        for (int w = 0; w < kQWin; ++w)
+            v[w] = qlane ? __hip_atomic_load(T + wrap_add(qi, w, ns), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)
+                         : 0ull;
 
-        for (int p0 = p_lo, first = 1; p0 <= p_hi || first; p0 += 64, first = 0) {
+        // direct match of the suffix against the appended positions (from
+        // their tokens), in flight with the first probe
+        u64 key_new = 0;
+        for (int p0 = p_lo; p0 <= p_hi; p0 += 64) {
             const int p = p0 + lane;
             const bool ins = p <= p_hi;
-            // opaque copies of the length bounds: tests against them hoisted
-            // out of this loop were held (and spilled) through the whole kernel
-            int lmin = a.l_min, lmax = a.l_max;
-            asm volatile("" : "+s"(lmin), "+s"(lmax));
-            int32_t t[kMaxL];
+            int lmax = a.l_max;
+            asm volatile("" : "+s"(lmax));
+            if (p0 != p_lo) {
 #pragma unroll
-            for (int j = 0; j < kMaxL; ++j)
-                t[j] = (ins && j < lmax && p - j >= 0) ? h[p - j] : 0;
-            // direct match length at end p (capped at l_max)
+                for (int j = 0; j < kMaxL; ++j) t[j] = (ins && j < lmax && p - j >= 0) ? h[p - j] : 0;
+            }
             int Lp = 0;
             bool run = ins;
 #pragma unroll
@@ -245,30 +452,9 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
                 run = run && j < lmax && p - j >= 0 && t[j] == s[j];
                 Lp += run ? 1 : 0;
             }
-            if (Lp >= lmin) {
+            if (Lp >= a.l_min) {
                 const u64 k = ((u64)Lp << 31) | (uint32_t)p;
                 key_new = k > key_new ? k : key_new;
-            }
-            // every length's first compare-and-swap in flight at once ...
-            u64 ent[kMaxL], slot[kMaxL], old[kMaxL];
-            u64 hs = kHashSeed;
-#pragma unroll
-            for (int j = 0; j < kMaxL; ++j) {
-                hs = roll(hs, t[j]);
-                const int Lj = j + 1;
-                const u64 k = finish_key(hs, Lj);
-                ent[j] = entry_of(k, a.fp_mask, p);
-                slot[j] = k & cmask;
-                old[j] = (ins && Lj >= lmin && Lj <= lmax && p - j >= 0)
-                             ? atomicCAS(T + slot[j], 0ull, ent[j]) : 0ull;
-            }
-            // ... and, on the first pass, the query's first probe with them
-            if (first && qlane) v = __hip_atomic_load(T + qi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int j = 0; j < kMaxL; ++j) {
-                if (old[j] == 0) continue;                          // inserted (or no such length)
-                if ((old[j] >> 32) == (ent[j] >> 32)) atomicMax(T + slot[j], ent[j]);
-                else ok = insert_from(T, bits, ent[j], (slot[j] + 1) & cmask) && ok;
             }
         }
 #pragma unroll
@@ -276,20 +462,32 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
             const u64 o = __shfl_xor(key_new, off);
             key_new = o > key_new ? o : key_new;
         }
-        if (__ballot(!ok) != 0) exact = overfull = true;
 
-        // ---- table query (continued): lane k takes length L = l_min + k ------
+        // ---- table query: lane k takes length L = l_min + k ------------------
         int e = -1;
         bool collide = false;
         if (qlane) {
-            for (int probes = 0; probes < kMaxProbe; ++probes) {
+            for (int probes = 0; probes < kMaxProbe; probes += kQWin) {
                 if (probes > 0) {
-                    qi = (qi + 1) & cmask;
-                    v = __hip_atomic_load(T + qi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    qi = wrap_add(qi, kQWin, ns);
+#pragma unroll
+                    for (int w = 0; w < kQWin; ++w)
+                        v[w] = __hip_atomic_load(T + wrap_add(qi, w, ns), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (v == 0) break;                                   // no occurrence
-                if ((uint32_t)(v >> 32) == qfp) {
-                    const int pe = (int)(uint32_t)v - 1;
+                // the first slot of the window that ends the probe sequence
+                u64 vv = 0;
+                bool found = false;
+#pragma unroll
+                for (int w = kQWin - 1; w >= 0; --w) {
+                    const bool stop = v[w] == 0 || (uint32_t)(v[w] >> 32) == qfp;
+                    vv = stop ? v[w] : vv;
+                    found = found || stop;
+                }
+                if (!found) continue;
+                if (vv == 0) break;                                  // no occurrence
+                {
+                    const int pe = (int)(uint32_t)vv - 1;
                     bool same = pe >= L - 1 && pe <= n - 2;
                     if (same) {
                         int Lv = L;                                  // opaque: see the hash above
@@ -319,12 +517,7 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
             if ((u64)ld > (key >> 31)) exact = true;
         }
     }
-    if (exact) {
-        key = exact_scan(h, n, a, lane);
-        if (lane == 0 && (il > n || overfull)) indexed_len[r] = -1;
-    } else if (lane == 0) {
-        indexed_len[r] = n;
-    }
+    if (exact) key = exact_scan(h, n, a, lane);
 
     // ---- match and LZ draft ------------------------------------------------
     const int m = (int)(key >> 31);
@@ -359,7 +552,7 @@ clear_flags_kernel(int32_t *__restrict__ flags, int32_t n) {
 __global__ void __launch_bounds__(kBuildThreads)
 index_build_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__ row_off,
                    const int32_t *__restrict__ len, int32_t B, IndexArgs a,
-                   const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_bits,
+                   const int64_t *__restrict__ table_off, const int32_t *__restrict__ table_slots,
                    u64 *__restrict__ tables, int32_t *__restrict__ indexed_len, int32_t chunk,
                    int32_t cpr, int32_t *__restrict__ failed) {
     const int r = blockIdx.x / cpr;
@@ -369,7 +562,7 @@ index_build_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
     const int n = n0 > 0 ? n0 : 0;
     const int32_t *__restrict__ h = hist + row_off[r];
     u64 *__restrict__ T = tables + table_off[r];
-    const int bits = table_bits[r];
+    const uint32_t ns = (uint32_t)table_slots[r];
     bool ok = true;
     // positions 0..n-2, chunks of `chunk` positions per workgroup, strided by cpr
     for (int p0 = c * chunk; p0 <= n - 2; p0 += cpr * chunk) {
@@ -378,7 +571,7 @@ index_build_kernel(const int32_t *__restrict__ hist, const int64_t *__restrict__
             for (int j = 0; j < a.l_max && p - j >= 0; ++j) {
                 hs = roll(hs, h[p - j]);
                 const int L = j + 1;
-                if (L >= a.l_min) ok = insert_one(T, bits, finish_key(hs, L), a.fp_mask, p) && ok;
+                if (L >= a.l_min) ok = insert_one(T, ns, finish_key(hs, L), a.fp_mask, p) && ok;
             }
         }
     }
@@ -403,44 +596,44 @@ IndexArgs index_args(const lcd_params *p, int32_t fp_bits) {
     return a;
 }
 
-int table_bits_for(int32_t cap, int nL) {
-    const int64_t need = 4 * (int64_t)nL * (int64_t)(cap > 1 ? cap : 1);
-    int b = 4;
-    while (((int64_t)1 << b) < need) ++b;
-    return b;
+// Slots of a row's table: index_load per indexed length and token of its
+// capacity (at most 1/index_load of them ever taken), at least 16.
+int64_t table_slots_for(int32_t cap, int nL, int load) {
+    const int64_t need = (int64_t)load * nL * (int64_t)(cap > 1 ? cap : 1);
+    return need > 16 ? need : 16;
 }
 
 }  // namespace
 }  // namespace lcd
 
 extern "C" int64_t lookup_index_plan(const int32_t *cap, int32_t B, const lcd_params *p,
-                                     int64_t *table_off, int32_t *table_bits) {
+                                     int64_t *table_off, int32_t *table_slots) {
     using namespace lcd;
     if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
-    if (B > 0 && (!cap || !table_off || !table_bits)) return LCD_EINVAL;
+    if (B > 0 && (!cap || !table_off || !table_slots)) return LCD_EINVAL;
     const int nL = p->l_max - p->l_min + 1;
     int64_t off = 0;
     for (int32_t r = 0; r < B; ++r) {
         if (cap[r] < 0) return LCD_EINVAL;
-        const int b = table_bits_for(cap[r], nL);
-        if (b > 34) return LCD_EINVAL;
+        const int64_t ns = table_slots_for(cap[r], nL, p->index_load);
+        if (ns > INT32_MAX) return LCD_EINVAL;
         table_off[r] = off;
-        table_bits[r] = b;
-        off += (int64_t)1 << b;
+        table_slots[r] = (int32_t)ns;
+        off += ns;
     }
     return off * 8;
 }
 
 extern "C" int lookup_index_build(const int32_t *hist, const int64_t *row_off, const int32_t *len,
                                   int32_t B, const lcd_params *p, int32_t fp_bits,
-                                  const int64_t *table_off, const int32_t *table_bits,
+                                  const int64_t *table_off, const int32_t *table_slots,
                                   void *tables, size_t table_bytes, int32_t *indexed_len,
                                   int32_t *scratch, int32_t max_len, void *stream) {
     using namespace lcd;
     if (B < 0 || max_len < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK)
         return LCD_EINVAL;
     if (B == 0) return LCD_OK;
-    if (!hist || !row_off || !len || !table_off || !table_bits || !tables || !indexed_len ||
+    if (!hist || !row_off || !len || !table_off || !table_slots || !tables || !indexed_len ||
         !scratch || (reinterpret_cast<uintptr_t>(tables) & 7) != 0 || table_bytes < 8)
         return LCD_EINVAL;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -456,7 +649,7 @@ extern "C" int lookup_index_build(const int32_t *hist, const int64_t *row_off, c
     const int64_t per_row = ((int64_t)max_len + chunk - 1) / chunk;
     const int32_t cpr = (int32_t)(per_row < 1 ? 1 : (per_row > 4096 ? 4096 : per_row));
     hipLaunchKernelGGL(index_build_kernel, dim3((unsigned)((int64_t)B * cpr)), dim3(kBuildThreads),
-                       0, st, hist, row_off, len, B, a, table_off, table_bits,
+                       0, st, hist, row_off, len, B, a, table_off, table_slots,
                        static_cast<u64 *>(tables), indexed_len, chunk, cpr, scratch);
     hipLaunchKernelGGL(index_mark_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st,
                        scratch, B, indexed_len);
@@ -468,62 +661,62 @@ namespace {
 template <bool kStep>
 int index_launch(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
                  const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
-                 const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                 const int32_t *table_slots, void *tables, int32_t *indexed_len,
                  int32_t *match_len, int32_t *match_end, int32_t *draft, const StepIO &io,
                  void *stream, void *ev0, void *ev1) {
     const IndexArgs a = index_args(p, fp_bits);
-    const dim3 grid((unsigned)((B + kWavesPerBlock - 1) / kWavesPerBlock));
+    const dim3 grid((unsigned)B);
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (ev0 != nullptr || ev1 != nullptr)
-        hipExtLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(64 * kWavesPerBlock), 0u, st,
+        hipExtLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(128), 0u, st,
                               reinterpret_cast<hipEvent_t>(ev0), reinterpret_cast<hipEvent_t>(ev1),
-                              0u, io, hist, row_off, len, B, a, table_off, table_bits,
+                              0u, io, hist, row_off, len, B, a, table_off, table_slots,
                               static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft);
     else
-        hipLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(64 * kWavesPerBlock), 0, st, io,
-                           hist, row_off, len, B, a, table_off, table_bits,
+        hipLaunchKernelGGL(index_propose_kernel<kStep>, grid, dim3(128), 0, st, io,
+                           hist, row_off, len, B, a, table_off, table_slots,
                            static_cast<u64 *>(tables), indexed_len, match_len, match_end, draft);
     return hipGetLastError() == hipSuccess ? LCD_OK : LCD_EHIP;
 }
 
 bool index_args_ok(const void *hist, const void *row_off, const void *len, const void *table_off,
-                   const void *table_bits, const void *tables, const void *indexed_len,
+                   const void *table_slots, const void *tables, const void *indexed_len,
                    const void *match_len, const void *match_end, const void *draft) {
-    return hist && row_off && len && table_off && table_bits && tables && indexed_len && match_len &&
+    return hist && row_off && len && table_off && table_slots && tables && indexed_len && match_len &&
            match_end && draft && (reinterpret_cast<uintptr_t>(tables) & 7) == 0;
 }
 
 int index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
                   const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
-                  const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                  const int32_t *table_slots, void *tables, int32_t *indexed_len,
                   int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream,
                   void *ev0, void *ev1) {
     if (B < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
-    if (!index_args_ok(hist, row_off, len, table_off, table_bits, tables, indexed_len, match_len,
+    if (!index_args_ok(hist, row_off, len, table_off, table_slots, tables, indexed_len, match_len,
                        match_end, draft))
         return LCD_EINVAL;
-    return index_launch<false>(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+    return index_launch<false>(hist, row_off, len, B, p, fp_bits, table_off, table_slots, tables,
                                indexed_len, match_len, match_end, draft, StepIO{}, stream, ev0, ev1);
 }
 
 int index_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap, int32_t B,
                const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
-               const int32_t *table_bits, void *tables, int32_t *indexed_len,
+               const int32_t *table_slots, void *tables, int32_t *indexed_len,
                const int32_t *model_draft, const int32_t *target, lcd_sched_state *state,
                int32_t *match_len, int32_t *match_end, int32_t *draft, int32_t *block,
                int32_t *block_len, int32_t *accept, int32_t *long_next, uint32_t *tele,
                int32_t append, void *stream, void *ev0, void *ev1) {
     if (B < 0 || fp_bits < 0 || fp_bits > 31 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B == 0) return LCD_OK;
-    if (!index_args_ok(hist, row_off, len, table_off, table_bits, tables, indexed_len, match_len,
+    if (!index_args_ok(hist, row_off, len, table_off, table_slots, tables, indexed_len, match_len,
                        match_end, draft))
         return LCD_EINVAL;
     if (!model_draft || !target || !state || !block || !block_len || !accept) return LCD_EINVAL;
     if (append && !cap) return LCD_EINVAL;
     const StepIO io{hist, len, cap, model_draft, target, state, block, block_len, accept, long_next,
                     tele, fuse_args(p), sched_args(p), append ? 1 : 0};
-    return index_launch<true>(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+    return index_launch<true>(hist, row_off, len, B, p, fp_bits, table_off, table_slots, tables,
                               indexed_len, match_len, match_end, draft, io, stream, ev0, ev1);
 }
 }  // namespace
@@ -531,35 +724,35 @@ int index_step(int32_t *hist, const int64_t *row_off, int32_t *len, const int32_
 
 extern "C" int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len,
                                     int32_t B, const lcd_params *p, int32_t fp_bits,
-                                    const int64_t *table_off, const int32_t *table_bits,
+                                    const int64_t *table_off, const int32_t *table_slots,
                                     void *tables, int32_t *indexed_len, int32_t *match_len,
                                     int32_t *match_end, int32_t *draft, void *stream) {
-    return lcd::index_propose(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+    return lcd::index_propose(hist, row_off, len, B, p, fp_bits, table_off, table_slots, tables,
                               indexed_len, match_len, match_end, draft, stream, nullptr, nullptr);
 }
 
 extern "C" int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off,
                                           const int32_t *len, int32_t B, const lcd_params *p,
                                           int32_t fp_bits, const int64_t *table_off,
-                                          const int32_t *table_bits, void *tables,
+                                          const int32_t *table_slots, void *tables,
                                           int32_t *indexed_len, int32_t *match_len,
                                           int32_t *match_end, int32_t *draft, void *stream,
                                           void *ev_start, void *ev_stop) {
-    return lcd::index_propose(hist, row_off, len, B, p, fp_bits, table_off, table_bits, tables,
+    return lcd::index_propose(hist, row_off, len, B, p, fp_bits, table_off, table_slots, tables,
                               indexed_len, match_len, match_end, draft, stream, ev_start, ev_stop);
 }
 
 extern "C" int lookup_index_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len,
                                         const int32_t *cap, int32_t B, const lcd_params *p,
                                         int32_t fp_bits, const int64_t *table_off,
-                                        const int32_t *table_bits, void *tables,
+                                        const int32_t *table_slots, void *tables,
                                         int32_t *indexed_len, const int32_t *model_draft,
                                         const int32_t *target, lcd_sched_state *state,
                                         int32_t *match_len, int32_t *match_end, int32_t *draft,
                                         int32_t *block, int32_t *block_len, int32_t *accept,
                                         int32_t *long_next, uint32_t *telemetry, int32_t append,
                                         void *stream) {
-    return lcd::index_step(hist, row_off, len, cap, B, p, fp_bits, table_off, table_bits, tables,
+    return lcd::index_step(hist, row_off, len, cap, B, p, fp_bits, table_off, table_slots, tables,
                            indexed_len, model_draft, target, state, match_len, match_end, draft,
                            block, block_len, accept, long_next, telemetry, append, stream, nullptr,
                            nullptr);
@@ -567,12 +760,12 @@ extern "C" int lookup_index_decode_step(int32_t *hist, const int64_t *row_off, i
 
 extern "C" int lookup_index_decode_step_timed(
     int32_t *hist, const int64_t *row_off, int32_t *len, const int32_t *cap, int32_t B,
-    const lcd_params *p, int32_t fp_bits, const int64_t *table_off, const int32_t *table_bits,
+    const lcd_params *p, int32_t fp_bits, const int64_t *table_off, const int32_t *table_slots,
     void *tables, int32_t *indexed_len, const int32_t *model_draft, const int32_t *target,
     lcd_sched_state *state, int32_t *match_len, int32_t *match_end, int32_t *draft, int32_t *block,
     int32_t *block_len, int32_t *accept, int32_t *long_next, uint32_t *telemetry, int32_t append,
     void *stream, void *ev_start, void *ev_stop) {
-    return lcd::index_step(hist, row_off, len, cap, B, p, fp_bits, table_off, table_bits, tables,
+    return lcd::index_step(hist, row_off, len, cap, B, p, fp_bits, table_off, table_slots, tables,
                            indexed_len, model_draft, target, state, match_len, match_end, draft,
                            block, block_len, accept, long_next, telemetry, append, stream, ev_start,
                            ev_stop);

@@ -137,6 +137,7 @@ extern "C" void lcd_default_params(lcd_params *p) {
     p->scan_wgs = 0;
     p->scan_balance = 0;
     p->merge_polls = 0;
+    p->index_load = 3;
 }
 
 extern "C" int lcd_check_params(const lcd_params *p) {
@@ -149,7 +150,8 @@ extern "C" int lcd_check_params(const lcd_params *p) {
                     p->agree_n >= 0 && p->agree_n <= p->n_head && p->tail_min >= 1 &&
                     p->entry_steps >= 1 && p->sticky >= 0 && p->near_full_slack >= 0 &&
                     p->scan_wgs >= 0 && p->scan_wgs <= (1 << 20) &&
-                    (p->scan_balance == 0 || p->scan_balance == 1) && p->merge_polls >= -1;
+                    (p->scan_balance == 0 || p->scan_balance == 1) && p->merge_polls >= -1 &&
+                    p->index_load >= 2 && p->index_load <= 16;
     return ok ? LCD_OK : LCD_EINVAL;
 }
 

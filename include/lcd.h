@@ -79,6 +79,8 @@ extern "C" {
  *                 for has started and publishes without waiting -- so the
  *                 bound is a safety net; a request whose merge gave up
  *                 reports match_len = -1 (an error, not a lookup result).
+ *   index_load    incremental index (lookup_index_plan): table slots per
+ *                 indexed length and token of capacity, 2..16 (3).
  */
 typedef struct lcd_params {
     int32_t l_min, l_max, k_max;
@@ -88,6 +90,7 @@ typedef struct lcd_params {
     int32_t scan_wgs;
     int32_t scan_balance;
     int32_t merge_polls;
+    int32_t index_load;
 } lcd_params;
 
 /* Largest batch the token-balanced scan (scan_balance = 1) handles. */
@@ -364,34 +367,39 @@ int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, 
  * maintained incrementally; a full scan at every step of a long context
  * costs more and more).  Results are identical to lookup_propose's.
  *
- * Per request r the index is one hash table of 2^table_bits[r] 8-byte slots at
+ * Per request r the index is one hash table of table_slots[r] 8-byte slots at
  * table_off[r] (in slots) inside `tables`, keyed by every L-gram, L in
  * [l_min, l_max], that ends at a position p <= len-2, holding the latest such
  * p; indexed_len[r] (int32, device) is the history length the table covers.
- * Tables are sized for at most 1/4 occupancy when rows grow up to cap[r].
+ * Tables are sized exactly: p->index_load slots per indexed length and token
+ * of capacity cap[r] (at most 1/index_load of them ever taken), i.e.
+ * 8 x index_load x (l_max - l_min + 1) bytes per token of capacity -- 216 at
+ * the defaults, 144 with index_load = 2.  Denser tables make longer probe
+ * runs; a step reads a window of neighbouring slots per round trip (8 for an
+ * insert, 4 for a query), so only runs longer than a window cost another.
  * l_min and l_max must be the same at build and at every propose, and so must
  * fp_bits (fingerprint bits, 1..31, 0 = 31; fewer bits only make fingerprint
  * collisions, and with them the slow path, more frequent).
  */
 
 /*
- * lookup_index_plan -- host only.  Fills table_off[r] (slots) and
- * table_bits[r] for B rows of capacities cap[r] (host arrays) and returns the
- * total table bytes, or LCD_EINVAL (< 0).
+ * lookup_index_plan -- host only.  Fills table_off[r] and table_slots[r] (in
+ * slots) for B rows of capacities cap[r] (host arrays) and returns the total
+ * table bytes, or LCD_EINVAL (< 0; also for a table of 2^31 slots or more).
  */
 int64_t lookup_index_plan(const int32_t *cap, int32_t B, const lcd_params *p,
-                          int64_t *table_off, int32_t *table_bits);
+                          int64_t *table_off, int32_t *table_slots);
 
 /*
  * lookup_index_build -- clears the tables (table_bytes of them) and indexes
  * every position p <= len[r]-2 of every row; sets indexed_len[r] = max(len[r],
- * 0) (or -1 for a row whose table overflowed).  table_off / table_bits are the
+ * 0) (or -1 for a row whose table overflowed).  table_off / table_slots are the
  * plan's arrays, on the device; scratch is int32[B] of device memory;
  * max_len >= every len[r] (launch sizing).  Several launches on `stream`.
  */
 int lookup_index_build(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
                        const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
-                       const int32_t *table_bits, void *tables, size_t table_bytes,
+                       const int32_t *table_slots, void *tables, size_t table_bytes,
                        int32_t *indexed_len, int32_t *scratch, int32_t max_len, void *stream);
 
 /*
@@ -406,7 +414,7 @@ int lookup_index_build(const int32_t *hist, const int64_t *row_off, const int32_
  */
 int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
                          const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
-                         const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                         const int32_t *table_slots, void *tables, int32_t *indexed_len,
                          int32_t *match_len, int32_t *match_end, int32_t *draft, void *stream);
 
 /*
@@ -416,7 +424,7 @@ int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int3
  */
 int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, const int32_t *len,
                                int32_t B, const lcd_params *p, int32_t fp_bits,
-                               const int64_t *table_off, const int32_t *table_bits, void *tables,
+                               const int64_t *table_off, const int32_t *table_slots, void *tables,
                                int32_t *indexed_len, int32_t *match_len, int32_t *match_end,
                                int32_t *draft, void *stream, void *ev_start, void *ev_stop);
 
@@ -435,7 +443,7 @@ int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, cons
  *
  * hist, row_off, len, cap   as for lookup_decode_step; hist rows must be padded
  *                           (row_off[r] + cap[r] <= row_off[r+1]) when appending
- * p, fp_bits, table_off, table_bits, tables, indexed_len
+ * p, fp_bits, table_off, table_slots, tables, indexed_len
  *                           as for lookup_index_propose (the same index)
  * model_draft, target, state, outputs, telemetry, append
  *                           as for lookup_decode_step
@@ -445,7 +453,7 @@ int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, cons
  */
 int lookup_index_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len,
                              const int32_t *cap, int32_t B, const lcd_params *p, int32_t fp_bits,
-                             const int64_t *table_off, const int32_t *table_bits, void *tables,
+                             const int64_t *table_off, const int32_t *table_slots, void *tables,
                              int32_t *indexed_len, const int32_t *model_draft,
                              const int32_t *target, lcd_sched_state *state, int32_t *match_len,
                              int32_t *match_end, int32_t *draft, int32_t *block,
@@ -457,7 +465,7 @@ int lookup_index_decode_step(int32_t *hist, const int64_t *row_off, int32_t *len
 int lookup_index_decode_step_timed(int32_t *hist, const int64_t *row_off, int32_t *len,
                                    const int32_t *cap, int32_t B, const lcd_params *p,
                                    int32_t fp_bits, const int64_t *table_off,
-                                   const int32_t *table_bits, void *tables, int32_t *indexed_len,
+                                   const int32_t *table_slots, void *tables, int32_t *indexed_len,
                                    const int32_t *model_draft, const int32_t *target,
                                    lcd_sched_state *state, int32_t *match_len, int32_t *match_end,
                                    int32_t *draft, int32_t *block, int32_t *block_len,

@@ -34,7 +34,7 @@ def test_default_params_are_the_articles_values():
     assert (p.n_head, p.n_block) == (7, 15)
     assert (p.head_full, p.head_agree, p.agree_n, p.tail_min) == (8, 6, 2, 4)
     assert (p.entry_steps, p.sticky, p.near_full_slack, p.scan_wgs) == (2, 3, 1, 0)
-    assert p.scan_balance == 0 and p.merge_polls == 0
+    assert p.scan_balance == 0 and p.merge_polls == 0 and p.index_load == 3
     assert lcd.check_params(p)
 
 
@@ -44,6 +44,7 @@ def test_default_params_are_the_articles_values():
     dict(head_full=0), dict(head_agree=0), dict(agree_n=-1), dict(agree_n=8),
     dict(tail_min=0), dict(entry_steps=0), dict(sticky=-1), dict(near_full_slack=-1),
     dict(scan_wgs=-1), dict(scan_balance=2), dict(scan_balance=-1), dict(merge_polls=-2),
+    dict(index_load=1), dict(index_load=17),
 ])
 def test_param_ranges_rejected(bad):
     assert not lcd.check_params(lcd.default_params(**bad))
@@ -266,22 +267,28 @@ def test_rejection_accept_rejects_misuse_without_launching():
 
 
 def test_index_plan_sizes_tables_on_the_host():
-    """lookup_index_plan runs on the host: power-of-two tables of at least
-    4 x (number of lengths) x capacity slots, laid out back to back."""
+    """lookup_index_plan runs on the host: tables of exactly index_load slots
+    per indexed length and token of capacity (at least 16), laid out back to
+    back: 8 x 3 x 9 = 216 bytes per token of capacity at the defaults, 144
+    with index_load = 2."""
     L = lcd.load()
-    p = lcd.default_params()
     cap = np.array([0, 1, 100, 25_000, 262_144], np.int32)
-    off = np.zeros(5, np.int64)
+    for load in (3, 2, 4, 16):
+        p = lcd.default_params(index_load=load)
+        off = np.zeros(5, np.int64)
+        slots = np.zeros(5, np.int32)
+        total = L.lookup_index_plan(cap.ctypes.data_as(ctypes.c_void_p), 5, ctypes.byref(p),
+                                    off.ctypes.data_as(ctypes.c_void_p),
+                                    slots.ctypes.data_as(ctypes.c_void_p))
+        nL = p.l_max - p.l_min + 1
+        want = np.maximum(load * nL * np.maximum(cap.astype(np.int64), 1), 16)
+        assert slots.tolist() == want.tolist()
+        assert off.tolist() == np.concatenate([[0], np.cumsum(want)[:-1]]).tolist()
+        assert total == 8 * int(want.sum())
+        assert total / cap[2:].sum() < 8 * load * nL + 0.01        # bytes per token of capacity
     bits = np.zeros(5, np.int32)
-    total = L.lookup_index_plan(cap.ctypes.data_as(ctypes.c_void_p), 5, ctypes.byref(p),
-                                off.ctypes.data_as(ctypes.c_void_p),
-                                bits.ctypes.data_as(ctypes.c_void_p))
-    nL = p.l_max - p.l_min + 1
-    for r in range(5):
-        slots = 1 << int(bits[r])
-        assert slots >= 4 * nL * max(int(cap[r]), 1) and slots // 2 < max(16, 4 * nL * max(int(cap[r]), 1))
-    assert off.tolist() == np.concatenate([[0], np.cumsum(1 << bits.astype(np.int64))[:-1]]).tolist()
-    assert total == 8 * int((1 << bits.astype(np.int64)).sum())
+    off = np.zeros(5, np.int64)
+    p = lcd.default_params()
     # misuse
     bad_cap = np.array([5, -1], np.int32)
     assert L.lookup_index_plan(bad_cap.ctypes.data_as(ctypes.c_void_p), 2, ctypes.byref(p),

@@ -110,12 +110,25 @@ def test_forced_fingerprint_collisions(gpu, fp_bits):
     flat, ro, ln = wl.pack_csr(_stress_batch(seed=13, B=120))
     assert_index_parity(flat, ro, ln, fp_bits=fp_bits)
     assert_index_parity(flat, ro, ln, lcd.default_params(l_min=2, l_max=7), fp_bits=fp_bits)
+    assert_index_parity(flat, ro, ln, lcd.default_params(index_load=2), fp_bits=fp_bits)
 
 
-def test_growth_by_many_tokens_and_shrinking(gpu):
+@pytest.mark.parametrize("k", [3, 5])
+def test_densest_tables_full_size(gpu, k):
+    """index_load = 2 (144 bytes per token of capacity): the full-size
+    batches, with the tables half full at capacity."""
+    import context_lookup_drafting_amd as lcd
+    w = wl.make_config(k)
+    flat, ro, ln, cap = wl.pack_rows(w.hists)
+    assert_index_parity(flat, ro, ln, lcd.default_params(index_load=2), cap=ln.copy())
+
+
+@pytest.mark.parametrize("prm", [dict(), dict(l_min=1, l_max=16), dict(index_load=2)])
+def test_growth_by_many_tokens_and_shrinking(gpu, prm):
     """Histories grow by 0..3000 tokens between two proposes (the propose
-    indexes all of them); then some rows shrink below the index (answered by
-    scans, rows marked stale), and grow again."""
+    indexes all of them: many rounds of 64 positions, up to 1,024 queued
+    entries each with 16 lengths); then some rows shrink below the index
+    (answered by scans, rows marked stale), and grow again."""
     import torch
     import context_lookup_drafting_amd as lcd
     rng = np.random.Generator(np.random.PCG64(31))
@@ -128,7 +141,7 @@ def test_growth_by_many_tokens_and_shrinking(gpu):
             full[r][n - 40:] = full[r][50:90]
     flat, ro, ln_full, cap = wl.pack_rows(full)
     start = np.array([int(rng.integers(0, len(h) + 1)) for h in full], np.int32)
-    p = lcd.default_params()
+    p = lcd.default_params(**prm)
     dev = torch.device("cuda:0")
     idx = lcd.LookupIndex(cap, dev, p)
     h_d = torch.from_numpy(flat).to(dev)

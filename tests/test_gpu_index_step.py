@@ -125,20 +125,24 @@ def test_index_step_stale_rows_and_collisions(gpu):
         _index_single_step(hs, q, tgt, lg, append=True, fp_bits=bits)
 
 
-@pytest.mark.parametrize("k,steps,fp_bits", [(2, 200, 0), (3, 256, 0), (3, 48, 2)])
-def test_index_step_decode_simulation(gpu, k, steps, fp_bits):
+@pytest.mark.parametrize("k,steps,fp_bits,load", [(2, 200, 0, 3), (3, 256, 0, 3), (3, 48, 2, 3),
+                                                   (3, 128, 0, 2), (5, 24, 0, 2), (3, 64, 0, 4)])
+def test_index_step_decode_simulation(gpu, k, steps, fp_bits, load):
     """Whole decode loops with one lookup_index_decode_step per step: every
-    step, the final histories and the telemetry equal the oracle's."""
+    step, the final histories and the telemetry equal the oracle's; also with
+    the densest tables (index_load = 2: up to half the slots taken, so inserts
+    and lookups probe past other keys often)."""
+    import context_lookup_drafting_amd as lcd
     from simulate import simulate_gpu_index_fused, simulate_oracle
     w = wl.make_config(k)
-    g = simulate_gpu_index_fused(w, steps, fp_bits=fp_bits)
+    g = simulate_gpu_index_fused(w, steps, lcd.default_params(index_load=load), fp_bits=fp_bits)
     _compare_sims(g, simulate_oracle(w, steps))
-    if fp_bits == 0:
-        # the last call indexed the history it read; its own append comes after
-        # (a call that fell back to the exact scan on a fingerprint collision
-        # leaves indexed_len where it was, so this holds without collisions)
-        gap = g["lens"] - g["indexed_len"]
-        assert ((gap >= 1) & (gap <= 16)).all()
+    # the last call indexed the history it read (also when a fingerprint
+    # collision sent its lookup to the exact scan); its own append comes after
+    gap = g["lens"] - g["indexed_len"]
+    assert ((gap >= 1) & (gap <= 16)).all()
     for r in range(w.B):
-        em = g["emitted"][r]
-        assert em == w.truths[r][:len(em)].tolist()
+        # past the end of its truth stream the target repeats the last token
+        em, tr = g["emitted"][r], w.truths[r]
+        want = np.concatenate([tr, np.full(max(0, len(em) - len(tr)), tr[-1], tr.dtype)])
+        assert em == want[:len(em)].tolist()
