@@ -407,10 +407,13 @@ int lookup_index_build(const int32_t *hist, const int64_t *row_off, const int32_
  * draft), from the index.  First indexes the positions appended since the last
  * call (indexed_len[r]-1 .. len[r]-2; histories only grow between calls), then
  * looks up every suffix length at once.  A row whose history got shorter than
- * indexed_len[r], whose table overflowed, or whose answer a fingerprint
- * collision leaves in doubt is answered by an exact scan of its history (the
- * first two mark the row stale, indexed_len[r] = -1, until it is rebuilt).
- * One launch, one wave per request, no allocation.
+ * indexed_len[r], or whose answer a fingerprint collision leaves in doubt, is
+ * answered by an exact scan of its history.  A shorter history, and an insert
+ * that hit the probe bound (never at the planned load; this call's answer is
+ * still exact, the new positions being matched directly), mark the row stale,
+ * indexed_len[r] = -1: later calls answer it by scans until it is rebuilt.
+ * One launch, one workgroup of two waves per request (one inserts, one looks
+ * up), no allocation.
  */
 int lookup_index_propose(const int32_t *hist, const int64_t *row_off, const int32_t *len, int32_t B,
                          const lcd_params *p, int32_t fp_bits, const int64_t *table_off,
@@ -436,13 +439,18 @@ int lookup_index_propose_timed(const int32_t *hist, const int64_t *row_off, cons
  * what those four calls produce in that order, and what lookup_decode_step
  * produces.  (Article sections "第 1 步" to "第 3 步" and the paragraph on
  * losslessness; the forum thread's reply on keeping the lookup index
- * incremental.)  One launch, one wave per request: the wave that answers a
- * request's lookup also fuses, accepts, appends and schedules it.  The
- * appended tokens are indexed by the next call, as lookup_index_propose does
- * for any growth of the histories between calls.
+ * incremental.)  One launch, one workgroup of two waves per request: the wave
+ * that answers a request's lookup also fuses, accepts, appends and schedules
+ * it.  The appended tokens are indexed by the next call, as
+ * lookup_index_propose does for any growth of the histories between calls.
  *
- * hist, row_off, len, cap   as for lookup_decode_step; hist rows must be padded
+ * hist, row_off, cap        as for lookup_decode_step; hist rows must be padded
  *                           (row_off[r] + cap[r] <= row_off[r+1]) when appending
+ * len                       int32[B], updated in place when appending (len[r]
+ *                           + a + 1, len[r] read as max(len[r], 0); unchanged
+ *                           when the append failed): only request r's own
+ *                           workgroup reads or writes len[r], so no separate
+ *                           output array is needed
  * p, fp_bits, table_off, table_slots, tables, indexed_len
  *                           as for lookup_index_propose (the same index)
  * model_draft, target, state, outputs, telemetry, append
