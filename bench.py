@@ -743,47 +743,40 @@ def sampled_alg_bytes(sb, acc):
 
 
 def cpu_baseline_sampled(sb, work_seconds):
-    """The CPU oracle (as it is) over the same sampled batch, threads over
-    requests; bounded to about `work_seconds` of CPU time summed over threads."""
-    from concurrent.futures import ThreadPoolExecutor
+    """The CPU oracle (as it is) over whole sampled-verification steps of the
+    same batch (rejection_accept per request, no append), on native threads
+    over requests (oracle/lcd_oracle_bench.c) and on one thread; bounded to
+    about `work_seconds` of CPU time in all."""
     import oracle
     if not os.path.exists(os.path.join(ROOT, "oracle", "liblcd_oracle.so")):
         oracle.build()
-    cores, aff = host_threads()
-    chunks = [list(range(i, sb.B, cores)) for i in range(cores)]
-
-    def run_chunk(idx):
-        for r in idx:
-            s = slice(r, r + 1)
-            oracle.rejection_accept(sb.block[s], sb.block_len[s], sb.target_probs[s], sb.u_accept[s],
-                                    sb.u_sample[s], sb.model_mask[s],
-                                    None if sb.model_probs is None else sb.model_probs[s])
-        return len(idx)
-
+    threads, aff = host_threads()
     acc, _ = oracle.rejection_accept(sb.block, sb.block_len, sb.target_probs, sb.u_accept,
                                      sb.u_sample, sb.model_mask, sb.model_probs)
     rows, _ = sampled_draw_rows(sb, acc)
     probs = int(rows.sum()) * sb.V
-    batches = 0
-    cpu0 = time.process_time()
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=cores) as pool:
-        while True:
-            list(pool.map(run_chunk, chunks))
-            batches += 1
-            if time.process_time() - cpu0 >= work_seconds or time.perf_counter() - t0 > 120:
-                break
-    wall = time.perf_counter() - t0
+    args = (sb.block, sb.block_len, sb.target_probs, sb.u_accept, sb.u_sample, sb.model_mask,
+            sb.model_probs)
+    budget = max(1.0, 0.75 * work_seconds / threads)
+    steps, wall, cpu, _ = oracle.bench_rejection(*args, nthreads=threads, min_seconds=budget)
+    steps1, wall1, _, _ = oracle.bench_rejection(*args, nthreads=1,
+                                                 min_seconds=max(1.0, 0.25 * work_seconds))
+    rate, rate1 = steps * probs / wall, steps1 * probs / wall1
     return {
-        "value": round(batches * probs / wall, 1),
+        "value": round(rate, 1),
         "unit": "vocabulary probabilities/s",
-        "cores": cores,
+        "cores": threads,
         "kind": "oracle",
         "affinity_cpus": aff,
+        "os_cpu_count": os.cpu_count(),
         "cpu_model": cpu_model(),
-        "sample": (f"{batches} full sampled-verification steps of the {sb.B}-request batch "
-                   f"({probs} probabilities scanned each), threads over requests, "
-                   f"{wall:.1f} s wall"),
+        "value_1thread": round(rate1, 1),
+        "thread_scaling": round(rate / rate1, 2),
+        "sample": (f"{steps} full sampled-verification steps (rejection_accept per request, no "
+                   f"append) of the {sb.B}-request batch, {probs} probabilities scanned each, on "
+                   f"{threads} native threads over requests ({wall:.2f} s wall, {cpu:.1f} s CPU); "
+                   f"{steps1} steps on one thread ({wall1:.2f} s)"),
+        "requests_per_s": round(steps * sb.B / wall, 1),
     }
 
 

@@ -71,10 +71,12 @@ def lib():
         L.oracle_rejection_accept.argtypes = [P, P, P, P, P, i32, P, P, i32, P, P, P, P, P, P]
         L.oracle_bench_steps.argtypes = [P, P, P, i32, P, P, pp, i32, ctypes.c_double, i32, P, P,
                                          P, P]
+        L.oracle_bench_rejection.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, ctypes.c_double,
+                                             i32, P, P, P, P]
         for f in (L.oracle_lookup_propose, L.oracle_fuse_verify_block,
                   L.oracle_greedy_accept, L.oracle_lookup_schedule_step,
                   L.oracle_telemetry_update, L.oracle_telemetry_reduce,
-                  L.oracle_rejection_accept, L.oracle_bench_steps):
+                  L.oracle_rejection_accept, L.oracle_bench_steps, L.oracle_bench_rejection):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -250,4 +252,32 @@ def bench_steps(hist, row_off, lens, q, target, params=None, nthreads=1, min_sec
                                   ctypes.byref(wall), ctypes.byref(cpu), ctypes.byref(chk))
     if rc != 0:
         raise RuntimeError("oracle_bench_steps failed")
+    return steps.value, wall.value, cpu.value, chk.value
+
+
+def bench_rejection(block, block_len, target_probs, u_accept, u_sample, model_mask=None,
+                    model_probs=None, nthreads=1, min_seconds=1.0, max_steps=1 << 30):
+    """Times whole sampled-verification steps of the batch (the oracle's
+    rejection_accept on every request, no append) on `nthreads` native threads
+    (lcd_oracle_bench.c).  Returns (steps, wall seconds, process CPU seconds,
+    checksum: the sum of every accepted count and emitted token per step)."""
+    block = _c(block, np.int32).reshape(-1, DRAFT_STRIDE)
+    block_len = _c(block_len, np.int32)
+    B = len(block_len)
+    tp = _c(target_probs, np.float32).reshape(B, TARGET_STRIDE, -1)
+    V = tp.shape[2]
+    mp = None if model_probs is None else _c(model_probs, np.float32).reshape(B, Q_STRIDE, V)
+    mm = None if model_mask is None else _c(model_mask, np.uint32)
+    ua = _c(u_accept, np.float64).reshape(B, DRAFT_STRIDE)
+    us = _c(u_sample, np.uint64).reshape(B)
+    steps = ctypes.c_int64()
+    wall = ctypes.c_double()
+    cpu = ctypes.c_double()
+    chk = ctypes.c_int64()
+    rc = lib().oracle_bench_rejection(_ptr(block), _ptr(block_len), _ptr(mm), _ptr(tp), _ptr(mp), V,
+                                      _ptr(ua), _ptr(us), B, int(nthreads), float(min_seconds),
+                                      int(max_steps), ctypes.byref(steps), ctypes.byref(wall),
+                                      ctypes.byref(cpu), ctypes.byref(chk))
+    if rc != 0:
+        raise RuntimeError("oracle_bench_rejection failed")
     return steps.value, wall.value, cpu.value, chk.value

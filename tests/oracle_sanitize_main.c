@@ -45,6 +45,9 @@ int oracle_telemetry_reduce(const uint32_t *, const int32_t *, int32_t, int32_t,
 int oracle_bench_steps(const int32_t *, const int64_t *, const int32_t *, int32_t, const int32_t *,
                        const int32_t *, const oracle_params *, int32_t, double, int32_t, int64_t *,
                        double *, double *, int64_t *);
+int oracle_bench_rejection(const int32_t *, const int32_t *, const uint32_t *, const float *,
+                           const float *, int32_t, const double *, const uint64_t *, int32_t,
+                           int32_t, double, int32_t, int64_t *, double *, double *, int64_t *);
 
 static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
 static uint64_t next_u64(void) {                 /* splitmix64 */
@@ -197,6 +200,16 @@ static void rejection_round(void) {
     oracle_rejection_accept(blk, bl, mm, tp, mp, V, ua, us, B, acc, em, hist, ro, len, cap);
     mix(acc, sizeof(int32_t) * B); mix(em, sizeof(int32_t) * B * 16);
     mix(hist, sizeof(int32_t) * (size_t)total); mix(len, sizeof(int32_t) * B);
+    /* the benchmark harness over the same batch, with and without model rows */
+    int64_t steps, chk;
+    double wall, cpu;
+    const int with_model = uni(0, 1);
+    if (oracle_bench_rejection(blk, bl, with_model ? mm : NULL, tp, with_model ? mp : NULL, V, ua,
+                               us, B, uni(1, 3), 0.0, 2, &steps, &wall, &cpu, &chk) != 0) {
+        fprintf(stderr, "oracle_bench_rejection failed\n");
+        exit(3);
+    }
+    mix(&steps, sizeof steps); mix(&chk, sizeof chk);
     free(blk); free(bl); free(mm); free(tp); free(mp); free(ua); free(us); free(acc); free(em);
     free(len); free(cap); free(ro); free(hist);
 }

@@ -1,6 +1,7 @@
 """The CPU-baseline harness (oracle/lcd_oracle_bench.c) runs the oracle's own
 functions unchanged: its checksum over one step equals the same step computed
-through the oracle's batch calls, for any thread count."""
+through the oracle's batch calls, for any thread count -- for the greedy decode
+step and for sampled verification."""
 
 import numpy as np
 
@@ -30,3 +31,21 @@ def test_harness_runs_the_oracle_step_unchanged():
     steps, _, _, chk = oracle.bench_steps(flat, ro, ln, q, tgt, nthreads=4, min_seconds=60.0,
                                           max_steps=5)
     assert steps == 5 and chk == 5 * want
+
+
+def test_harness_runs_the_oracle_rejection_unchanged():
+    sb = wl.sampled_batch(B=24, V=2048)
+    for mm, mp in ((sb.model_mask, sb.model_probs), (None, None)):
+        acc, em = oracle.rejection_accept(sb.block, sb.block_len, sb.target_probs, sb.u_accept,
+                                          sb.u_sample, mm, mp)
+        want = int(acc.sum() + em.sum())
+        for nt in (1, 5):
+            steps, wall, cpu, chk = oracle.bench_rejection(sb.block, sb.block_len, sb.target_probs,
+                                                           sb.u_accept, sb.u_sample, mm, mp,
+                                                           nthreads=nt, min_seconds=0.0,
+                                                           max_steps=1)
+            assert steps == 1 and chk == want
+        steps, _, _, chk = oracle.bench_rejection(sb.block, sb.block_len, sb.target_probs,
+                                                  sb.u_accept, sb.u_sample, mm, mp, nthreads=3,
+                                                  min_seconds=60.0, max_steps=4)
+        assert steps == 4 and chk == 4 * want
