@@ -24,8 +24,8 @@ namespace lcd {
 // history: the append lies past every position a lookup of the row reads.
 // len_out receives the lengths after the step; the scan's decode step takes it
 // apart from the lengths its launch reads (a workgroup may read a row's length
-// after another has finished that row), the index step, whose one wave per
-// request reads and writes only its own row, may pass the same array.
+// after another has finished that row), the index step, whose one workgroup
+// per request reads and writes only its own row, may pass the same array.
 struct StepIO {
     int32_t *hist_w;
     int32_t *len_out;
@@ -63,9 +63,9 @@ __device__ __forceinline__ int load_step_input(int r, int lane, const StepIO &io
 // whole wave: lane k < 15 holds dk, the draft token of verify slot k (PAD past
 // k_max or without a match); sin holds the step inputs as load_step_input left
 // them and tin the request's telemetry counter of the lane (unused without
-// telemetry).
-__device__ __forceinline__ void finish_step(int r, int m, int dk, int sin, uint32_t tin, int lane,
-                                            int64_t ro, int32_t lr, int n, const StepIO &io) {
+// telemetry).  Returns the accepted count (-1 for a failed append).
+__device__ __forceinline__ int finish_step(int r, int m, int dk, int sin, uint32_t tin, int lane,
+                                           int64_t ro, int32_t lr, int n, const StepIO &io) {
     constexpr int kSt = LCD_Q_STRIDE + LCD_TARGET_STRIDE;      // sin lane of the state
     const int qk = sin;                                       // lanes 0..6: proposal
     const int tk = __shfl(sin, LCD_Q_STRIDE + (lane < LCD_TARGET_STRIDE ? lane : 0));
@@ -100,6 +100,7 @@ __device__ __forceinline__ void finish_step(int r, int m, int dk, int sin, uint3
     if (io.tele != nullptr && lane < LCD_TELE_HIST + 16)
         io.tele[(int64_t)r * LCD_TELE_WORDS + lane] =
             tin + telemetry_inc(lane, m, head, tail, was_long, ln != 0, acc);
+    return acc;
 }
 
 }  // namespace lcd

@@ -147,6 +147,16 @@ __device__ u64 exact_scan(const int32_t *__restrict__ h, int n, const IndexArgs 
 // time (the tables hold at least 16 slots, so a window never wraps twice).
 constexpr int kWin = 8;
 constexpr int kQWin = 4;
+// Each request's last tokens as the previous call left them, in the first
+// kCacheWords words of the tables buffer per request (the plan puts the
+// tables after them): word 0 is kCacheTag << 32 | the row length they end
+// at, words 1.. hold kCacheTok tokens, the last first.  A call whose row
+// length equals the cached one takes its suffix (and the tokens of the
+// positions appended since) from there, in the same round trip as the row's
+// length, instead of reading them from the history after it.
+constexpr int kCacheWords = 32;
+constexpr int kCacheTok = 48;
+constexpr uint32_t kCacheTag = 0x4C434443u;
 constexpr int kLanePairs = 4;          // queued entries one lane probes at once
 constexpr int kQueue = 64 * kMaxL;     // (position, length) entries per 64 positions
 
@@ -343,36 +353,60 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
             tin = io0.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
     }
     __shared__ int s_meta[2];
-    int32_t n0 = 0;
+    __shared__ int s_tok[kCacheTok];
+    const int64_t ro = row_off[r];
+    const int32_t *__restrict__ h = hist + ro;
+    u64 *__restrict__ cache = tables + (int64_t)r * kCacheWords;
+    int32_t *__restrict__ ctok = reinterpret_cast<int32_t *>(cache + 1);
+    // the row's last tokens, lane k < kCacheTok: h[n-1-k] (where n-1-k >= 0)
+    int32_t n0 = 0, tok = 0;
     int il = 0;
+    bool cached = false;
     if (!inserter) {
+        const u64 head = cache[0];
+        tok = lane < kCacheTok ? ctok[lane] : 0;
         n0 = len[r];
         il = indexed_len[r];
+        const int nn = n0 > 0 ? n0 : 0;
+        cached = (uint32_t)(head >> 32) == kCacheTag && (uint32_t)head == (uint32_t)nn;
+        if (!cached) {
+            const int sp = nn - 1 - (lane < kCacheTok ? lane : 0);
+            tok = nn > 0 && lane < kCacheTok ? h[sp > 0 ? sp : 0] : 0;
+        }
         if (lane == 0) {
             s_meta[0] = n0;
             s_meta[1] = il;
         }
+        if (lane < kCacheTok) s_tok[lane] = tok;
     }
-    const int64_t ro = row_off[r];
     lds_barrier();
     if (inserter) {
         n0 = s_meta[0];
         il = s_meta[1];
+        tok = lane < kCacheTok ? s_tok[lane] : 0;
     }
     const int n = n0 > 0 ? n0 : 0;
-    const int32_t *__restrict__ h = hist + ro;
     const bool stale = il < 0 || il > n;     // answered by a scan from now on
     const int p_lo = il > 0 ? il - 1 : 0;    // positions appended since the last call
     const int p_hi = n - 2;
 
     // tokens ending at the first 64 appended positions (lane k: p_lo + k), for
-    // the inserts (wave 1) or the direct match (wave 0)
+    // the inserts (wave 1) or the direct match (wave 0): h[p-j] is the token
+    // (n-1-p)+j from the end, among the last tokens when p_lo >= n-33
     int32_t t[kMaxL];
     {
         const int p = p_lo + lane;
         const bool ins = !stale && p <= p_hi;
+        if (p_lo >= n - (kCacheTok - kMaxL + 1)) {
 #pragma unroll
-        for (int j = 0; j < kMaxL; ++j) t[j] = (ins && j < a.l_max && p - j >= 0) ? h[p - j] : 0;
+            for (int j = 0; j < kMaxL; ++j) {
+                const int v = __shfl(tok, (n - 1 - p + j) & 63);
+                t[j] = (ins && j < a.l_max && p - j >= 0) ? v : 0;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMaxL; ++j) t[j] = (ins && j < a.l_max && p - j >= 0) ? h[p - j] : 0;
+        }
     }
 
     if (inserter) {
@@ -392,14 +426,8 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
     const int nL = a.l_max - a.l_min + 1;
     bool exact = stale;
     u64 key = 0;
-    // The suffix s_j = h[n-1-j]: lane j < 16 loads it (one vector load) and
-    // every lane reads them all.  (As uniform loads they became one scalar
-    // load per token, each waited for before the next.)
-    int32_t sv = 0;
-    if (!stale && n > 0) {
-        const int sp = n - 1 - (lane < kMaxL ? lane : 0);
-        sv = h[sp > 0 ? sp : 0];
-    }
+    // The suffix s_j = h[n-1-j] is in lane j of tok; every lane reads them all.
+    const int32_t sv = tok;
     if (!exact) {
         const uint32_t ns = (uint32_t)table_slots[r];
         const u64 *__restrict__ T = tables + table_off[r];
@@ -532,7 +560,22 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
         match_len[r] = m;
         match_end[r] = e;
     }
-    if (kStep) finish_step(r, m, d, sin, tin, lane, ro, n0, n, *iop);
+    // the row's last tokens after this call, for the next one: with an append,
+    // the emitted target tokens 0..acc then the tokens before them
+    int n_next = n, tok_next = tok;
+    if (kStep) {
+        const int acc = finish_step(r, m, d, sin, tin, lane, ro, n0, n, *iop);
+        if (iop->append && acc >= 0) {
+            n_next = n + acc + 1;
+            const int tk = __shfl(sin, LCD_Q_STRIDE + (lane <= acc ? acc - lane : 0));
+            const int old = __shfl(tok, (lane - acc - 1) & 63);
+            tok_next = lane <= acc ? tk : old;
+        }
+    }
+    if (n_next != n || !cached) {
+        if (lane < kCacheTok) ctok[lane] = tok_next;
+        if (lane == 0) cache[0] = ((u64)kCacheTag << 32) | (uint32_t)n_next;
+    }
 }
 
 // Build: clear the tables, then insert every position p <= n-2 of every row.
@@ -612,7 +655,7 @@ extern "C" int64_t lookup_index_plan(const int32_t *cap, int32_t B, const lcd_pa
     if (B < 0 || lcd_check_params(p) != LCD_OK) return LCD_EINVAL;
     if (B > 0 && (!cap || !table_off || !table_slots)) return LCD_EINVAL;
     const int nL = p->l_max - p->l_min + 1;
-    int64_t off = 0;
+    int64_t off = (int64_t)B * kCacheWords;            // the requests' token caches come first
     for (int32_t r = 0; r < B; ++r) {
         if (cap[r] < 0) return LCD_EINVAL;
         const int64_t ns = table_slots_for(cap[r], nL, p->index_load);

@@ -367,7 +367,12 @@ int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, 
  * maintained incrementally; a full scan at every step of a long context
  * costs more and more).  Results are identical to lookup_propose's.
  *
- * Per request r the index is one hash table of table_slots[r] 8-byte slots at
+ * `tables` begins with 256 bytes per request holding the request's last 48
+ * tokens as the last call left them and the row length they end at: a cache
+ * the calls keep for themselves (a call whose row length equals the cached
+ * one reads its suffix from there, in the same round trip as the length;
+ * lookup_index_build clears it).  After those, per request r the index is one
+ * hash table of table_slots[r] 8-byte slots at
  * table_off[r] (in slots) inside `tables`, keyed by every L-gram, L in
  * [l_min, l_max], that ends at a position p <= len-2, holding the latest such
  * p; indexed_len[r] (int32, device) is the history length the table covers.
@@ -385,7 +390,8 @@ int lookup_telemetry_reduce(const uint32_t *telemetry, const int32_t *class_id, 
 /*
  * lookup_index_plan -- host only.  Fills table_off[r] and table_slots[r] (in
  * slots) for B rows of capacities cap[r] (host arrays) and returns the total
- * table bytes, or LCD_EINVAL (< 0; also for a table of 2^31 slots or more).
+ * bytes of `tables` (256 x B bytes of token cache, then the tables), or
+ * LCD_EINVAL (< 0; also for a table of 2^31 slots or more).
  */
 int64_t lookup_index_plan(const int32_t *cap, int32_t B, const lcd_params *p,
                           int64_t *table_off, int32_t *table_slots);

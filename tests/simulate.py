@@ -126,10 +126,15 @@ def simulate_gpu_fused(w: Workload, steps: int, params=None, record: bool = True
 
 
 def simulate_gpu_index_fused(w: Workload, steps: int, params=None, record: bool = True,
-                             device="cuda:0", fp_bits: int = 0):
+                             device="cuda:0", fp_bits: int = 0, separate_every: int = 0,
+                             rebuild_at=()):
     """The decode loop through lookup_index_decode_step: one kernel per step,
     the lookup answered from the index (built once from the prompts) and the
-    step's appended tokens indexed by the next call."""
+    step's appended tokens indexed by the next call.  With separate_every = k,
+    every k-th step goes through the four entry points instead (the index
+    propose, then fusion, the appending greedy accept and the scheduler), so
+    the next call finds histories grown behind its back; before each step in
+    rebuild_at the index is built again from the current histories."""
     import torch
     import context_lookup_drafting_amd as lcd
     params = params or lcd.default_params()
@@ -151,8 +156,18 @@ def simulate_gpu_index_fused(w: Workload, steps: int, params=None, record: bool 
     for step in range(steps):
         q, tgt = w.step_inputs(pos, step)
         long_used = state[:, 0].clone()
-        idx.decode_step(h_d, ro_d, len_d, cap_d, t(q), t(tgt), state, m, e, d, block, bl, acc,
-                        long_next, True, telemetry=tele)
+        if step in rebuild_at:
+            idx.build(h_d, ro_d, len_d, max_len)
+        if separate_every and step % separate_every == separate_every - 1:
+            q_d, tgt_d = t(q), t(tgt)
+            idx.propose(h_d, ro_d, len_d, m, e, d)
+            lcd.fuse_verify_block(d, m, q_d, long_used, block, bl, params)
+            lcd.greedy_accept(block, bl, tgt_d, acc, hist=h_d, row_off=ro_d, lens=len_d, cap=cap_d)
+            lcd.lookup_schedule_step(state, m, acc, bl, long_next, params)
+            lcd.telemetry_update(tele, m, d, q_d, long_used, bl, acc, long_next, params)
+        else:
+            idx.decode_step(h_d, ro_d, len_d, cap_d, t(q), t(tgt), state, m, e, d, block, bl, acc,
+                            long_next, True, telemetry=tele)
         acc_h = acc.cpu().numpy()
         for r in range(B):
             if acc_h[r] >= 0:

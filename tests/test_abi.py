@@ -269,8 +269,8 @@ def test_rejection_accept_rejects_misuse_without_launching():
 def test_index_plan_sizes_tables_on_the_host():
     """lookup_index_plan runs on the host: tables of exactly index_load slots
     per indexed length and token of capacity (at least 16), laid out back to
-    back: 8 x 3 x 9 = 216 bytes per token of capacity at the defaults, 144
-    with index_load = 2."""
+    back after 256 bytes of token cache per request: 8 x 3 x 9 = 216 bytes per
+    token of capacity at the defaults, 144 with index_load = 2."""
     L = lcd.load()
     cap = np.array([0, 1, 100, 25_000, 262_144], np.int32)
     for load in (3, 2, 4, 16):
@@ -283,9 +283,11 @@ def test_index_plan_sizes_tables_on_the_host():
         nL = p.l_max - p.l_min + 1
         want = np.maximum(load * nL * np.maximum(cap.astype(np.int64), 1), 16)
         assert slots.tolist() == want.tolist()
-        assert off.tolist() == np.concatenate([[0], np.cumsum(want)[:-1]]).tolist()
-        assert total == 8 * int(want.sum())
-        assert total / cap[2:].sum() < 8 * load * nL + 0.01        # bytes per token of capacity
+        # 32 words of token cache per request first, then the tables
+        assert off.tolist() == (32 * 5 + np.concatenate([[0], np.cumsum(want)[:-1]])).tolist()
+        assert total == 8 * (32 * 5 + int(want.sum()))
+        # bytes per token of capacity, past the token caches and the 16-slot minimum
+        assert 8 * int(want[2:].sum()) == 8 * load * nL * int(cap[2:].sum())
     bits = np.zeros(5, np.int32)
     off = np.zeros(5, np.int64)
     p = lcd.default_params()

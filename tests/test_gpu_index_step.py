@@ -146,3 +146,17 @@ def test_index_step_decode_simulation(gpu, k, steps, fp_bits, load):
         em, tr = g["emitted"][r], w.truths[r]
         want = np.concatenate([tr, np.full(max(0, len(em) - len(tr)), tr[-1], tr.dtype)])
         assert em == want[:len(em)].tolist()
+
+
+@pytest.mark.parametrize("k,steps", [(2, 60), (3, 48)])
+def test_index_step_token_cache_across_outside_appends_and_rebuilds(gpu, k, steps):
+    """The index step keeps each request's last tokens for the next call; a
+    call whose rows grew through other entry points in between (every third
+    step goes through the four entry points), or after a rebuild, reads them
+    from the history again.  Every step equals the oracle's."""
+    import context_lookup_drafting_amd as lcd
+    from simulate import simulate_gpu_index_fused, simulate_oracle
+    w = wl.make_config(k)
+    g = simulate_gpu_index_fused(w, steps, lcd.default_params(), separate_every=3,
+                                 rebuild_at=(steps // 2, steps // 2 + 1))
+    _compare_sims(g, simulate_oracle(w, steps))
