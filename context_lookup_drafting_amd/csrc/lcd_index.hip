@@ -214,7 +214,7 @@ __device__ bool probe_batch(u64 *__restrict__ T, uint32_t ns, const u64 *q_ent,
             for (int w = 0; w < kWin; ++w)
                 win[c][w] = (act >> c) & 1u
                                 ? __hip_atomic_load(T + wrap_add(st[c], w, ns), __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                                    __HIP_MEMORY_SCOPE_WORKGROUP)
                                 : 0ull;
         uint32_t cas = 0, mx = 0;
 #pragma unroll
@@ -314,6 +314,16 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Memory scope.  Within a launch a request's table is touched only by its own
+// workgroup, so the table reads of both waves are workgroup-scope loads (they
+// may be served by the CU's cache): a read may miss an insert made by the
+// other wave, or by another lane, earlier in the same launch, never one made
+// by an earlier launch (the caches hold nothing from before the launch).  That
+// is enough: a slot only ever goes from empty to a fingerprint, and then only
+// to later positions; an insert that relied on a stale empty slot loses its
+// compare-and-swap and goes on; and a query that stops at a stale empty slot
+// misses only this launch's positions, which the direct match covers.
+//
 // Two waves per request (one workgroup).  Wave 1 inserts the appended
 // positions and records the indexed length; wave 0 answers the lookup (the
 // table query, and the direct match over the appended positions, which the
@@ -458,7 +468,7 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
 #pragma unroll
         for (int w = 0; w < kQWin; ++w)
             v[w] = qlane ? __hip_atomic_load(T + wrap_add(qi, w, ns), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)
+                                             __HIP_MEMORY_SCOPE_WORKGROUP)
                          : 0ull;
 
         // direct match of the suffix against the appended positions (from
@@ -501,7 +511,7 @@ index_propose_kernel(StepIO io_arg, const int32_t *__restrict__ hist,
 #pragma unroll
                     for (int w = 0; w < kQWin; ++w)
                         v[w] = __hip_atomic_load(T + wrap_add(qi, w, ns), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 // the first slot of the window that ends the probe sequence
                 u64 vv = 0;
