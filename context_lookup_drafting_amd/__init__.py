@@ -521,7 +521,8 @@ class LookupIndex:
             raise LCDError("lookup_index_plan", nbytes)
         self.device = torch.device(device)
         self.table_bytes = max(nbytes, 8)
-        self.tables = torch.empty(self.table_bytes // 8, dtype=torch.int64, device=self.device)
+        # zeroed: empty tables and no cached tokens until build() indexes the rows
+        self.tables = torch.zeros(self.table_bytes // 8, dtype=torch.int64, device=self.device)
         self.table_off = torch.from_numpy(off[:self.B].copy()).to(self.device)
         self.table_slots = torch.from_numpy(slots[:self.B].copy()).to(self.device)
         self.indexed_len = torch.zeros(self.B, dtype=torch.int32, device=self.device)

@@ -325,7 +325,7 @@ def test_index_entry_points_reject_misuse_without_launching():
     assert L.lookup_index_propose(None, None, None, 0, pp, 0, None, None, None, None, None, None,
                                   None, s) == lcd.LCD_OK
     # the whole step through the index: the propose checks plus the step's own
-    # (hist, row_off, len, cap, B, p, fp_bits, table_off, table_bits, tables,
+    # (hist, row_off, len, cap, B, p, fp_bits, table_off, table_slots, tables,
     #  indexed_len, model_draft, target, state, match_len, match_end, draft,
     #  block, block_len, accept, long_next, telemetry, append, stream)
     step = lambda *a: L.lookup_index_decode_step(*a)
