@@ -160,3 +160,28 @@ def test_index_step_token_cache_across_outside_appends_and_rebuilds(gpu, k, step
     g = simulate_gpu_index_fused(w, steps, lcd.default_params(), separate_every=3,
                                  rebuild_at=(steps // 2, steps // 2 + 1))
     _compare_sims(g, simulate_oracle(w, steps))
+
+
+def test_index_step_short_rows_grow_through_the_token_cache(gpu):
+    """Rows of 0-60 tokens over a 3-token alphabet grow step by step past the
+    48 cached tokens (periodic truths, so blocks are accepted and long blocks
+    entered): every step of the one-kernel index decode, also every other step
+    through the four entry points, equals the oracle's."""
+    import context_lookup_drafting_amd as lcd
+    from simulate import simulate_gpu_index_fused, simulate_oracle
+    rng = np.random.Generator(np.random.PCG64(77))
+    B, steps = 48, 40
+    hists, truths = [], []
+    for r in range(B):
+        n = int(rng.integers(0, 61))
+        period = int(rng.integers(1, 5))
+        pat = rng.integers(0, 3, period).astype(np.int32)
+        h = rng.integers(0, 3, n).astype(np.int32)
+        if r % 2 and n:
+            h = np.resize(pat, n).astype(np.int32)
+        hists.append(h)
+        truths.append(np.resize(pat, 16 * steps + 16).astype(np.int32))
+    w = wl.Workload("short_ragged", 77, 3, hists, truths, steps)
+    for every in (0, 2):
+        g = simulate_gpu_index_fused(w, steps, lcd.default_params(), separate_every=every)
+        _compare_sims(g, simulate_oracle(w, steps))
