@@ -254,7 +254,7 @@ def work_spread(lcd, w, max_len, p):
 
 def host_threads():
     """(threads for the CPU baseline, CPUs this process may run on): the
-    affinity set, at most 16 -- a GPU machine's CPU share per GPU."""
+    affinity set, at most 16 -- one GPU's share of a multi-GPU host's CPUs."""
     try:
         aff = len(os.sched_getaffinity(0))
     except AttributeError:
