@@ -84,12 +84,10 @@ constexpr int kWavesLarge = 16;
 constexpr int kNumCUs = 256;
 // 4-wave workgroups of the scan resident on one CU at once, as compiled (106
 // SGPRs and at most 52 VGPRs per wave: 7 waves per SIMD; lookup_scan_occupancy
-// reports the runtime's figure and the GPU tests hold it to this).  Automatic
-// grids stay within 7 x 256 workgroups: a workgroup beyond them is dispatched
-// only when an earlier one ends, and on ragged batches that put a long row's
-// chunks 12 us behind (256 rows of 1k-262k tokens: 24.2 us at 2048 workgroups,
-// 19.9-20.7 us at 1792).  Forcing 8 waves per SIMD with a launch bound cost
-// more in spilled registers than it gained.
+// reports the runtime's figure and the GPU tests hold it to this).  A
+// workgroup beyond 7 x 256 is dispatched only when an earlier one ends.
+// Forcing 8 waves per SIMD with a launch bound cost more in spilled registers
+// than it gained.
 constexpr int kResidentSmall = 7;
 constexpr int kTileTok = 256;   // chunk lengths are multiples of this
 constexpr int64_t kMaxChunk = int64_t(1) << 28;   // a chunk's descriptor range stays below 2^32 bytes
@@ -113,6 +111,7 @@ constexpr u64 kEndMask = (1ull << kLenShift) - 1;
 constexpr int kMaxCpr = 64;                               // workgroups per request, at most
 constexpr int kSlotWords = 16;
 constexpr int kReqWords = 2 + kMaxCpr * kSlotWords;
+constexpr int kPollBatch = 8;                             // slot words per lane loaded at once
 constexpr u64 kTagLimit = (1ull << 28) - 1;               // epochs 0 .. kTagLimit - 1
 constexpr int kPollMax = 1 << 20;                         // gathering polls, at most (default)
 constexpr int kBufferWord3 = 0x00020000;                  // gfx9 buffer descriptor, dword 3
@@ -751,11 +750,25 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
                     ok = (v0 >> (is_key ? 36 : 32)) == tag;
                 }
             } else {
-                for (int u = lane; u < nu; u += 64) {
-                    if (u / kSlotWords != c0) {
-                        const u64 v = __hip_atomic_load(slots + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        s_units[u] = v;
-                        ok = ok && ((v >> (((u & (kSlotWords - 1)) == kSlotWords - 1) ? 36 : 32)) == tag);
+                // the loads of a batch of up to 32 slots all in flight before
+                // the first is used (a loop that consumed each word before
+                // loading the next waited one round trip per 64 words)
+                for (int k0 = 0; 64 * k0 < nu; k0 += kPollBatch) {
+                    u64 pv[kPollBatch];
+#pragma unroll
+                    for (int k = 0; k < kPollBatch; ++k) {
+                        const int u = lane + 64 * (k0 + k);
+                        pv[k] = 0;
+                        if (64 * (k0 + k) < nu && u < nu && u / kSlotWords != c0)
+                            pv[k] = __hip_atomic_load(slots + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int k = 0; k < kPollBatch; ++k) {
+                        const int u = lane + 64 * (k0 + k);
+                        if (64 * (k0 + k) < nu && u < nu && u / kSlotWords != c0) {
+                            s_units[u] = pv[k];
+                            ok = ok && ((pv[k] >> (is_key ? 36 : 32)) == tag);
+                        }
                     }
                 }
             }
@@ -808,23 +821,25 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
 }
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
-// batch's size bound B x max_len, between 256 and 2048 per launch (1 to 8 per
-// CU), with chunks of at least 2048 and at most 32768 tokens of the longest row,
-// and no more workgroups than are resident at once (kResidentSmall per CU).
+// batch's size bound B x max_len, at least 256 per launch, with chunks of at
+// least 2048 and at most 32768 tokens of the longest row.  Large batches take
+// several dispatch rounds: with equal chunks the long rows' chunks are the
+// critical path, so they are kept short, and the workgroups past a short row's
+// end leave at once.  Measured on 256 rows of 1k-262k tokens: 16.8 us against
+// 19.4 us with the grid held to one round (1,792 workgroups); on 256 x 262k,
+// 53.1 against 57.5 us; on 200 x 150k and 256 x 53.6k, even.
 int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
     int64_t cpr;
     if (scan_wgs > 0) {
         cpr = scan_wgs / B;
     } else {
         int64_t wgs = (int64_t)B * max_len / 12000;
-        wgs = wgs < 256 ? 256 : (wgs > 2048 ? 2048 : wgs);
+        wgs = wgs < 256 ? 256 : wgs;
         cpr = (wgs + B / 2) / B;
         const int64_t most = ((int64_t)max_len + 2047) / 2048;
         const int64_t least = ((int64_t)max_len + 32767) / 32768;
         if (cpr > most) cpr = most;
         if (cpr < least) cpr = least;
-        const int64_t fit = (int64_t)kResidentSmall * kNumCUs / (B > 0 ? B : 1);
-        if (cpr > fit) cpr = fit;                // one dispatch round
     }
     if (cpr < 1) cpr = 1;
     if (cpr > kMaxCpr) cpr = kMaxCpr;

@@ -381,17 +381,24 @@ def test_launch_shape_query():
     assert lcd.launch_shape(1100, 100, pb, big) == lcd.launch_shape(1100, 100, p)
 
 
-def test_automatic_grids_fit_one_dispatch_round():
-    """Automatic grids of 4-wave workgroups stay within the 7 x 256 that are
-    resident at once (the GPU tests check the 7 against the runtime): 256 rows
-    of up to 262k tokens get 7 chunks per row, not 8; explicit scan_wgs and
-    one-chunk-per-row batches are left alone."""
+def test_automatic_grids_of_large_batches():
+    """Batches past the 16-wave shapes get about one 4-wave workgroup per 12k
+    tokens of B x max_len (chunks of ~12k tokens of the longest row, between
+    2048 and 32768), even where that takes several dispatch rounds of the 7 x
+    256 resident workgroups; the token-balanced default stays within one
+    round; explicit scan_wgs and one-chunk-per-row batches are left alone."""
     p = lcd.default_params()
-    assert lcd.launch_shape(256, 262_144, p)[0] == 1792
-    for B, n in ((200, 262_144), (300, 150_000), (512, 100_000), (1024, 1 << 20)):
-        assert lcd.launch_shape(B, n, p)[0] <= max(1792, B)
+    wgs, T = lcd.launch_shape(256, 262_144, p)
+    assert (wgs, T) == (22 * 256, 12_032)                 # 262,143 ends in 22 chunks
+    assert lcd.launch_shape(256, 53_600, p) == (1024, 13_568)
+    assert lcd.launch_shape(200, 150_000, p) == (2600, 11_776)
+    for B, n in ((200, 262_144), (300, 150_000), (512, 100_000)):
+        wgs, T = lcd.launch_shape(B, n, p)
+        assert wgs % B == 0 and T % 256 == 0 and abs(T - 12_000) <= 1_000, (B, n, T)
+    assert lcd.launch_shape(1024, 1 << 20, p) == (64 * 1024, 16_384)   # 64 chunks per row at most
     assert lcd.launch_shape(256, 262_144, lcd.default_params(scan_wgs=2048))[0] == 2048
-    assert lcd.launch_shape(2000, 262_144, p)[0] == 2000
+    assert lcd.launch_shape(2000, 262_144, p)[0] == 2000 * 22
+    assert lcd.launch_shape(2000, 1000, p) == (2000, 1024)
     pb = lcd.default_params(scan_balance=1)
     assert lcd.launch_shape(512, 4096, pb, np.full(512, 4096, np.int32))[0] == 1792
     with pytest.raises(lcd.LCDError):

@@ -241,15 +241,18 @@ def test_launch_shapes_do_not_change_results(gpu, wgs):
 
 
 def test_automatic_grid_is_resident(gpu):
-    """The automatic launch rule assumes 7 resident 4-wave workgroups per CU on
-    a 256-CU part; the runtime's occupancy for the compiled kernels must allow
-    at least that (a kernel change that costs registers would break it)."""
+    """The token-balanced launch rule assumes 7 resident 4-wave workgroups per
+    CU on a 256-CU part; the runtime's occupancy for the compiled kernels must
+    allow at least that (a kernel change that costs registers would break it)."""
+    import numpy as np
     import torch
     lcd = _lcd()
     assert torch.cuda.get_device_properties(0).multi_processor_count == 256
     assert lcd.scan_occupancy(4) >= 7
     assert lcd.scan_occupancy(16) >= 1
-    assert lcd.launch_shape(256, 262_144)[0] <= lcd.scan_occupancy(4) * 256
+    pb = lcd.default_params(scan_balance=1)
+    lens = np.full(512, 262_144, np.int32)
+    assert lcd.launch_shape(512, 262_144, pb, lens)[0] == 7 * 256 <= lcd.scan_occupancy(4) * 256
 
 
 def test_match_across_workgroup_boundaries(gpu):
