@@ -151,9 +151,6 @@ __host__ __device__ inline int32_t balanced_chunk_len(int64_t total, int64_t lon
     return (int32_t)(t < kMaxChunk ? t : kMaxChunk);
 }
 
-__host__ __device__ inline int balanced_chunks(int64_t nc, int32_t t) {
-    return nc > 0 ? (int)((nc + t - 1) / t) : 1;   // a row without candidates still has chunk 0
-}
 // (The kernel takes cpr and T as separate leading arguments.)
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -279,15 +276,6 @@ __device__ __forceinline__ void lds_barrier() {
 // greedily (optionally appending) and advances the scheduler.
 enum { kPropose = 0, kStep = 1 };
 
-__device__ __forceinline__ u64 wave_max(u64 v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const u64 o = __shfl_xor(v, off);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
 __device__ __forceinline__ u64 readlane64(u64 v, int l) {
     return ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
@@ -360,58 +348,80 @@ __device__ __forceinline__ void finish_request(int r, u64 key, bool failed, int 
 
 constexpr int kBalPer = LCD_BALANCE_MAX_B / 64;           // lengths held per lane
 
-__device__ __forceinline__ int wave_scan_int(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
+// Inclusive prefix over the wave's 64 lanes by DPP: row shifts by 1, 2, 4 and
+// 8 within each row of 16 lanes (lanes with no source take 0), then lane 15's
+// value into row 1 and lane 47's into row 3 (row_bcast:15), and lane 31's into
+// rows 2 and 3 (row_bcast:31).  kMax: running maximum instead of sum.
+template <bool kMax>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    auto op = [](uint32_t x, uint32_t y) { return kMax ? (x > y ? x : y) : x + y; };
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, true));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, true));
     return v;
 }
 
 // Token-balanced assignment of workgroup blockIdx.x: every wave reads all B
 // lengths (one round trip), derives the batch's chunk length and finds its
 // (request, chunk) by a prefix over the rows' chunk counts.  Returns false
-// when the workgroup has no chunk.
+// when the workgroup has no chunk.  Only the groups of 64 rows that exist are
+// visited, and the cross-lane sums are DPP scans: 7 such workgroups share a
+// CU, and a wave's instructions here are all in front of its first tile.
 __device__ __forceinline__ bool balanced_assignment(const int32_t *__restrict__ len, int B, int lane,
                                                     int &r, int &c0, int &P, int &T) {
-    int nc[kBalPer];
+    const int groups = (B + 63) >> 6;
+    uint32_t nc[kBalPer];
 #pragma unroll
     for (int k = 0; k < kBalPer; ++k) {
         const int row = k * 64 + lane;
-        const int l = row < B ? len[row] : 0;
-        nc[k] = l > 1 ? l - 1 : 0;
+        int l = 0;
+        if (k < groups && row < B) l = len[row];
+        nc[k] = l > 1 ? (uint32_t)(l - 1) : 0u;
     }
-    u64 tot = 0;
-    u64 mx = 0;
+    // the total of candidate ends in two 32-bit halves (no carry out of either
+    // for up to 1024 rows), and the longest row's
+    uint32_t lo = 0, hi = 0, mx = 0;
 #pragma unroll
     for (int k = 0; k < kBalPer; ++k) {
-        tot += (u64)nc[k];
-        mx = (u64)nc[k] > mx ? (u64)nc[k] : mx;
+        lo += nc[k] & 0xffffu;
+        hi += nc[k] >> 16;
+        mx = nc[k] > mx ? nc[k] : mx;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
-    mx = wave_max(mx);
-    T = balanced_chunk_len((int64_t)tot, (int64_t)mx, (int64_t)gridDim.x, (int64_t)B);
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan<false>(lo), 63);
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan<false>(hi), 63);
+    mx = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan<true>(mx), 63);
+    T = balanced_chunk_len(((int64_t)hi << 16) + lo, (int64_t)mx, (int64_t)gridDim.x, (int64_t)B);
+    // chunks of a row: ceil(nc / T) = ceil(ceil(nc / 256) / t8), T = 256 t8,
+    // from a double reciprocal: for a <= 2^23 the truncated product is the
+    // quotient or, when t8 divides a, one less, which the remainder corrects
+    const uint32_t t8 = (uint32_t)T >> 8;
+    const double rt = 1.0 / (double)t8;
     const int w = (int)blockIdx.x;
     int base = 0;
+    bool found = false;
 #pragma unroll
     for (int k = 0; k < kBalPer; ++k) {
-        if (k * 64 >= B) break;
+        if (found || k >= groups) continue;     // uniform
         const int row = k * 64 + lane;
-        const int kr = row < B ? balanced_chunks(nc[k], T) : 0;
-        const int incl = wave_scan_int(kr, lane);
+        const uint32_t a = (nc[k] + 255u) >> 8;
+        uint32_t q = (uint32_t)((double)a * rt);
+        q += a - q * t8 >= t8 ? 1u : 0u;
+        const int kr = row < B ? (nc[k] > 0 ? (int)(q + (q * t8 != a ? 1u : 0u)) : 1) : 0;
+        const int incl = (int)wave_incl_scan<false>((uint32_t)kr);
         const int gsum = __builtin_amdgcn_readlane(incl, 63);
         if (w < base + gsum) {
             const int l = (int)__builtin_ctzll(ballot(base + incl > w));
             r = k * 64 + l;
             c0 = w - base - __builtin_amdgcn_readlane(incl - kr, l);
             P = __builtin_amdgcn_readlane(kr, l);
-            return true;
+            found = true;
         }
         base += gsum;
     }
-    return false;
+    return found;
 }
 
 template <int PF, int kMode, bool kBal, int kWaves>
@@ -448,6 +458,11 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
     } else {
         r = (int)(blockIdx.x / (unsigned)cpr);
         c0 = (int)blockIdx.x - r * cpr;
+        // 4-wave launches: a row's chunks in an order rotated by the row, so
+        // that the first chunks of short rows (their only busy workgroups)
+        // are spread over the XCDs (workgroup i runs on XCD i mod 8) instead
+        // of landing on the same one whenever 8 divides cpr x (row distance)
+        if (kWaves == kWavesSmall) c0 = (int)(((unsigned)c0 + (unsigned)r) % (unsigned)cpr);
     }
     int sin = 0;
     uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
@@ -821,20 +836,23 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
 }
 
 // Workgroups per request.  By default one workgroup per ~12k tokens of the
-// batch's size bound B x max_len, at least 256 per launch, with chunks of at
-// least 2048 and at most 32768 tokens of the longest row.  Large batches take
-// several dispatch rounds: with equal chunks the long rows' chunks are the
-// critical path, so they are kept short, and the workgroups past a short row's
-// end leave at once.  Measured on 256 rows of 1k-262k tokens: 16.8 us against
-// 19.4 us with the grid held to one round (1,792 workgroups); on 256 x 262k,
-// 53.1 against 57.5 us; on 200 x 150k and 256 x 53.6k, even.
+// batch's size bound B x max_len, at least 256 and at most 4 dispatch rounds
+// (4 x 7 x 256) per launch, with chunks of at least 2048 and at most 32768
+// tokens of the longest row.  Large batches take several rounds: with equal
+// chunks the long rows' chunks are the critical path, so they are kept short,
+// and the workgroups past a short row's end leave at once -- but not for free,
+// hence the cap.  Measured (with the rotated chunk order): 256 rows of 1k-262k
+// tokens 16.7 us against 19.4 us held to one round (1,792 workgroups); 256 x
+// 262k 52.5 against 57.5 us; one 1M-token row among 255 of 8k, 12.8 us at the
+// cap against 14.9 us at 16,384 workgroups; 200 x 150k and 256 x 53.6k even.
 int pick_cpr(int32_t B, int32_t max_len, int32_t scan_wgs) {
     int64_t cpr;
     if (scan_wgs > 0) {
         cpr = scan_wgs / B;
     } else {
         int64_t wgs = (int64_t)B * max_len / 12000;
-        wgs = wgs < 256 ? 256 : wgs;
+        const int64_t most_wgs = 4 * (int64_t)kResidentSmall * kNumCUs;
+        wgs = wgs < 256 ? 256 : (wgs > most_wgs ? most_wgs : wgs);
         cpr = (wgs + B / 2) / B;
         const int64_t most = ((int64_t)max_len + 2047) / 2048;
         const int64_t least = ((int64_t)max_len + 32767) / 32768;

@@ -383,21 +383,23 @@ def test_launch_shape_query():
 
 def test_automatic_grids_of_large_batches():
     """Batches past the 16-wave shapes get about one 4-wave workgroup per 12k
-    tokens of B x max_len (chunks of ~12k tokens of the longest row, between
-    2048 and 32768), even where that takes several dispatch rounds of the 7 x
-    256 resident workgroups; the token-balanced default stays within one
-    round; explicit scan_wgs and one-chunk-per-row batches are left alone."""
+    tokens of B x max_len, at most 4 dispatch rounds of the 7 x 256 resident
+    workgroups (chunks of ~12k tokens of the longest row where that fits),
+    unless 32768-token chunks of the longest row need more; the token-balanced
+    default stays within one round; explicit scan_wgs and one-chunk-per-row
+    batches are left alone."""
     p = lcd.default_params()
-    wgs, T = lcd.launch_shape(256, 262_144, p)
-    assert (wgs, T) == (22 * 256, 12_032)                 # 262,143 ends in 22 chunks
+    assert lcd.launch_shape(256, 262_144, p) == (22 * 256, 12_032)   # 262,143 ends in 22 chunks
     assert lcd.launch_shape(256, 53_600, p) == (1024, 13_568)
     assert lcd.launch_shape(200, 150_000, p) == (2600, 11_776)
     for B, n in ((200, 262_144), (300, 150_000), (512, 100_000)):
         wgs, T = lcd.launch_shape(B, n, p)
         assert wgs % B == 0 and T % 256 == 0 and abs(T - 12_000) <= 1_000, (B, n, T)
-    assert lcd.launch_shape(1024, 1 << 20, p) == (64 * 1024, 16_384)   # 64 chunks per row at most
+    assert lcd.launch_shape(512, 262_144, p) == (4 * 7 * 256, 18_944)  # the 4-round cap
+    assert lcd.launch_shape(1024, 262_144, p) == (8 * 1024, 32_768)   # 32k-token chunks at most
+    assert lcd.launch_shape(1024, 1 << 20, p) == (32 * 1024, 32_768)
     assert lcd.launch_shape(256, 262_144, lcd.default_params(scan_wgs=2048))[0] == 2048
-    assert lcd.launch_shape(2000, 262_144, p)[0] == 2000 * 22
+    assert lcd.launch_shape(2000, 262_144, p)[0] == 2000 * 8
     assert lcd.launch_shape(2000, 1000, p) == (2000, 1024)
     pb = lcd.default_params(scan_balance=1)
     assert lcd.launch_shape(512, 4096, pb, np.full(512, 4096, np.int32))[0] == 1792

@@ -231,8 +231,11 @@ def test_stress_params(gpu, prm):
     assert_lookup_parity(flat, ro, ln, p)
 
 
-@pytest.mark.parametrize("wgs", [1, 2, 3, 7, 64, 257, 1000, 4096])
+@pytest.mark.parametrize("wgs", [1, 2, 3, 7, 64, 257, 968, 1000, 3872, 4096])
 def test_launch_shapes_do_not_change_results(gpu, wgs):
+    """121 rows: 120 of up to 3,000 tokens and one of 25,000, so most chunks of
+    most rows are empty; 968 and 3,872 workgroups give 8 and 32 chunks per row
+    (the chunk order within a row is rotated by the row)."""
     lcd = _lcd()
     hs = _stress_batch(seed=5, B=120) + [wl.config2().hists[0]]
     flat, ro, ln = wl.pack_csr(hs)
