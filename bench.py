@@ -192,10 +192,14 @@ def _event_mean_us(hev, launch, n, warm=10):
     return float(us.mean())
 
 
+PROBE_SWEEP = ("contig4", "contig8", "interleave4", "interleave8", "interleave16")
+
+
 def read_ceiling(lcd, sets, nbytes, n=200, blocks=(1024, 2048, 4096, 8192),
-                 variants=("contig4", "contig8", "interleave4", "interleave8", "interleave16")):
+                 variants=PROBE_SWEEP + tuple(v + "-nt" for v in PROBE_SWEEP)):
     """Practical HBM read ceiling at nbytes: lcd_read_probe over the rotating
-    buffers, GPU-stamped, in every variant and grid; the best mean."""
+    buffers, GPU-stamped, in every variant (plain and non-temporal loads) and
+    grid; the best mean."""
     import torch
     nbytes = nbytes // 16 * 16
     hev = HipEvents(lcd.load())

@@ -623,6 +623,8 @@ def scan_occupancy(waves: int) -> int:
 
 PROBE_VARIANTS = {"contig4": 0, "contig8": 1, "interleave4": 2, "interleave8": 3,
                   "interleave16": 4}
+PROBE_NT = 8                       # or-ed in: non-temporal loads ("...-nt" names)
+PROBE_VARIANTS.update({k + "-nt": v | PROBE_NT for k, v in list(PROBE_VARIANTS.items())})
 
 
 def read_probe(buf, nbytes: int, blocks: int, out, ev_start=None, ev_stop=None,

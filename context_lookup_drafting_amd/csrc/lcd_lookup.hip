@@ -115,6 +115,7 @@ constexpr int kPollBatch = 8;                             // slot words per lane
 constexpr u64 kTagLimit = (1ull << 28) - 1;               // epochs 0 .. kTagLimit - 1
 constexpr int kPollMax = 1 << 20;                         // gathering polls, at most (default)
 constexpr int kBufferWord3 = 0x00020000;                  // gfx9 buffer descriptor, dword 3
+constexpr int kLoadNT = 2;                                 // buffer-load cache policy: non-temporal
 constexpr int kFullAfter = 4;                             // flagged tiles before a wave drops the quick test
 
 struct ScanArgs {
@@ -560,13 +561,17 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<int32_t *>(hist + X0 - kHaloTok), 0, (g_last + 4 + kHaloTok) * 4,
             kBufferWord3);
+        // The history is read once: its tiles are loaded non-temporal (the
+        // nt cache-policy bit), which keeps the streamed lines from pushing
+        // the launch's small per-request data out of the caches (measured:
+        // 64 x 150k 11.9 -> 11.3 us, 256 ragged rows 16.8 -> 16.4 us).
         const unsigned lane_off = 16u * (unsigned)lane;
         const unsigned head_off = head ? (unsigned)kHaloTok * 4u : 0u;
         auto load_tile = [&](int kt) -> int4 {
             unsigned off = (unsigned)(kTileCand * 4) * (unsigned)kt + lane_off;
             off = kt < nt ? off : kNoTileOff;
             off = off < head_off ? head_off : off;
-            return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+            return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kLoadNT));
         };
         int idx[kUnroll];
         int4 buf[kUnroll];

@@ -52,6 +52,10 @@ constexpr u64 kSumMask = (1ull << kTagShift) - 1;
 constexpr u64 kTagLimit = (1ull << (64 - kTagShift)) - 1;   // epochs 0 .. kTagLimit - 1
 constexpr int kPollMax = 1 << 20;           // bound on the gathering's polls (default)
 constexpr int kBufferWord3 = 0x00020000;    // gfx9 buffer descriptor, dword 3
+// The rows are streamed with the non-temporal cache policy (the nt bit): each
+// is read once, and its lines would otherwise displace the launch's small
+// per-request data (measured: the sampled batch 25.8 -> 24.8 us per step).
+constexpr int kLoadNT = 2;
 
 // Kinds of the distribution a request draws from.
 constexpr int kPlain = 0;                   // the target row p_a itself
@@ -181,12 +185,12 @@ __device__ __forceinline__ u64 unit_sum(__amdgpu_buffer_rsrc_t prs, __amdgpu_buf
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         pv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               prs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, 0));
+                                               prs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, kLoadNT));
     if (model) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             qv[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   qrs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, 0));
+                                                   qrs, (u * kUnit + 4 * (lane + 64 * k)) * 4, 0, kLoadNT));
     } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);

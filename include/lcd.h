@@ -63,14 +63,16 @@ extern "C" {
  *                 workgroups, at most 256, for batches of 32-128 rows whose
  *                 longest row has 16k+ tokens, or 8k+ with B x max_len of
  *                 1.2M+, and of 1-31 rows whose longest row has 6k+ tokens;
- *                 4-wave workgroups otherwise).  Results never depend on it.
+ *                 4-wave workgroups otherwise, about one per 12k tokens of
+ *                 B x max_len, at most 7168).  Results never depend on it.
  *   scan_balance  launch tuning of the scan (lookup_propose, lookup_decode_step)
  *                 for ragged batches: 1 = chunks of equal token count, sized on
  *                 the device from the rows' lengths, so long rows get more
  *                 workgroups than short ones (B <= LCD_BALANCE_MAX_B; larger
  *                 batches use equal chunks per row); 0 = every row is cut into
- *                 the same number of chunks, sized from max_len.  Results never
- *                 depend on it.
+ *                 the same number of chunks, sized from max_len.  1 pays where
+ *                 one row is far longer than very many short ones; elsewhere
+ *                 the automatic launch is faster.  Results never depend on it.
  *   merge_polls   diagnostics: how often the workgroup that completes a
  *                 request's lookup polls the other workgroups' results before
  *                 it gives up (0 = the default, 2^20; -1 = not at all, which
@@ -513,7 +515,8 @@ int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, const i
  * 256 threads, each writing one int32 to out[blocks] (device), in one of the
  * variants below (loads in flight per lane; each workgroup reading one
  * contiguous share, or the workgroups interleaved over blocks of 256 x depth
- * granules).  The GPU stamps the kernel's start and end into ev_start /
+ * granules), each with plain loads or, with LCD_PROBE_NT or-ed in,
+ * non-temporal ones (how the scan and the sampled verification stream).  The GPU stamps the kernel's start and end into ev_start /
  * ev_stop (hipEvent_t, nullable).  The best variant and grid gives the
  * practical HBM read ceiling at a byte count on the running GPU.
  */
@@ -522,6 +525,7 @@ int lookup_launch_shape(int32_t B, int32_t max_len, const lcd_params *p, const i
 #define LCD_PROBE_INTERLEAVE_4 2
 #define LCD_PROBE_INTERLEAVE_8 3
 #define LCD_PROBE_INTERLEAVE_16 4
+#define LCD_PROBE_NT 8
 int lcd_read_probe(const void *buf, int64_t bytes, int32_t blocks, int32_t variant, int32_t *out,
                    void *stream, void *ev_start, void *ev_stop);
 

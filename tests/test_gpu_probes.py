@@ -9,7 +9,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("variant", ["contig4", "contig8", "interleave4", "interleave8",
-                                     "interleave16"])
+                                     "interleave16", "contig4-nt", "contig8-nt", "interleave4-nt",
+                                     "interleave8-nt", "interleave16-nt"])
 def test_read_probe_reads_every_granule_once(gpu, variant):
     import torch
     import context_lookup_drafting_amd as lcd
