@@ -73,7 +73,7 @@ def test_full_size_sampled_batch(gpu):
     args = (sb.block, sb.block_len, sb.target_probs, sb.u_accept, sb.u_sample, sb.model_mask,
             sb.model_probs)
     acc, _ = assert_rejection_parity(*args, ws=ws)
-    for wg in (0, 1, 4, 61, 243):
+    for wg in (0, 1, 4, 8, 61, 243):          # 0: 32 units, 8 workgroups per request
         assert_rejection_parity(*args, wg_units=wg, ws=ws)
     assert rejection_ws_clean(ws, sb.B)
     # the batch exercises every kind of draw: point-mass and draft-model
