@@ -63,6 +63,7 @@ constexpr int kPointResidual = 1;           // p_a without the rejected token x
 constexpr int kModelResidual = 2;           // max(p_a - q_a, 0)
 constexpr int kKeep = 4;                    // unit sums a lane keeps in registers (U <= 256)
 constexpr int kMaxUpw = 256;                // units per workgroup, at most
+constexpr int kPollBatch = 8;               // unit sums a lane loads at once past kKeep
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -302,10 +303,20 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
                 lsum += kept[k];
             }
         } else {
-            for (int u = ua; u < ub; ++u) {
-                const u64 v = __hip_atomic_load(sums + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = ok && ((v & ~kSumMask) == tagged);
-                lsum += v & kSumMask;
+            // more than kKeep units per lane (vocabularies past 256 units):
+            // batches of kPollBatch loads in flight, not one load per round trip
+            for (int u0b = ua; u0b < ub; u0b += kPollBatch) {
+                u64 v[kPollBatch];
+#pragma unroll
+                for (int k = 0; k < kPollBatch; ++k)
+                    v[k] = u0b + k < ub ? __hip_atomic_load(sums + u0b + k, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : tagged;
+#pragma unroll
+                for (int k = 0; k < kPollBatch; ++k) {
+                    ok = ok && ((v[k] & ~kSumMask) == tagged);
+                    lsum += v[k] & kSumMask;
+                }
             }
         }
         all = __ballot(!ok) == 0;

@@ -93,10 +93,15 @@ def test_vocabulary_sizes_and_launch_shapes(gpu, V):
                                     sb.u_sample, sb.model_mask, sb.model_probs, wg_units=wg)
 
 
-def test_largest_vocabulary(gpu):
-    """V = 2^22: 4096 units, the most a request's gathering handles (64 per lane)."""
+@pytest.mark.parametrize("units", [260, 600, 4096])
+def test_large_vocabularies(gpu, units):
+    """Past 256 units each lane of the gathering loads its unit sums in batches
+    of 8: 260 units (5 a lane, one partial batch), 600 (10 a lane, a full and a
+    partial batch) and V = 2^22, 4096 units, the most a request's gathering
+    handles (64 a lane)."""
     import context_lookup_drafting_amd as lcd
-    V = lcd.SAMPLE_MAX_VOCAB
+    V = units * 1024
+    assert V <= lcd.SAMPLE_MAX_VOCAB
     sb = wl.sampled_batch(seed=4, B=2, V=V)
     assert_rejection_parity(sb.block, sb.block_len, sb.target_probs, sb.u_accept, sb.u_sample,
                             sb.model_mask, sb.model_probs)
