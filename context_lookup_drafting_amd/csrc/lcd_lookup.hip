@@ -339,12 +339,12 @@ __device__ __forceinline__ void finish_request(int r, u64 key, bool failed, int 
     const int kk = lane < LCD_DRAFT_STRIDE ? lane : 0;
     int dk = __shfl(src, base + kk % D);
     dk = (m > 0 && lane < k_max) ? dk : LCD_PAD;
-    if (lane < LCD_DRAFT_STRIDE) so.draft[(int64_t)r * LCD_DRAFT_STRIDE + lane] = dk;
+    if (lane < LCD_DRAFT_STRIDE) gstore<true>(so.draft + (int64_t)r * LCD_DRAFT_STRIDE + lane, dk);
     if (lane == 0) {
-        so.match_len[r] = m;
-        so.match_end[r] = e;
+        gstore<true>(so.match_len + r, m);
+        gstore<true>(so.match_end + r, e);
     }
-    if (kMode == kStep) finish_step(r, m, dk, sin, tin, lane, ro, lr, n, so.io);
+    if (kMode == kStep) finish_step<true>(r, m, dk, sin, tin, lane, ro, lr, n, so.io);
 }
 
 constexpr int kBalPer = LCD_BALANCE_MAX_B / 64;           // lengths held per lane
