@@ -876,6 +876,10 @@ def bench_sampled(args):
     achieved = alg_bytes / k_avg / 1e9
     probs = rows * V
     value = K * probs / elapsed
+    # the plain streaming read of as many bytes as the draw rows, from the
+    # same rotating probability tensors
+    ceiling = read_ceiling(lcd, [s[0] for s in sets], read_bytes)
+    ceiling["frac_of_ceiling"] = round(achieved / ceiling["gbps"], 4)
     out = {
         "metric": SAMPLED_METRIC,
         "value": round(value, 1),
@@ -915,6 +919,7 @@ def bench_sampled(args):
             "alg_bytes_per_launch": alg_bytes,
             "launches_timed": n_k,
         },
+        "read_ceiling": ceiling,
         "cpu_baseline": (cpu_baseline_sampled(sb, args.cpu_work_seconds)
                          if args.cpu_work_seconds > 0 else None),
     }
