@@ -220,8 +220,9 @@ def _stress_batch(seed=11, B=300):
 
 
 @pytest.mark.parametrize("prm", [
-    dict(), dict(l_min=1, l_max=1), dict(l_min=2, l_max=5, k_max=7), dict(l_min=3, l_max=16),
-    dict(l_min=4, l_max=16, k_max=0), dict(l_min=12, l_max=12), dict(l_min=6, l_max=9, k_max=3),
+    dict(), dict(l_min=1, l_max=1), dict(l_min=1, l_max=16), dict(l_min=2, l_max=5, k_max=7),
+    dict(l_min=3, l_max=16), dict(l_min=4, l_max=16, k_max=0), dict(l_min=12, l_max=12),
+    dict(l_min=6, l_max=9, k_max=3),
 ])
 def test_stress_params(gpu, prm):
     lcd = _lcd()
