@@ -64,7 +64,9 @@ extern "C" {
  *                 longest row has 16k+ tokens, or 8k+ with B x max_len of
  *                 1.2M+, and of 1-31 rows whose longest row has 6k+ tokens;
  *                 4-wave workgroups otherwise, about one per 12k tokens of
- *                 B x max_len, at most 7168).  Results never depend on it.
+ *                 B x max_len, at most 7168, except that each row gets
+ *                 enough of them (up to 64) for chunks of at most 32,768
+ *                 tokens of the longest row).  Results never depend on it.
  *   scan_balance  launch tuning of the scan (lookup_propose, lookup_decode_step)
  *                 for ragged batches: 1 = chunks of equal token count, sized on
  *                 the device from the rows' lengths, so long rows get more
@@ -202,8 +204,7 @@ int fuse_verify_block(const int32_t *draft, const int32_t *match_len,
  * (a+1 tokens).  When hist is non-NULL those a+1 tokens are appended at
  * hist[row_off[r] + n], n = max(len[r], 0), and len[r] becomes n+a+1; if
  * n+a+1 > cap[r] nothing is written for that request and accept[r] = -1.
- * row_off, len and
- * cap are only read when hist is non-NULL.
+ * row_off, len and cap are only read when hist is non-NULL.
  *
  * block int32[B*15], block_len int32[B], target int32[B*16],
  * accept int32[B]; hist int32 buffer (nullable), row_off int64[B],
