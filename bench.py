@@ -505,7 +505,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the lookup path needs no "
+        print("bench.py: the benchmark runs on one GPU only (the lookup path needs no "
               "cross-GPU exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
