@@ -163,9 +163,20 @@ __device__ __forceinline__ int walk_block(int r, int lane, const SampleArgs &sa,
     const bool valid = lane < L && xk >= 0 && xk < sa.V;
     const bool use_model = valid && lane < LCD_Q_STRIDE && ((mm >> lane) & 1u);
     const double u = lane < LCD_DRAFT_STRIDE ? io.u_accept[(int64_t)r * LCD_DRAFT_STRIDE + lane] : 0.0;
-    float P = 0.0f, Q = 1.0f;
-    if (valid) P = prob01(io.target_probs[((int64_t)r * LCD_TARGET_STRIDE + lane) * sa.V + xk]);
-    if (use_model) Q = prob01(io.model_probs[((int64_t)r * LCD_Q_STRIDE + lane) * sa.V + xk]);
+    // Both gathers in flight at once: every lane loads from an address inside
+    // the request's rows (slot 0's row and token 0 where its own slot has no
+    // valid token; the target rows where no draft-model rows are given) and
+    // masks the value afterwards.
+    const int xs = valid ? xk : 0;
+    const int ks = lane < LCD_DRAFT_STRIDE ? lane : 0;
+    const int qs = lane < LCD_Q_STRIDE ? lane : 0;
+    const float *pp = io.target_probs + ((int64_t)r * LCD_TARGET_STRIDE + ks) * sa.V + xs;
+    const float *qp = io.model_probs != nullptr
+                          ? io.model_probs + ((int64_t)r * LCD_Q_STRIDE + qs) * sa.V + xs
+                          : pp;
+    const float pv = *pp, qv = *qp;
+    const float P = valid ? prob01(pv) : 0.0f;
+    const float Q = use_model ? prob01(qv) : 1.0f;
     const bool ok = valid && (u * (double)Q < (double)P);
     const u64 stop = __ballot(lane < L && !ok);
     const int a = stop ? (int)__builtin_ctzll(stop) : L;
@@ -224,7 +235,14 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     u64 *__restrict__ req = ws + (int64_t)r * words;
     u64 *__restrict__ sums = req + 2;
 
-    unsigned long long ticket = 0;
+    // Arrival ticket, taken by thread 0 and read back (from wave 0's lane 0)
+    // only after the stream; the other lanes' value is left unspecified.  Its
+    // return arrives with the walk's first loads, issued after it (taken after
+    // the walk instead, or by the last wave, it measured no better).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wsometimes-uninitialized"
+#pragma clang diagnostic ignored "-Wuninitialized"
+    unsigned long long ticket;
     if (tid == 0)
         ticket = __hip_atomic_fetch_add(req, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -268,6 +286,7 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
     // lane 0 took the ticket: the arrival count and the call's epoch
     const u64 hdr = ((u64)(uint32_t)__builtin_amdgcn_readfirstlane((int)(ticket >> 32)) << 32) |
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)ticket);
+#pragma clang diagnostic pop
     const u64 tagged = ((hdr >> 32) + 1) << kTagShift;   // this call's tag, in place
     for (int k = lane; k < u1 - u0; k += 64)
         __hip_atomic_store(sums + u0 + k, tagged | s_sums[k], __ATOMIC_RELAXED,
