@@ -475,6 +475,10 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         // of landing on the same one whenever 8 divides cpr x (row distance)
         if (kWaves == kWavesSmall) c0 = (int)(((unsigned)c0 + (unsigned)r) % (unsigned)cpr);
     }
+    // the row's offset and length first: every tile load waits on them (wave
+    // 0's step inputs below would otherwise go out ahead of them)
+    const int64_t ro = row_off[r];
+    const int32_t lr = len[r];
     int sin = 0;
     uint32_t tin = 0;                 // the request's telemetry row, lane k: counter k
     // 16-wave workgroups: word k of the first argument (the outputs and the
@@ -496,8 +500,6 @@ lookup_scan_kernel(ScanOut out_arg, const int32_t *__restrict__ hist,
         if (io0.tele != nullptr)
             tin = io0.tele[(int64_t)r * LCD_TELE_WORDS + (lane & (LCD_TELE_WORDS - 1))];
     }
-    const int64_t ro = row_off[r];
-    const int32_t lr = len[r];
     const int n = lr > 0 ? lr : 0;
     const int nc = n - 1;             // candidate ends 0..n-2
     if (nc <= 0) {                    // no earlier position: chunk 0 finishes the request
