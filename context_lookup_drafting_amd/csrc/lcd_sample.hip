@@ -401,14 +401,25 @@ rejection_accept_kernel(SampleArgs sa, SampleIO io, u64 *__restrict__ ws) {
         // lane k holds floats [16k, 16k+16) of the unit
         const int base = unit * kUnit + 16 * lane;
         const bool dm = draw_kind == kModelResidual;
+        // all eight loads in flight before the first is used: the draft
+        // model's row is read whatever the kind (qrs is the target row itself
+        // unless the request drew a draft-model residual), and used only for
+        // a draft-model residual.  With the second load behind the kind's
+        // test, each 16-float step waited on its own round trip.
+        float4 pv4[4], qv4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            pv4[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    prs, (base + 4 * k) * 4, 0, 0));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            qv4[k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    qrs, (base + 4 * k) * 4, 0, 0));
         u64 w[16], ls = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float4 pv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          prs, (base + 4 * k) * 4, 0, 0));
-            const float4 qv = dm ? __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                   qrs, (base + 4 * k) * 4, 0, 0))
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 pv = pv4[k];
+            const float4 qv = dm ? qv4[k] : make_float4(0.f, 0.f, 0.f, 0.f);
             const float f[4] = {pv.x, pv.y, pv.z, pv.w};
             const float g[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
