@@ -544,6 +544,21 @@ def test_balanced_scan_stress_and_edges(gpu):
     assert_lookup_parity(flat3, ro3, ln3, p)
 
 
+def test_balanced_scan_batches_at_the_limit(gpu):
+    """Token-balanced chunks at 1,024 rows (all 16 groups of 64 lengths per
+    lane present), 1,023 and 961 rows (the last group partial), each with one
+    50k-token row among short ones: every length load of a lane is in flight at
+    once and rows past the batch are masked."""
+    lcd = _lcd()
+    p = lcd.default_params(scan_balance=1)
+    long_row = wl.config4(B=1, n=50_000).hists[0]
+    for B in (1024, 1023, 961):
+        hs = _stress_batch(seed=23 + B, B=B - 1) + [long_row]
+        flat, ro, ln = wl.pack_csr(hs)
+        assert lcd.launch_shape(B, int(ln.max()), p, ln)[0] >= B
+        assert_lookup_parity(flat, ro, ln, p)
+
+
 def test_balanced_fused_simulation(gpu):
     """The fused decode step with token-balanced chunks: 128 steps of config 3
     equal the oracle's simulation."""
